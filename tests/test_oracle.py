@@ -1,0 +1,336 @@
+"""Pins for the CPU float64 oracle (no GPU).
+
+The oracle is checked against things other than itself: torch's float64
+cross-entropy and autograd (an independent library routine), central finite
+differences, closed forms, and invariants that follow from the definition.
+A final test plants mistakes in the oracle and checks that the pins catch
+them.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+
+from lce_inputs import IGNORE_INDEX, WORKLOADS, make_case, make_inputs
+from oracle import lce_oracle as O
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _case(n, h, v, seed=0, bias=False, ignore_frac=0.2, hidden_dist="normal", weight_std=0.3):
+    inp = make_case(n, h, v, seed=seed, bias_std=(0.5 if bias else None), ignore_frac=ignore_frac,
+                    hidden_dist=hidden_dist, weight_std=weight_std)
+    return inp.hidden_f32().astype(np.float64), inp.weight_f32().astype(np.float64), \
+        (None if inp.bias_bits is None else inp.bias_f32().astype(np.float64)), inp.labels
+
+
+def _torch_reference(h, w, b, y, reduction, grad_scale=1.0):
+    """torch float64: F.linear + F.cross_entropy(ignore_index=-100) + autograd."""
+    ht = torch.tensor(h, requires_grad=True)
+    wt = torch.tensor(w, requires_grad=True)
+    bt = None if b is None else torch.tensor(b, requires_grad=True)
+    z = F.linear(ht, wt, bt)
+    yt = torch.tensor(y)
+    valid = yt != IGNORE_INDEX
+    if reduction == "mean" and int(valid.sum()) == 0:
+        loss = (z * 0.0).sum()
+    else:
+        loss = F.cross_entropy(z, yt, ignore_index=IGNORE_INDEX, reduction=reduction)
+    if reduction == "none":
+        g = torch.as_tensor(np.broadcast_to(grad_scale, (len(y),)).copy())
+        loss.backward(g)
+    else:
+        (loss * grad_scale).backward()
+    lse = torch.logsumexp(z.detach(), dim=1)
+    return (loss.detach().numpy(), lse.numpy(), ht.grad.numpy(), wt.grad.numpy(),
+            None if bt is None else bt.grad.numpy())
+
+
+SHAPES = [(1, 1, 1), (5, 3, 7), (17, 8, 33), (64, 16, 130), (300, 24, 257)]
+
+
+@pytest.mark.parametrize("shape", SHAPES)
+@pytest.mark.parametrize("bias", [False, True])
+@pytest.mark.parametrize("reduction", ["sum", "mean", "none"])
+def test_matches_torch_cross_entropy(shape, bias, reduction):
+    n, hd, v = shape
+    h, w, b, y = _case(n, hd, v, seed=n + v, bias=bias)
+    gs = 0.75 if reduction != "none" else np.linspace(0.5, 1.5, n)
+    res = O.forward_backward(h, w, b, y, reduction=reduction, grad_scale=gs)
+    tl, tlse, tgh, tgw, tgb = _torch_reference(h, w, b, y, reduction, gs)
+    np.testing.assert_allclose(res.loss, tl, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(res.lse, tlse, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(res.grad_hidden, tgh, rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(res.grad_weight, tgw, rtol=1e-10, atol=1e-12)
+    if bias:
+        np.testing.assert_allclose(res.grad_bias, tgb, rtol=1e-10, atol=1e-12)
+    assert res.n_valid == int((y != IGNORE_INDEX).sum())
+
+
+def test_finite_differences():
+    """Central differences of the oracle's own loss, step 1e-6, float64."""
+    n, hd, v = 6, 5, 7
+    h, w, b, y = _case(n, hd, v, seed=3, bias=True, ignore_frac=0.2, weight_std=0.5)
+    res = O.forward_backward(h, w, b, y, reduction="mean", grad_scale=1.3)
+
+    def loss_of(hh, ww, bb):
+        return 1.3 * O.forward(hh, ww, bb, y, reduction="mean").loss
+
+    eps = 1e-6
+    for arr, grad in ((h, res.grad_hidden), (w, res.grad_weight), (b, res.grad_bias)):
+        fd = np.zeros_like(arr)
+        for idx in np.ndindex(arr.shape):
+            orig = arr[idx]
+            arr[idx] = orig + eps
+            lp = loss_of(h, w, b)
+            arr[idx] = orig - eps
+            lm = loss_of(h, w, b)
+            arr[idx] = orig
+            fd[idx] = (lp - lm) / (2 * eps)
+        np.testing.assert_allclose(grad, fd, rtol=1e-6, atol=1e-8)
+
+
+def test_zero_weight_closed_form():
+    """W = 0, b = 0: every valid row has loss ln V; grad_hidden = 0;
+    grad_weight[j] = (1/V) sum_valid h_i - sum_{i: y_i = j} h_i;
+    grad_bias[j] = n_valid / V - #{i : y_i = j}."""
+    n, hd, v = 40, 6, 9
+    h, _, _, y = _case(n, hd, v, seed=5, ignore_frac=0.25)
+    w = np.zeros((v, hd))
+    b = np.zeros(v)
+    res = O.forward_backward(h, w, b, y, reduction="sum")
+    valid = y != IGNORE_INDEX
+    nv = int(valid.sum())
+    assert res.loss == pytest.approx(nv * math.log(v), rel=1e-14)
+    assert np.all(res.grad_hidden == 0)
+    hv = h[valid].sum(axis=0)
+    for j in range(v):
+        expect = hv / v - h[valid & (y == j)].sum(axis=0)
+        np.testing.assert_allclose(res.grad_weight[j], expect, rtol=1e-13, atol=1e-13)
+        assert res.grad_bias[j] == pytest.approx(nv / v - int((y == j).sum()), abs=1e-12)
+
+
+@pytest.mark.parametrize("v", [4096, 151936])
+def test_zero_weight_loss_is_log_vocab(v):
+    n, hd = 8, 4
+    h = np.ones((n, hd))
+    y = np.arange(n) % v
+    res = O.forward(h, np.zeros((v, hd)), None, y)
+    assert res.loss / n == pytest.approx(math.log(v), rel=1e-13)
+
+
+def test_bias_only_closed_form():
+    """W = 0, b != 0: l_i = logsumexp(b) - b_{y_i}, evaluated with math.fsum."""
+    v, n, hd = 11, 13, 3
+    rng = np.random.default_rng(7)
+    b = rng.normal(size=v)
+    y = rng.integers(0, v, n)
+    res = O.forward(rng.normal(size=(n, hd)), np.zeros((v, hd)), b, y)
+    mb = max(b)
+    lse_b = mb + math.log(math.fsum(math.exp(x - mb) for x in b))
+    for i in range(n):
+        assert res.row_loss[i] == pytest.approx(lse_b - b[y[i]], rel=1e-13)
+
+
+def test_two_class_is_logistic_loss():
+    """V = 2: l = softplus(z_other - z_y) and dl/dz_other = sigmoid(z_other - z_y)."""
+    rng = np.random.default_rng(11)
+    n, hd = 20, 4
+    h = rng.normal(size=(n, hd))
+    w = rng.normal(size=(2, hd))
+    y = rng.integers(0, 2, n)
+    res = O.forward_backward(h, w, None, y, reduction="sum")
+    z = h @ w.T
+    for i in range(n):
+        t = z[i, 1 - y[i]] - z[i, y[i]]
+        assert res.row_loss[i] == pytest.approx(math.log1p(math.exp(-abs(t))) + max(t, 0.0), rel=1e-12)
+        sig = 1.0 / (1.0 + math.exp(-t))
+        np.testing.assert_allclose(res.grad_hidden[i], sig * (w[1 - y[i]] - w[y[i]]), rtol=1e-12, atol=1e-14)
+
+
+@pytest.mark.parametrize("reduction", ["sum", "mean"])
+def test_chunk_size_invariance(reduction):
+    """Rows split cleanly (TRL guide, 'chunking'): chunk sizes 1, 3 and N give
+    the same loss and gradients as the unchunked definition."""
+    n, hd, v = 37, 7, 19
+    h, w, b, y = _case(n, hd, v, seed=2, bias=True)
+    full = O.forward_backward(h, w, b, y, reduction=reduction, grad_scale=0.5)
+    for c in (1, 3, n, 1000):
+        ch = O.chunked_forward_backward(h, w, b, y, c, reduction=reduction, grad_scale=0.5)
+        assert ch.loss == pytest.approx(full.loss, rel=1e-12, abs=1e-12)
+        np.testing.assert_allclose(ch.grad_hidden, full.grad_hidden, rtol=1e-12, atol=1e-15)
+        np.testing.assert_allclose(ch.grad_weight, full.grad_weight, rtol=1e-11, atol=1e-14)
+        np.testing.assert_allclose(ch.grad_bias, full.grad_bias, rtol=1e-11, atol=1e-14)
+        assert len(ch.chunk_loss) == -(-n // c)
+        assert math.fsum(ch.chunk_loss) == pytest.approx(math.fsum(full.row_loss), rel=1e-12)
+
+
+def test_ignored_rows_contribute_nothing():
+    n, hd, v = 30, 5, 12
+    h, w, b, y = _case(n, hd, v, seed=4, bias=True, ignore_frac=0.3)
+    ign = y == IGNORE_INDEX
+    assert ign.any()
+    a = O.forward_backward(h, w, b, y)
+    h2 = h.copy()
+    h2[ign] = np.random.default_rng(0).normal(size=(int(ign.sum()), hd)) * 50
+    bres = O.forward_backward(h2, w, b, y)
+    assert a.loss == bres.loss
+    np.testing.assert_array_equal(a.grad_weight, bres.grad_weight)
+    np.testing.assert_array_equal(a.grad_bias, bres.grad_bias)
+    assert np.all(bres.grad_hidden[ign] == 0)
+    assert np.all(bres.row_loss[ign] == 0)
+    assert a.n_valid == n - int(ign.sum())
+
+
+def test_bias_shift_invariance():
+    n, hd, v = 25, 4, 10
+    h, w, b, y = _case(n, hd, v, seed=8, bias=True)
+    a = O.forward_backward(h, w, b, y)
+    s = O.forward_backward(h, w, b + 3.25, y)
+    assert s.loss == pytest.approx(a.loss, rel=1e-13)
+    np.testing.assert_allclose(s.grad_weight, a.grad_weight, rtol=1e-10, atol=1e-13)
+    np.testing.assert_allclose(s.lse, a.lse + 3.25, rtol=1e-14)
+
+
+def test_gradient_sums_vanish():
+    """Each valid row's softmax sums to 1, minus its one-hot: sum_j G_ij = 0,
+    so sum_j grad_bias_j = 0 and sum_j grad_weight[j, :] = 0."""
+    h, w, b, y = _case(50, 6, 23, seed=9, bias=True)
+    r = O.forward_backward(h, w, b, y)
+    assert abs(r.grad_bias.sum()) < 1e-12
+    np.testing.assert_allclose(r.grad_weight.sum(axis=0), 0, atol=1e-12)
+
+
+def test_row_permutation_equivariance():
+    h, w, b, y = _case(31, 5, 14, seed=10, bias=True)
+    perm = np.random.default_rng(1).permutation(31)
+    a = O.forward_backward(h, w, b, y)
+    p = O.forward_backward(h[perm], w, b, y[perm])
+    assert p.loss == pytest.approx(a.loss, rel=1e-13)
+    np.testing.assert_allclose(p.grad_hidden, a.grad_hidden[perm], rtol=1e-13, atol=1e-16)
+    np.testing.assert_allclose(p.grad_weight, a.grad_weight, rtol=1e-11, atol=1e-14)
+
+
+def test_row_shard_additivity():
+    """Disjoint row shards, summed, equal the whole (the data-parallel split)."""
+    h, w, b, y = _case(40, 5, 16, seed=12, bias=True)
+    whole = O.forward_backward(h, w, b, y)
+    parts = [O.forward_backward(h[s:s + 13], w, b, y[s:s + 13]) for s in range(0, 40, 13)]
+    assert sum(p.loss for p in parts) == pytest.approx(whole.loss, rel=1e-13)
+    assert sum(p.n_valid for p in parts) == whole.n_valid
+    np.testing.assert_allclose(sum(p.grad_weight for p in parts), whole.grad_weight, rtol=1e-11, atol=1e-14)
+    np.testing.assert_allclose(np.concatenate([p.grad_hidden for p in parts]), whole.grad_hidden,
+                               rtol=1e-13, atol=1e-16)
+
+
+def test_mean_with_no_valid_rows_is_zero():
+    h, w, b, _ = _case(6, 3, 5, seed=1, bias=True)
+    y = np.full(6, IGNORE_INDEX)
+    r = O.forward_backward(h, w, b, y, reduction="mean")
+    assert r.loss == 0.0 and r.n_valid == 0
+    assert np.all(r.grad_hidden == 0) and np.all(r.grad_weight == 0) and np.all(r.grad_bias == 0)
+
+
+def test_empty_rows():
+    r = O.forward_backward(np.zeros((0, 4)), np.ones((3, 4)), None, np.zeros(0, dtype=np.int64))
+    assert r.loss == 0.0 and r.n_valid == 0 and r.grad_weight.shape == (3, 4)
+
+
+def test_page_facts():
+    facts = json.load(open(os.path.join(GOLDEN, "pages_facts.json")))
+    assert O.IGNORE_INDEX == IGNORE_INDEX == facts["ignore_index"]["value"]
+    assert WORKLOADS["tiny"].chunk_rows == facts["default_chunk_rows"]["value"]
+    for bad in (0, -1, -256):
+        with pytest.raises(ValueError):
+            O.check_problem(4, 4, 4, bad)
+    O.check_problem(4, 4, 4, None)
+
+
+def test_label_out_of_range_raises():
+    h, w, b, y = _case(5, 3, 4, seed=0)
+    y = y.copy()
+    y[2] = 4
+    with pytest.raises(ValueError):
+        O.forward(h, w, b, y)
+    y[2] = -5
+    with pytest.raises(ValueError):
+        O.forward(h, w, b, y)
+
+
+def test_blocked_and_subset_helpers_match_full():
+    h, w, b, y = _case(90, 8, 40, seed=13, bias=True)
+    full = O.forward_backward(h, w, b, y, reduction="mean", grad_scale=2.0)
+    lse = O.lse_rows_blocked(h.astype(np.float32), w.astype(np.float32), b, block_rows=17)
+    np.testing.assert_allclose(lse, full.lse, rtol=1e-14)
+    rows = np.array([0, 5, 17, 89])
+    rl, rr, rgh = O.rows_reference(h, w, b, y, rows, n_valid=full.n_valid, reduction="mean", grad_scale=2.0)
+    np.testing.assert_allclose(rl, full.lse[rows], rtol=1e-14)
+    np.testing.assert_allclose(rr, full.row_loss[rows], rtol=1e-13, atol=1e-15)
+    np.testing.assert_allclose(rgh, full.grad_hidden[rows], rtol=1e-12, atol=1e-16)
+    cols = np.array([0, 3, 39, int(y[y >= 0][0])])
+    gw, gb = O.cols_reference(h, w, b, y, full.lse, cols, n_valid=full.n_valid, reduction="mean",
+                              grad_scale=2.0, block_rows=23)
+    np.testing.assert_allclose(gw, full.grad_weight[cols], rtol=1e-11, atol=1e-14)
+    np.testing.assert_allclose(gb, full.grad_bias[cols], rtol=1e-11, atol=1e-14)
+
+
+def test_loss_statistics_tiny_workload():
+    """Sanity, not parity: mean row loss ~ ln V + var(z)/2 with var(z) = H * 0.02^2."""
+    inp = make_inputs(WORKLOADS["tiny"])
+    r = O.forward(inp.hidden_f32(), inp.weight_f32(), None, inp.labels)
+    assert r.n_valid == 461
+    expect = math.log(4096) + 256 * 0.02 ** 2 / 2
+    assert abs(r.loss / r.n_valid - expect) < 0.05
+
+
+def test_generator_ignore_counts():
+    """n_valid follows from the recipe: N - floor(p N) rows keep a label."""
+    t = make_inputs(WORKLOADS["tiny"])
+    assert int((t.labels != IGNORE_INDEX).sum()) == 461
+    q = make_inputs(WORKLOADS["qwen3_0p6b_head"])
+    assert int((q.labels != IGNORE_INDEX).sum()) == 1434
+    assert np.all(q.labels[:614] == IGNORE_INDEX) and np.all(q.labels[614:] >= 0)
+    for name, nv in (("qwen3_4b_32k", 31130), ("qwen3_4b_160k", 163840), ("qwen3_8b_1m_shard", 128451)):
+        w = WORKLOADS[name]
+        assert w.n_rows - w.n_ignored == nv
+
+
+# --- planted mistakes: each must be caught by at least one pin above -------
+
+def _mutants():
+    orig = O.dlogits
+
+    def drop_onehot(z, lse, labels, valid, scale):
+        g = np.exp(z - lse[:, None])
+        return g * (scale * valid)[:, None]
+
+    def flip_sign(z, lse, labels, valid, scale):
+        return -orig(z, lse, labels, valid, scale)
+
+    def forget_scale(z, lse, labels, valid, scale):
+        return orig(z, lse, labels, valid, np.ones_like(scale))
+
+    return {"drop_onehot": drop_onehot, "flip_sign": flip_sign, "forget_scale": forget_scale}
+
+
+@pytest.mark.parametrize("name", ["drop_onehot", "flip_sign", "forget_scale", "transpose_lse", "bias_ignored"])
+def test_planted_mistakes_are_caught(monkeypatch, name):
+    h, w, b, y = _case(17, 8, 33, seed=50, bias=True)
+    if name in ("drop_onehot", "flip_sign", "forget_scale"):
+        monkeypatch.setattr(O, "dlogits", _mutants()[name])
+    elif name == "transpose_lse":
+        monkeypatch.setattr(O, "row_logsumexp", lambda z: np.log(np.exp(z).sum(axis=0))[: z.shape[0]]
+                            if z.shape[1] >= z.shape[0] else np.log(np.exp(z).sum(axis=1)) + 0.1)
+    elif name == "bias_ignored":
+        orig = O.logits
+        monkeypatch.setattr(O, "logits", lambda hh, ww, bb: orig(hh, ww, None))
+    caught = False
+    try:
+        test_matches_torch_cross_entropy((17, 8, 33), True, "mean")
+    except AssertionError:
+        caught = True
+    assert caught, f"planted mistake {name} was not caught"
