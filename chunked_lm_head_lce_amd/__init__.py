@@ -1,0 +1,201 @@
+"""Chunked linear-cross-entropy on MI355X (gfx950): thin Python binding.
+
+The functions here only marshal arguments to the C ABI of ``liblce.so``
+(include/lce.h): they check dtypes and shapes, take device memory and the
+current stream from PyTorch, and call the library. Every step of the loss
+runs in the library's HIP kernels; there is no fallback implementation.
+
+    lce_forward(hidden, weight, bias, labels, ...)          -> LceOutput
+    lce_forward_backward(hidden, weight, bias, labels, ...) -> LceOutput with grads
+
+``chunk_rows`` follows the pages' ``chunk_loss_size`` (LlamaFactory section 2):
+positive, ``None`` meaning one chunk of all rows, anything else a ValueError.
+"""
+from __future__ import annotations
+
+import ctypes
+from dataclasses import dataclass
+
+import torch
+
+from . import _lib
+from ._lib import LceProblem
+
+IGNORE_INDEX = -100
+DEFAULT_CHUNK_ROWS = 256
+
+__all__ = ["lce_forward", "lce_forward_backward", "lce_workspace_bytes", "LceOutput", "LceError",
+           "IGNORE_INDEX", "DEFAULT_CHUNK_ROWS"]
+
+
+class LceError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        super().__init__(f"{where}: {_lib.status_string(code)} (status {code})")
+        self.code = code
+
+
+@dataclass
+class LceOutput:
+    loss: torch.Tensor                  # [] for sum/mean, [N] for none (float32)
+    lse: torch.Tensor | None            # [N] float32
+    chunk_loss: torch.Tensor | None     # [T] float32
+    n_valid: torch.Tensor               # [] int64
+    status: torch.Tensor                # [] int32 (device-side status word)
+    grad_hidden: torch.Tensor | None = None
+    grad_weight: torch.Tensor | None = None
+    grad_bias: torch.Tensor | None = None
+    grad_weight_f32: torch.Tensor | None = None
+    grad_bias_f32: torch.Tensor | None = None
+    workspace_bytes: int = 0
+
+    def check(self) -> "LceOutput":
+        """Synchronise and raise if the device reported a label outside [0, V)."""
+        code = int(self.status.item())
+        if code != _lib.LCE_OK:
+            raise LceError(code, "device status")
+        return self
+
+
+def _ptr(t: torch.Tensor | None) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+def _problem(hidden, weight, labels, ignore_index, chunk_rows, reduction, rows_in_flight) -> LceProblem:
+    if reduction not in _lib.LCE_REDUCTION:
+        raise ValueError(f"reduction must be one of {sorted(_lib.LCE_REDUCTION)}, got {reduction!r}")
+    if hidden.dim() != 2 or weight.dim() != 2 or labels.dim() != 1:
+        raise ValueError("expected hidden [N,H], weight [V,H], labels [N]")
+    n, h = hidden.shape
+    v, hw = weight.shape
+    if hw != h or labels.shape[0] != n:
+        raise ValueError(f"shape mismatch: hidden {tuple(hidden.shape)}, weight {tuple(weight.shape)}, "
+                         f"labels {tuple(labels.shape)}")
+    if hidden.dtype != torch.bfloat16 or weight.dtype != torch.bfloat16:
+        raise ValueError("hidden and weight must be bfloat16")
+    if labels.dtype != torch.int64:
+        raise ValueError("labels must be int64")
+    for name, t in (("hidden", hidden), ("weight", weight)):
+        if t.numel() > 0 and t.stride(1) != 1:
+            raise ValueError(f"{name} rows must be contiguous")
+    if chunk_rows is None:
+        chunk_rows = max(n, 1)
+    if chunk_rows <= 0:
+        raise ValueError("`chunk_rows` must be positive.")
+    p = LceProblem()
+    p.n_rows, p.hidden, p.vocab = n, h, v
+    p.ld_hidden = hidden.stride(0) if n > 1 else h
+    p.ld_weight = weight.stride(0) if v > 1 else h
+    p.ignore_index = ignore_index
+    p.chunk_rows = chunk_rows
+    p.rows_in_flight = rows_in_flight or 0
+    p.reduction = _lib.LCE_REDUCTION[reduction]
+    p.dtype = _lib.LCE_DTYPE_BF16
+    return p
+
+
+def _raise(code: int, where: str):
+    if code == _lib.LCE_ERR_INVALID_ARG:
+        raise ValueError(f"{where}: {_lib.status_string(code)}")
+    raise LceError(code, where)
+
+
+def lce_workspace_bytes(hidden, weight, labels, *, backward: bool, external_f32: bool = False,
+                        ignore_index: int = IGNORE_INDEX, chunk_rows: int | None = DEFAULT_CHUNK_ROWS,
+                        reduction: str = "sum", rows_in_flight: int | None = None) -> int:
+    lib = _lib.load()
+    p = _problem(hidden, weight, labels, ignore_index, chunk_rows, reduction, rows_in_flight)
+    kind = (_lib.LCE_WS_BACKWARD_EXTERNAL_F32 if external_f32 else _lib.LCE_WS_BACKWARD) if backward \
+        else _lib.LCE_WS_FORWARD
+    return int(lib.lce_workspace_bytes(ctypes.byref(p), kind))
+
+
+def _device_checks(*ts):
+    for t in ts:
+        if t is not None and not t.is_cuda:
+            raise ValueError("all tensors must be on the GPU")
+
+
+def _common_outputs(n, reduction, chunk_rows, want_lse, want_chunks, dev):
+    loss = torch.empty((n,) if reduction == "none" else (), dtype=torch.float32, device=dev)
+    lse = torch.empty(n, dtype=torch.float32, device=dev) if want_lse else None
+    t = -(-n // chunk_rows) if n else 0
+    chunk = torch.empty(t, dtype=torch.float32, device=dev) if want_chunks else None
+    n_valid = torch.empty((), dtype=torch.int64, device=dev)
+    status = torch.empty((), dtype=torch.int32, device=dev)
+    return loss, lse, chunk, n_valid, status
+
+
+def lce_forward(hidden: torch.Tensor, weight: torch.Tensor, bias: torch.Tensor | None, labels: torch.Tensor,
+                *, ignore_index: int = IGNORE_INDEX, chunk_rows: int | None = DEFAULT_CHUNK_ROWS,
+                reduction: str = "sum", want_lse: bool = True, want_chunk_loss: bool = False,
+                workspace: torch.Tensor | None = None, out: LceOutput | None = None,
+                trace: "_lib.LceTrace | None" = None) -> LceOutput:
+    """Loss (+ per-row lse, per-chunk sums, valid count) without the [N,V] logits."""
+    lib = _lib.load()
+    _device_checks(hidden, weight, bias, labels)
+    p = _problem(hidden, weight, labels, ignore_index, chunk_rows, reduction, None)
+    dev = hidden.device
+    if out is None:
+        out = LceOutput(*_common_outputs(hidden.shape[0], reduction, p.chunk_rows, want_lse, want_chunk_loss, dev))
+    nbytes = int(lib.lce_workspace_bytes(ctypes.byref(p), _lib.LCE_WS_FORWARD))
+    if workspace is None or workspace.numel() < nbytes:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+    out.workspace_bytes = nbytes
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    code = lib.lce_forward_traced(ctypes.byref(p), _ptr(hidden), _ptr(weight), _ptr(bias), _ptr(labels),
+                                  _ptr(out.loss), _ptr(out.lse), _ptr(out.chunk_loss), _ptr(out.n_valid),
+                                  _ptr(out.status), _ptr(workspace), workspace.numel(), stream,
+                                  None if trace is None else ctypes.byref(trace))
+    if code != _lib.LCE_OK:
+        _raise(code, "lce_forward")
+    return out
+
+
+def lce_forward_backward(hidden: torch.Tensor, weight: torch.Tensor, bias: torch.Tensor | None,
+                         labels: torch.Tensor, *, grad_scale: float = 1.0, ignore_index: int = IGNORE_INDEX,
+                         chunk_rows: int | None = DEFAULT_CHUNK_ROWS, reduction: str = "sum",
+                         want_grad_hidden: bool = True, want_grad_weight: bool = True,
+                         want_grad_bias: bool | None = None, want_f32: bool = False, want_lse: bool = True,
+                         want_chunk_loss: bool = False, rows_in_flight: int | None = None,
+                         workspace: torch.Tensor | None = None, out: LceOutput | None = None,
+                         trace: "_lib.LceTrace | None" = None) -> LceOutput:
+    """Loss and gradients in one call. grad_weight / grad_bias are accumulated
+    in FP32 and cast to bf16 at the end; ``want_f32`` also returns the FP32
+    accumulators (and makes the call use them instead of workspace)."""
+    lib = _lib.load()
+    _device_checks(hidden, weight, bias, labels)
+    if want_grad_bias is None:
+        want_grad_bias = bias is not None
+    if want_grad_bias and bias is None:
+        raise ValueError("grad_bias requested without a bias")
+    p = _problem(hidden, weight, labels, ignore_index, chunk_rows, reduction, rows_in_flight)
+    dev = hidden.device
+    n, h = hidden.shape
+    v = weight.shape[0]
+    if out is None:
+        out = LceOutput(*_common_outputs(n, reduction, p.chunk_rows, want_lse, want_chunk_loss, dev))
+        if want_grad_hidden:
+            out.grad_hidden = torch.empty((n, h), dtype=torch.bfloat16, device=dev)
+        if want_grad_weight:
+            out.grad_weight = torch.empty((v, h), dtype=torch.bfloat16, device=dev)
+            if want_f32:
+                out.grad_weight_f32 = torch.empty((v, h), dtype=torch.float32, device=dev)
+        if want_grad_bias:
+            out.grad_bias = torch.empty(v, dtype=torch.bfloat16, device=dev)
+            if want_f32:
+                out.grad_bias_f32 = torch.empty(v, dtype=torch.float32, device=dev)
+    external = out.grad_weight_f32 is not None or out.grad_weight is None
+    kind = _lib.LCE_WS_BACKWARD_EXTERNAL_F32 if external else _lib.LCE_WS_BACKWARD
+    nbytes = int(lib.lce_workspace_bytes(ctypes.byref(p), kind))
+    if workspace is None or workspace.numel() < nbytes:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+    out.workspace_bytes = nbytes
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    code = lib.lce_forward_backward_traced(
+        ctypes.byref(p), _ptr(hidden), _ptr(weight), _ptr(bias), _ptr(labels), float(grad_scale), _ptr(out.loss),
+        _ptr(out.lse), _ptr(out.chunk_loss), _ptr(out.n_valid), _ptr(out.grad_hidden), _ptr(out.grad_weight),
+        _ptr(out.grad_bias), _ptr(out.grad_weight_f32), _ptr(out.grad_bias_f32), _ptr(out.status),
+        _ptr(workspace), workspace.numel(), stream, None if trace is None else ctypes.byref(trace))
+    if code != _lib.LCE_OK:
+        _raise(code, "lce_forward_backward")
+    return out

@@ -1,0 +1,332 @@
+// Host side of the C ABI declared in include/lce.h: argument validation,
+// workspace carve-up and the launch sequence on the caller's stream. The
+// library allocates nothing and keeps no state.
+#include "../../include/lce.h"
+
+#include <hip/hip_runtime_api.h>
+#include <stdint.h>
+#include <string.h>
+
+#include "lce_internal.h"
+
+namespace {
+
+using lce::Shapes;
+
+constexpr int64_t kTile = 256;
+constexpr int64_t kDefaultRowsInFlight = 16384;
+
+int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+struct Layout {
+  // forward
+  size_t label32 = 0, n_valid = 0, status = 0, zlab = 0, lse = 0, part_m = 0, part_s = 0, chunk_acc = 0;
+  // backward
+  size_t wT = 0, hT = 0, dlog = 0, dlogT = 0, gw_f32 = 0, gb_f32 = 0;
+  size_t total = 0;
+};
+
+int validate_problem(const lce_problem* p) {
+  if (p == nullptr) return LCE_ERR_INVALID_ARG;
+  if (p->n_rows < 0 || p->hidden <= 0 || p->vocab <= 0) return LCE_ERR_INVALID_ARG;
+  if (p->ld_hidden < p->hidden || p->ld_weight < p->hidden) return LCE_ERR_INVALID_ARG;
+  if (p->chunk_rows <= 0) return LCE_ERR_INVALID_ARG;
+  if (p->rows_in_flight < 0) return LCE_ERR_INVALID_ARG;
+  if (p->reduction < LCE_REDUCTION_NONE || p->reduction > LCE_REDUCTION_MEAN) return LCE_ERR_INVALID_ARG;
+  if (p->dtype != LCE_DTYPE_BF16) return LCE_ERR_UNSUPPORTED;
+  if (p->hidden % 64 != 0) return LCE_ERR_UNSUPPORTED;
+  if (p->ld_hidden % 8 != 0 || p->ld_weight % 8 != 0) return LCE_ERR_UNSUPPORTED;
+  // labels and tile indices are 32-bit on the device
+  if (p->vocab > (int64_t)INT32_MAX - 1024 || p->n_rows > (int64_t)INT32_MAX - 1024) return LCE_ERR_UNSUPPORTED;
+  const int64_t tiles = round_up(p->n_rows, kTile) / kTile * (round_up(p->vocab, kTile) / kTile);
+  if (tiles > (int64_t)INT32_MAX) return LCE_ERR_UNSUPPORTED;
+  return LCE_OK;
+}
+
+Shapes shapes_of(const lce_problem* p) {
+  Shapes s;
+  s.N = p->n_rows;
+  s.Np = round_up(p->n_rows, kTile);
+  s.H = p->hidden;
+  s.V = p->vocab;
+  s.Vp = round_up(p->vocab, kTile);
+  s.ldh = p->ld_hidden;
+  s.ldw = p->ld_weight;
+  s.chunk_rows = p->chunk_rows;
+  return s;
+}
+
+int64_t group_rows(const lce_problem* p, const Shapes& s) {
+  int64_t g = p->rows_in_flight > 0 ? p->rows_in_flight : kDefaultRowsInFlight;
+  g = round_up(g, kTile);
+  return g < s.Np ? g : s.Np;
+}
+
+int64_t n_chunks(const lce_problem* p) { return (p->n_rows + p->chunk_rows - 1) / p->chunk_rows; }
+
+Layout make_layout(const lce_problem* p, int kind) {
+  const Shapes s = shapes_of(p);
+  Layout L;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off = align256(off + bytes);
+    return at;
+  };
+  const int64_t n_vt = s.Vp / kTile;
+  L.label32 = take((size_t)s.Np * 4);
+  L.n_valid = take(8);
+  L.status = take(4);
+  L.zlab = take((size_t)s.Np * 4);
+  L.lse = take((size_t)s.Np * 4);
+  L.part_m = take((size_t)n_vt * s.Np * 4);
+  L.part_s = take((size_t)n_vt * s.Np * 4);
+  L.chunk_acc = take((size_t)n_chunks(p) * 8);
+  if (kind == LCE_WS_BACKWARD || kind == LCE_WS_BACKWARD_EXTERNAL_F32) {
+    const int64_t G = group_rows(p, s);
+    L.wT = take((size_t)s.H * s.Vp * 2);
+    L.hT = take((size_t)s.H * G * 2);
+    L.dlog = take((size_t)G * s.Vp * 2);
+    L.dlogT = take((size_t)s.Vp * G * 2);
+    L.gb_f32 = take((size_t)s.Vp * 4);
+    if (kind == LCE_WS_BACKWARD) L.gw_f32 = take((size_t)s.V * s.H * 4);
+  }
+  L.total = off;
+  return L;
+}
+
+bool aligned(const void* ptr, size_t a) { return ((uintptr_t)ptr % a) == 0; }
+
+#define LCE_TRY(expr)                       \
+  do {                                      \
+    if ((expr) != hipSuccess) return LCE_ERR_HIP; \
+  } while (0)
+
+// Optional per-launch event recording (lce_trace in include/lce.h).
+struct Tracer {
+  lce_trace* t = nullptr;
+  hipStream_t st = nullptr;
+  bool pending = false;
+  void before(int kind, int64_t m, int64_t n, int64_t k) {
+    if (t == nullptr || t->count >= t->capacity) return;
+    if (hipEventRecord(t->events[2 * t->count], st) != hipSuccess) return;
+    t->kinds[t->count] = kind;
+    if (t->dims) {
+      t->dims[3 * t->count] = m;
+      t->dims[3 * t->count + 1] = n;
+      t->dims[3 * t->count + 2] = k;
+    }
+    pending = true;
+  }
+  void after() {
+    if (!pending) return;
+    pending = false;
+    if (hipEventRecord(t->events[2 * t->count + 1], st) == hipSuccess) t->count++;
+  }
+};
+
+#define LCE_LAUNCH(tr, kind, m, n, k, call) \
+  do {                                      \
+    (tr).before((kind), (m), (n), (k));     \
+    const hipError_t e_ = (call);           \
+    (tr).after();                           \
+    if (e_ != hipSuccess) return LCE_ERR_HIP; \
+  } while (0)
+
+struct Common {
+  const lce_problem* p;
+  Shapes s;
+  Layout L;
+  char* ws;
+  int32_t* label32;
+  unsigned long long* n_valid;
+  int32_t* status;
+  float* lse_ws;
+  double* chunk_acc;
+  int64_t T;
+};
+
+int check_common(const lce_problem* p, const void* hidden, const void* weight, const void* bias,
+                 const int64_t* labels, const float* loss, void* workspace, size_t workspace_bytes, int kind,
+                 Common& c) {
+  int st = validate_problem(p);
+  if (st != LCE_OK) return st;
+  if (loss == nullptr) return LCE_ERR_INVALID_ARG;
+  if (p->n_rows > 0 && (hidden == nullptr || labels == nullptr)) return LCE_ERR_INVALID_ARG;
+  if (weight == nullptr) return LCE_ERR_INVALID_ARG;
+  if (!aligned(hidden, 16) || !aligned(weight, 16) || !aligned(bias, 2) || !aligned(labels, 8))
+    return LCE_ERR_UNSUPPORTED;
+  c.p = p;
+  c.s = shapes_of(p);
+  c.L = make_layout(p, kind);
+  if (c.L.total > 0 && (workspace == nullptr || workspace_bytes < c.L.total)) return LCE_ERR_WORKSPACE;
+  if (!aligned(workspace, 16)) return LCE_ERR_WORKSPACE;
+  c.ws = (char*)workspace;
+  c.T = n_chunks(p);
+  return LCE_OK;
+}
+
+// Steps a1..a6 of the method: count and validate labels, logits tiles with the
+// online log-sum-exp epilogue, per-row lse / NLL / chunk sums.
+int run_forward(Common& c, const void* hidden, const void* weight, const void* bias, const int64_t* labels,
+                float* loss, float* lse_out, int64_t* n_valid_out, int32_t* status_out, hipStream_t st,
+                Tracer& tr) {
+  const Shapes& s = c.s;
+  char* ws = c.ws;
+  c.label32 = (int32_t*)(ws + c.L.label32);
+  c.n_valid = n_valid_out ? (unsigned long long*)n_valid_out : (unsigned long long*)(ws + c.L.n_valid);
+  c.status = status_out ? status_out : (int32_t*)(ws + c.L.status);
+  c.lse_ws = (float*)(ws + c.L.lse);
+  c.chunk_acc = (double*)(ws + c.L.chunk_acc);
+  float* part_m = (float*)(ws + c.L.part_m);
+  float* part_s = (float*)(ws + c.L.part_s);
+  float* zlab = (float*)(ws + c.L.zlab);
+
+  LCE_LAUNCH(tr, LCE_K_ZERO, 0, 0, 0, lce::launch_zero(c.n_valid, 8, st));
+  LCE_LAUNCH(tr, LCE_K_ZERO, 0, 0, 0, lce::launch_zero(c.status, 4, st));
+  LCE_LAUNCH(tr, LCE_K_ZERO, 0, 0, 0, lce::launch_zero(c.chunk_acc, c.T * 8, st));
+  if (s.N == 0) return LCE_OK;
+  LCE_LAUNCH(tr, LCE_K_PREPARE_LABELS, 0, 0, 0,
+             lce::launch_prepare_labels(labels, s.N, s.Np, s.V, c.p->ignore_index, c.label32, c.n_valid,
+                                        c.status, st));
+  LCE_LAUNCH(tr, LCE_K_FWD_LSE, s.N, s.V, s.H,
+             lce::launch_fwd_lse(s, hidden, weight, bias, c.label32, part_m, part_s, zlab, st));
+  LCE_LAUNCH(tr, LCE_K_FINALIZE_ROWS, 0, 0, 0,
+             lce::launch_finalize_rows(s, part_m, part_s, zlab, c.label32, c.status, c.p->reduction, c.lse_ws,
+                                       lse_out, c.p->reduction == LCE_REDUCTION_NONE ? loss : nullptr,
+                                       c.chunk_acc, st));
+  return LCE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int lce_abi_version(void) { return 100; }
+
+const char* lce_status_string(int status) {
+  switch (status) {
+    case LCE_OK: return "ok";
+    case LCE_ERR_INVALID_ARG: return "invalid argument";
+    case LCE_ERR_UNSUPPORTED: return "unsupported configuration";
+    case LCE_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
+    case LCE_ERR_HIP: return "HIP launch failed";
+    case LCE_ERR_LABEL_RANGE: return "label outside [0, vocab) that is not ignore_index";
+    default: return "unknown status";
+  }
+}
+
+size_t lce_workspace_bytes(const lce_problem* p, int kind) {
+  if (validate_problem(p) != LCE_OK) return 0;
+  if (kind < LCE_WS_FORWARD || kind > LCE_WS_BACKWARD_EXTERNAL_F32) return 0;
+  return make_layout(p, kind).total;
+}
+
+int lce_forward_traced(const lce_problem* p, const void* hidden, const void* weight, const void* bias,
+                       const int64_t* labels, float* loss, float* lse, float* chunk_loss, int64_t* n_valid,
+                       int32_t* status, void* workspace, size_t workspace_bytes, hipStream_t stream,
+                       lce_trace* trace) {
+  Common c;
+  int st = check_common(p, hidden, weight, bias, labels, loss, workspace, workspace_bytes, LCE_WS_FORWARD, c);
+  if (st != LCE_OK) return st;
+  Tracer tr;
+  tr.t = trace;
+  tr.st = stream;
+  if (trace) trace->count = 0;
+  st = run_forward(c, hidden, weight, bias, labels, loss, lse, n_valid, status, stream, tr);
+  if (st != LCE_OK) return st;
+  LCE_LAUNCH(tr, LCE_K_FINALIZE_LOSS, 0, 0, 0,
+             lce::launch_finalize_loss(c.chunk_acc, c.T, c.n_valid, c.status, p->reduction, loss, chunk_loss,
+                                       stream));
+  return LCE_OK;
+}
+
+int lce_forward(const lce_problem* p, const void* hidden, const void* weight, const void* bias,
+                const int64_t* labels, float* loss, float* lse, float* chunk_loss, int64_t* n_valid,
+                int32_t* status, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return lce_forward_traced(p, hidden, weight, bias, labels, loss, lse, chunk_loss, n_valid, status, workspace,
+                            workspace_bytes, stream, nullptr);
+}
+
+int lce_forward_backward_traced(const lce_problem* p, const void* hidden, const void* weight, const void* bias,
+                                const int64_t* labels, float grad_scale, float* loss, float* lse,
+                                float* chunk_loss, int64_t* n_valid, void* grad_hidden, void* grad_weight,
+                                void* grad_bias, float* grad_weight_f32, float* grad_bias_f32, int32_t* status,
+                                void* workspace, size_t workspace_bytes, hipStream_t stream, lce_trace* trace) {
+  int st = validate_problem(p);
+  if (st != LCE_OK) return st;
+  if (p->reduction == LCE_REDUCTION_NONE) return LCE_ERR_UNSUPPORTED;
+  if ((grad_bias != nullptr || grad_bias_f32 != nullptr) && bias == nullptr) return LCE_ERR_INVALID_ARG;
+  if (!aligned(grad_hidden, 2) || !aligned(grad_weight, 2) || !aligned(grad_bias, 2) ||
+      !aligned(grad_weight_f32, 4) || !aligned(grad_bias_f32, 4))
+    return LCE_ERR_UNSUPPORTED;
+  const bool need_gh = grad_hidden != nullptr && p->n_rows > 0;
+  const bool need_gw = grad_weight != nullptr || grad_weight_f32 != nullptr;
+  const bool need_gb = grad_bias != nullptr || grad_bias_f32 != nullptr;
+  const int kind = (need_gw && grad_weight_f32 == nullptr) ? LCE_WS_BACKWARD : LCE_WS_BACKWARD_EXTERNAL_F32;
+  Common c;
+  st = check_common(p, hidden, weight, bias, labels, loss, workspace, workspace_bytes, kind, c);
+  if (st != LCE_OK) return st;
+  Tracer tr;
+  tr.t = trace;
+  tr.st = stream;
+  if (trace) trace->count = 0;
+  st = run_forward(c, hidden, weight, bias, labels, loss, lse, n_valid, status, stream, tr);
+  if (st != LCE_OK) return st;
+
+  const Shapes& s = c.s;
+  char* ws = c.ws;
+  float* gw = grad_weight_f32 ? grad_weight_f32 : (float*)(ws + c.L.gw_f32);
+  float* gb = grad_bias_f32 ? grad_bias_f32 : (float*)(ws + c.L.gb_f32);
+  if (need_gb) LCE_LAUNCH(tr, LCE_K_ZERO, 0, 0, 0, lce::launch_zero(gb, s.V * 4, stream));
+  if (s.N == 0) {
+    if (need_gw) LCE_LAUNCH(tr, LCE_K_ZERO, 0, 0, 0, lce::launch_zero(gw, s.V * s.H * 4, stream));
+  } else if (need_gh || need_gw || need_gb) {
+    const int64_t G = group_rows(p, s);
+    void* wT = ws + c.L.wT;
+    void* hT = ws + c.L.hT;
+    void* dlog = ws + c.L.dlog;
+    void* dlogT = ws + c.L.dlogT;
+    const int is_mean = p->reduction == LCE_REDUCTION_MEAN;
+    if (need_gh)
+      LCE_LAUNCH(tr, LCE_K_TRANSPOSE, 0, 0, 0,
+                 lce::launch_transpose(weight, s.ldw, 0, s.V, s.H, wT, s.Vp, s.Vp, stream));
+    for (int64_t g0 = 0; g0 < s.Np; g0 += G) {
+      const int64_t Gc = (s.Np - g0) < G ? (s.Np - g0) : G;
+      const int64_t rows_valid = (s.N - g0) < Gc ? (s.N - g0) : Gc;
+      LCE_LAUNCH(tr, LCE_K_BWD_DLOGITS, rows_valid, s.V, s.H,
+                 lce::launch_bwd_dlogits(s, hidden, weight, bias, c.label32, c.lse_ws, c.n_valid, grad_scale,
+                                         is_mean, g0, Gc, need_gh ? dlog : nullptr, need_gw ? dlogT : nullptr,
+                                         need_gb ? gb : nullptr, stream));
+      if (need_gh)
+        LCE_LAUNCH(tr, LCE_K_GRAD_HIDDEN, rows_valid, s.H, s.V,
+                   lce::launch_grad_hidden(s, dlog, wT, g0, Gc, grad_hidden, stream));
+      if (need_gw) {
+        LCE_LAUNCH(tr, LCE_K_TRANSPOSE, 0, 0, 0,
+                   lce::launch_transpose(hidden, s.ldh, g0, rows_valid, s.H, hT, Gc, Gc, stream));
+        LCE_LAUNCH(tr, LCE_K_GRAD_WEIGHT, s.V, s.H, rows_valid,
+                   lce::launch_grad_weight(s, dlogT, hT, Gc, g0 == 0 ? 1 : 0, gw, stream));
+      }
+    }
+  }
+  if (need_gw && grad_weight)
+    LCE_LAUNCH(tr, LCE_K_CAST, 0, 0, 0, lce::launch_cast(gw, grad_weight, s.V * s.H, stream));
+  if (need_gb && grad_bias) LCE_LAUNCH(tr, LCE_K_CAST, 0, 0, 0, lce::launch_cast(gb, grad_bias, s.V, stream));
+  LCE_LAUNCH(tr, LCE_K_FINALIZE_LOSS, 0, 0, 0,
+             lce::launch_finalize_loss(c.chunk_acc, c.T, c.n_valid, c.status, p->reduction, loss, chunk_loss,
+                                       stream));
+  return LCE_OK;
+}
+
+int lce_forward_backward(const lce_problem* p, const void* hidden, const void* weight, const void* bias,
+                         const int64_t* labels, float grad_scale, float* loss, float* lse, float* chunk_loss,
+                         int64_t* n_valid, void* grad_hidden, void* grad_weight, void* grad_bias,
+                         float* grad_weight_f32, float* grad_bias_f32, int32_t* status, void* workspace,
+                         size_t workspace_bytes, hipStream_t stream) {
+  return lce_forward_backward_traced(p, hidden, weight, bias, labels, grad_scale, loss, lse, chunk_loss, n_valid,
+                                     grad_hidden, grad_weight, grad_bias, grad_weight_f32, grad_bias_f32, status,
+                                     workspace, workspace_bytes, stream, nullptr);
+}
+
+}  // extern "C"

@@ -1,0 +1,599 @@
+// Device kernels of the chunked linear-cross-entropy library, written for
+// gfx950 (CDNA4, MI355X): 64-lane wavefronts, v_mfma_f32_32x32x16_bf16,
+// 160 KB of LDS per workgroup, direct global->LDS loads.
+//
+// What is computed (LlamaFactory PR #10762 analysis, section 4; TRL
+// "training on 1M+ tokens", section "chunking"):
+//   z = h W^T + b, lse_i = log sum_j exp z_ij, l_i = valid_i (lse_i - z_{i,y_i}),
+//   G = s valid (softmax - onehot), grad_hidden = G W, grad_weight = G^T h,
+//   grad_bias = sum_i G_i  (FP32 accumulation, one cast at the end).
+//
+// Every contraction runs through one bf16 MFMA tile routine that computes
+//   C[m][n] = sum_k X[m][k] * Y[n][k]        (both operands K-contiguous)
+// for a 256 x 256 output tile, so the kernels differ only in their operands
+// and epilogues:
+//   forward   z tile   X = hidden rows,    Y = weight rows,      K = H
+//   backward  z tile   (same, recomputed), epilogue writes dlogits (bf16)
+//             grad_hidden  X = dlogits [G][Vp], Y = W^T [H][Vp],  K = Vp
+//             grad_weight  X = dlogits^T [Vp][G], Y = h^T [H][G], K = G
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <math.h>
+
+#include "lce_internal.h"
+
+#define LDS_AS __attribute__((address_space(3)))
+
+namespace lce {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint16_t u16;
+
+constexpr int TILE = 256;                 // output tile edge (rows and columns)
+constexpr int BK = 64;                    // K depth of one LDS stage
+constexpr int NTHREADS = 256;             // 4 waves, 2 x 2, each owns 128 x 128
+constexpr int OPERAND_STAGE = TILE * BK * 2;       // 32 KB: one operand, one stage
+constexpr int STAGE = 2 * OPERAND_STAGE;           // 64 KB: both operands
+constexpr int MAINLOOP_LDS = 2 * STAGE;            // 128 KB: double buffered
+constexpr float LOG2E = 1.4426950408889634f;       // log2(e): exp(x) = 2^(x log2 e)
+
+__device__ __forceinline__ float bf2f(u16 u) { return __builtin_bit_cast(float, (uint32_t)u << 16); }
+__device__ __forceinline__ u16 f2bf(float x) {
+  __bf16 b = (__bf16)x;                    // v_cvt_pk_bf16_f32: round to nearest even
+  return __builtin_bit_cast(u16, b);
+}
+__device__ __forceinline__ float exp_fast(float x) { return __builtin_amdgcn_exp2f(x * LOG2E); }
+
+__device__ __forceinline__ float max32(float v) {
+#pragma unroll
+  for (int o = 16; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+__device__ __forceinline__ float sum32(float v) {
+#pragma unroll
+  for (int o = 16; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+// ---------------------------------------------------------------------------
+// Tile order. Workgroups are dispatched round-robin over the 8 XCDs, so
+// dispatch id b runs on XCD b % 8. Remap so each XCD walks a contiguous range
+// of logical tiles, and walk them GROUP_M row-tiles at a time across all
+// column tiles, so concurrently running tiles on one XCD share operand panels
+// in that XCD's L2.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void tile_coords(int n_m, int n_n, int& tm, int& tn) {
+  const int nb = gridDim.x;
+  int t = blockIdx.x;
+  if ((nb & 7) == 0) t = (t & 7) * (nb >> 3) + (t >> 3);
+  constexpr int GROUP_M = 4;
+  const int per_group = GROUP_M * n_n;
+  const int g = t / per_group;
+  const int first_m = g * GROUP_M;
+  const int gm = min(n_m - first_m, GROUP_M);
+  const int in_g = t - g * per_group;
+  tm = first_m + in_g % gm;
+  tn = in_g / gm;
+}
+
+// ---------------------------------------------------------------------------
+// LDS stage layout: operand tile [256 rows][64 k] bf16, 128 B per row, the
+// eight 16-byte k-chunks of row r stored at chunk slot (c ^ (r & 7)) so that
+// the eight rows read together by a fragment load hit distinct banks.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int lds_off(int r, int c) { return r * 128 + ((c ^ (r & 7)) << 4); }
+
+// Direct global->LDS fill of one operand stage. One global_load_lds_dwordx4
+// writes 64 x 16 B contiguously (lane i at +16 i), i.e. 8 tile rows; lane i
+// therefore fetches logical chunk (i & 7) ^ (i >> 3) of row (i >> 3) of its
+// 8-row block. Rows past the operand's end are clamped to its last row (the
+// values are finite and the epilogues discard them).
+__device__ __forceinline__ void stage_fill(const u16* __restrict__ base, int64_t ld, int64_t row0,
+                                           int64_t nrows, int64_t k0, LDS_AS char* dst, int wave,
+                                           int lane) {
+  const int r_in = lane >> 3;
+  const int c = (lane & 7) ^ r_in;
+#pragma unroll
+  for (int b = 0; b < 8; ++b) {
+    const int r = wave * 64 + b * 8 + r_in;
+    int64_t gr = row0 + r;
+    gr = gr < nrows ? gr : nrows - 1;
+    const u16* src = base + gr * ld + k0 + c * 8;
+    __builtin_amdgcn_global_load_lds((const void*)src, (LDS_AS void*)(dst + (wave * 64 + b * 8) * 128),
+                                     16, 0, 0);
+  }
+}
+
+__device__ __forceinline__ bf16x8 frag(const LDS_AS char* stage, int r, int c) {
+  return *(const LDS_AS bf16x8*)(stage + lds_off(r, c));
+}
+
+struct Acc {
+  f32x16 v[4][4];   // [row block i][col block j], 32 x 32 each
+};
+
+// Accumulator layout (v_mfma_f32_32x32x16_bf16): lane l, register r of block
+// (i, j) of wave (wm, wn) holds C[row][col] with
+//   row = wm*128 + i*32 + 8*(r/4) + 4*(l/32) + (r%4),   col = wn*128 + j*32 + (l%32).
+__device__ __forceinline__ int acc_row(int wm, int i, int r, int lane) {
+  return wm * 128 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+}
+__device__ __forceinline__ int acc_col(int wn, int j, int lane) { return wn * 128 + j * 32 + (lane & 31); }
+
+// C tile (256 x 256, fp32 in registers) = X[x_row0 : +256][0:K] * Y[y_row0 : +256][0:K]^T.
+// K % 64 == 0. smem must hold MAINLOOP_LDS bytes. Ends with a barrier, after
+// which smem may be reused.
+__device__ __forceinline__ void gemm_tile(Acc& acc, const u16* __restrict__ X, int64_t ldx, int64_t x_row0,
+                                          int64_t x_rows, const u16* __restrict__ Y, int64_t ldy,
+                                          int64_t y_row0, int64_t y_rows, int64_t K, LDS_AS char* smem) {
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int wm = wave >> 1, wn = wave & 1;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc.v[i][j][r] = 0.f;
+
+  const int nk = (int)(K / BK);
+  stage_fill(X, ldx, x_row0, x_rows, 0, smem, wave, lane);
+  stage_fill(Y, ldy, y_row0, y_rows, 0, smem + OPERAND_STAGE, wave, lane);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  for (int kt = 0; kt < nk; ++kt) {
+    LDS_AS char* cur = smem + (kt & 1) * STAGE;
+    if (kt + 1 < nk) {
+      LDS_AS char* nxt = smem + ((kt + 1) & 1) * STAGE;
+      stage_fill(X, ldx, x_row0, x_rows, (int64_t)(kt + 1) * BK, nxt, wave, lane);
+      stage_fill(Y, ldy, y_row0, y_rows, (int64_t)(kt + 1) * BK, nxt + OPERAND_STAGE, wave, lane);
+    }
+#pragma unroll
+    for (int kk = 0; kk < BK / 16; ++kk) {
+      const int c = kk * 2 + (lane >> 5);
+      bf16x8 a[4], b[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) a[i] = frag(cur, wm * 128 + i * 32 + (lane & 31), c);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) b[j] = frag(cur + OPERAND_STAGE, wn * 128 + j * 32 + (lane & 31), c);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc.v[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc.v[i][j], 0, 0, 0);
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Small kernels
+// ---------------------------------------------------------------------------
+__global__ void k_zero(uint32_t* __restrict__ p, int64_t n_words) {
+  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t s = (int64_t)gridDim.x * blockDim.x;
+  for (; i < n_words; i += s) p[i] = 0u;
+}
+
+// label32[i] = y_i if valid and in range, else -1 (rows N..Np-1 too).
+// n_valid += #valid rows; *status = LCE_ERR_LABEL_RANGE if any label is out of range.
+__global__ void __launch_bounds__(256) k_prepare_labels(const int64_t* __restrict__ labels, int64_t N,
+                                                        int64_t V, int64_t ignore_index,
+                                                        int32_t* __restrict__ label32,
+                                                        unsigned long long* __restrict__ n_valid,
+                                                        int32_t* __restrict__ status) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  int lab = -1, bad = 0;
+  if (i < N) {
+    const int64_t y = labels[i];
+    if (y != ignore_index) {
+      if (y >= 0 && y < V) lab = (int)y;
+      else bad = 1;
+    }
+  }
+  label32[i] = lab;
+  const int cnt = __syncthreads_count(lab >= 0);
+  const int anybad = __syncthreads_or(bad);
+  if (threadIdx.x == 0) {
+    if (cnt) atomicAdd(n_valid, (unsigned long long)cnt);
+    if (anybad) *status = 5;  // LCE_ERR_LABEL_RANGE
+  }
+}
+
+// Forward tile: z = h W^T + b for 256 rows x 256 vocabulary ids, reduced in
+// the epilogue to each row's (max, sum exp(z - max)) over the tile, plus the
+// label logit for rows whose label falls in the tile. z never leaves registers.
+__global__ void __launch_bounds__(NTHREADS, 1)
+k_fwd_lse(const u16* __restrict__ hidden, int64_t ldh, const u16* __restrict__ weight, int64_t ldw,
+          const u16* __restrict__ bias, const int32_t* __restrict__ label32, int64_t N, int64_t Np,
+          int64_t V, int64_t H, int n_mt, int n_vt, float* __restrict__ part_m,
+          float* __restrict__ part_s, float* __restrict__ zlab) {
+  __shared__ __attribute__((aligned(16))) char smem_raw[MAINLOOP_LDS];
+  __shared__ float s_bias[TILE];
+  __shared__ int s_lab[TILE];
+  __shared__ float s_red_m[2][TILE];
+  __shared__ float s_red_s[2][TILE];
+  LDS_AS char* smem = (LDS_AS char*)smem_raw;
+
+  int tm, tn;
+  tile_coords(n_mt, n_vt, tm, tn);
+  const int64_t row0 = (int64_t)tm * TILE, col0 = (int64_t)tn * TILE;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int wm = wave >> 1, wn = wave & 1;
+  s_lab[tid] = label32[row0 + tid];
+  s_bias[tid] = (bias != nullptr && col0 + tid < V) ? bf2f(bias[col0 + tid]) : 0.f;
+
+  Acc acc;
+  gemm_tile(acc, hidden, ldh, row0, N, weight, ldw, col0, V, H, smem);
+
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int rl = acc_row(wm, i, r, lane);
+      const int lab = s_lab[rl];
+      float v[4];
+      float m = -INFINITY;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int cl = acc_col(wn, j, lane);
+        const bool ok = col0 + cl < V;
+        const float z = acc.v[i][j][r] + s_bias[cl];
+        v[j] = ok ? z : -INFINITY;
+        m = fmaxf(m, v[j]);
+        if (ok && (int64_t)lab == col0 + cl) zlab[row0 + rl] = z;
+      }
+      m = max32(m);
+      float s = 0.f;
+      if (m != -INFINITY) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) s += exp_fast(v[j] - m);
+      }
+      s = sum32(s);
+      if ((lane & 31) == 0) {
+        s_red_m[wn][rl] = m;
+        s_red_s[wn][rl] = s;
+      }
+    }
+  }
+  __syncthreads();
+  {
+    const float m0 = s_red_m[0][tid], m1 = s_red_m[1][tid];
+    const float s0 = s_red_s[0][tid], s1 = s_red_s[1][tid];
+    const float M = fmaxf(m0, m1);   // m0 is finite: column 0 of every tile is < V
+    float S = s0 * exp_fast(m0 - M);
+    if (m1 != -INFINITY) S += s1 * exp_fast(m1 - M);
+    part_m[(int64_t)tn * Np + row0 + tid] = M;
+    part_s[(int64_t)tn * Np + row0 + tid] = S;
+  }
+}
+
+// Per row: merge the tiles' (max, sumexp) into lse, form l_i, write lse (and
+// l_i for reduction NONE), and add l_i into its chunk's float64 sum.
+__global__ void __launch_bounds__(256) k_finalize_rows(
+    const float* __restrict__ part_m, const float* __restrict__ part_s, const float* __restrict__ zlab,
+    const int32_t* __restrict__ label32, int64_t N, int64_t Np, int n_vt, int64_t chunk_rows,
+    const int32_t* __restrict__ status, int reduction, float* __restrict__ lse_ws,
+    float* __restrict__ lse_out, float* __restrict__ rowloss_out, double* __restrict__ chunk_acc) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= Np) return;
+  if (i >= N) {
+    lse_ws[i] = 0.f;
+    return;
+  }
+  float M = -INFINITY;
+  for (int t = 0; t < n_vt; ++t) M = fmaxf(M, part_m[(int64_t)t * Np + i]);
+  float S = 0.f;
+  for (int t = 0; t < n_vt; ++t) S += part_s[(int64_t)t * Np + i] * exp_fast(part_m[(int64_t)t * Np + i] - M);
+  const float lse = M + logf(S);
+  const int lab = label32[i];
+  const float l = lab >= 0 ? lse - zlab[i] : 0.f;
+  lse_ws[i] = lse;
+  if (lse_out) lse_out[i] = lse;
+  if (reduction == 0 && rowloss_out) rowloss_out[i] = (*status != 0) ? NAN : l;
+  atomicAdd(&chunk_acc[i / chunk_rows], (double)l);
+}
+
+// One block: total loss from the chunk sums (float64), MEAN scaling, NaN on a
+// device-side label error; optional per-chunk output.
+__global__ void __launch_bounds__(256) k_finalize_loss(const double* __restrict__ chunk_acc, int64_t T,
+                                                       const unsigned long long* __restrict__ n_valid,
+                                                       const int32_t* __restrict__ status, int reduction,
+                                                       float* __restrict__ loss, float* __restrict__ chunk_out) {
+  __shared__ double s_part[256];
+  double acc = 0.0;
+  for (int64_t k = threadIdx.x; k < T; k += 256) {
+    const double c = chunk_acc[k];
+    acc += c;
+    if (chunk_out) chunk_out[k] = (float)c;
+  }
+  s_part[threadIdx.x] = acc;
+  __syncthreads();
+  for (int o = 128; o >= 1; o >>= 1) {
+    if ((int)threadIdx.x < o) s_part[threadIdx.x] += s_part[threadIdx.x + o];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0 && reduction != 0) {
+    double total = s_part[0];
+    if (reduction == 2) {
+      const unsigned long long nv = *n_valid;
+      total /= (double)(nv > 0 ? nv : 1ull);
+    }
+    loss[0] = (*status != 0) ? NAN : (float)total;
+  }
+}
+
+// out[c][r_out] = in[r0 + r_out][c] for r_out < R_valid (else 0), c < C, r_out < R_pad.
+__global__ void __launch_bounds__(256) k_transpose(const u16* __restrict__ in, int64_t ld_in, int64_t r0,
+                                                   int64_t R_valid, int64_t C, u16* __restrict__ out,
+                                                   int64_t ld_out, int64_t R_pad) {
+  __shared__ u16 t[64][66];
+  const int64_t cb = (int64_t)blockIdx.x * 64, rb = (int64_t)blockIdx.y * 64;
+  const int tid = threadIdx.x;
+  {
+    const int rr = tid >> 2, cc = (tid & 3) * 16;
+    const int64_t r = rb + rr;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int64_t c = cb + cc + e;
+      t[rr][cc + e] = (r < R_valid && c < C) ? in[(r0 + r) * ld_in + c] : (u16)0;
+    }
+  }
+  __syncthreads();
+  {
+    const int co = tid >> 2, ro = (tid & 3) * 16;
+    const int64_t c = cb + co;
+    if (c < C) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int64_t r = rb + ro + e;
+        if (r < R_pad) out[c * ld_out + r] = t[ro + e][co];
+      }
+    }
+  }
+}
+
+// Backward tile for one row group: recompute z for 256 rows x 256 ids, form
+// G = s valid (softmax - onehot) in registers, add its column sums into the
+// FP32 bias gradient, and write G (bf16) in the two layouts the gradient
+// products read: dlog [G][Vp] (vocabulary contiguous) and dlogT [Vp][G]
+// (rows contiguous). Rows >= N and ids >= V get exact zeros.
+__global__ void __launch_bounds__(NTHREADS, 1)
+k_bwd_dlogits(const u16* __restrict__ hidden, int64_t ldh, const u16* __restrict__ weight, int64_t ldw,
+              const u16* __restrict__ bias, const int32_t* __restrict__ label32,
+              const float* __restrict__ lse_ws, const unsigned long long* __restrict__ n_valid,
+              float grad_scale, int is_mean, int64_t N, int64_t V, int64_t Vp, int64_t H, int64_t g0,
+              int64_t G, int n_mt, int n_vt, u16* __restrict__ dlog, u16* __restrict__ dlogT,
+              float* __restrict__ gb_f32) {
+  __shared__ __attribute__((aligned(16))) char smem_raw[MAINLOOP_LDS];
+  __shared__ float s_bias[TILE];
+  __shared__ int s_lab[TILE];
+  __shared__ float s_lse[TILE];
+  __shared__ float s_gb[2][TILE];
+  LDS_AS char* smem = (LDS_AS char*)smem_raw;
+
+  int tm, tn;
+  tile_coords(n_mt, n_vt, tm, tn);
+  const int64_t lrow0 = (int64_t)tm * TILE;       // row inside the group
+  const int64_t row0 = g0 + lrow0;                 // global row
+  const int64_t col0 = (int64_t)tn * TILE;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int wm = wave >> 1, wn = wave & 1;
+  s_lab[tid] = label32[row0 + tid];
+  s_lse[tid] = lse_ws[row0 + tid];
+  s_bias[tid] = (bias != nullptr && col0 + tid < V) ? bf2f(bias[col0 + tid]) : 0.f;
+
+  Acc acc;
+  gemm_tile(acc, hidden, ldh, row0, N, weight, ldw, col0, V, H, smem);
+
+  float scale = grad_scale;
+  if (is_mean) {
+    const unsigned long long nv = *n_valid;
+    scale = grad_scale / (float)(nv > 0 ? nv : 1ull);
+  }
+  float colsum[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      float d[4][4];   // [j][r & 3]
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const int r = q * 4 + rr;
+        const int rl = acc_row(wm, i, r, lane);
+        const int lab = s_lab[rl];
+        const float lse = s_lse[rl];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int cl = acc_col(wn, j, lane);
+          const int64_t col = col0 + cl;
+          const float z = acc.v[i][j][r] + s_bias[cl];
+          const float p = exp_fast(z - lse);
+          float g = scale * (p - ((int64_t)lab == col ? 1.f : 0.f));
+          g = (lab >= 0 && col < V) ? g : 0.f;
+          d[j][rr] = g;
+          colsum[j] += g;
+          if (dlog) dlog[(lrow0 + rl) * Vp + col] = f2bf(g);
+        }
+      }
+      if (dlogT) {
+        const int rbase = acc_row(wm, i, q * 4, lane);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int64_t col = col0 + acc_col(wn, j, lane);
+          uint2 pk;
+          pk.x = (uint32_t)f2bf(d[j][0]) | ((uint32_t)f2bf(d[j][1]) << 16);
+          pk.y = (uint32_t)f2bf(d[j][2]) | ((uint32_t)f2bf(d[j][3]) << 16);
+          *(uint2*)(dlogT + col * G + lrow0 + rbase) = pk;
+        }
+      }
+    }
+  }
+  if (gb_f32) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) colsum[j] += __shfl_xor(colsum[j], 32, 64);
+    if (lane < 32) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) s_gb[wm][acc_col(wn, j, lane)] = colsum[j];
+    }
+    __syncthreads();
+    if (col0 + tid < V) atomicAdd(gb_f32 + col0 + tid, s_gb[0][tid] + s_gb[1][tid]);
+  }
+}
+
+// grad_hidden rows of one group: C = dlog [G][Vp] * (W^T [H][Vp])^T, cast to bf16.
+__global__ void __launch_bounds__(NTHREADS, 1)
+k_gemm_grad_hidden(const u16* __restrict__ dlog, const u16* __restrict__ wT, int64_t Vp, int64_t H,
+                   int64_t N, int64_t g0, int64_t G, int n_mt, int n_nt, u16* __restrict__ grad_hidden) {
+  __shared__ __attribute__((aligned(16))) char smem_raw[MAINLOOP_LDS];
+  LDS_AS char* smem = (LDS_AS char*)smem_raw;
+  int tm, tn;
+  tile_coords(n_mt, n_nt, tm, tn);
+  const int64_t lrow0 = (int64_t)tm * TILE, col0 = (int64_t)tn * TILE;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int wm = wave >> 1, wn = wave & 1;
+  Acc acc;
+  gemm_tile(acc, dlog, Vp, lrow0, G, wT, Vp, col0, H, Vp, smem);
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int64_t row = g0 + lrow0 + acc_row(wm, i, r, lane);
+      if (row >= N) continue;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int64_t col = col0 + acc_col(wn, j, lane);
+        if (col < H) grad_hidden[row * H + col] = f2bf(acc.v[i][j][r]);
+      }
+    }
+}
+
+// grad_weight FP32 accumulation for one group: gw[v][:] (+)= dlogT [Vp][G] * (h^T [H][G])^T.
+__global__ void __launch_bounds__(NTHREADS, 1)
+k_gemm_grad_weight(const u16* __restrict__ dlogT, const u16* __restrict__ hT, int64_t G, int64_t H,
+                   int64_t V, int64_t Vp, int n_mt, int n_nt, int first, float* __restrict__ gw_f32) {
+  __shared__ __attribute__((aligned(16))) char smem_raw[MAINLOOP_LDS];
+  LDS_AS char* smem = (LDS_AS char*)smem_raw;
+  int tm, tn;
+  tile_coords(n_mt, n_nt, tm, tn);
+  const int64_t row0 = (int64_t)tm * TILE, col0 = (int64_t)tn * TILE;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int wm = wave >> 1, wn = wave & 1;
+  Acc acc;
+  gemm_tile(acc, dlogT, G, row0, Vp, hT, G, col0, H, G, smem);
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int64_t v = row0 + acc_row(wm, i, r, lane);
+      if (v >= V) continue;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int64_t col = col0 + acc_col(wn, j, lane);
+        if (col < H) {
+          float* p = gw_f32 + v * H + col;
+          *p = first ? acc.v[i][j][r] : *p + acc.v[i][j][r];
+        }
+      }
+    }
+}
+
+__global__ void k_cast_bf16(const float* __restrict__ in, u16* __restrict__ out, int64_t n) {
+  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t s = (int64_t)gridDim.x * blockDim.x;
+  for (; i < n; i += s) out[i] = f2bf(in[i]);
+}
+
+// ---------------------------------------------------------------------------
+// Launchers (host side). Each returns the launch's hipError_t.
+// ---------------------------------------------------------------------------
+static int grid_1d(int64_t n, int per_block = 256, int cap = 65536) {
+  int64_t b = (n + per_block - 1) / per_block;
+  if (b < 1) b = 1;
+  return (int)(b < cap ? b : cap);
+}
+
+hipError_t launch_zero(void* p, int64_t bytes, hipStream_t st) {
+  if (bytes <= 0) return hipSuccess;
+  const int64_t words = (bytes + 3) / 4;
+  hipLaunchKernelGGL(k_zero, dim3(grid_1d(words, 256, 4096)), dim3(256), 0, st, (uint32_t*)p, words);
+  return hipGetLastError();
+}
+
+hipError_t launch_prepare_labels(const int64_t* labels, int64_t N, int64_t Np, int64_t V, int64_t ignore,
+                                 int32_t* label32, unsigned long long* n_valid, int32_t* status,
+                                 hipStream_t st) {
+  hipLaunchKernelGGL(k_prepare_labels, dim3((unsigned)(Np / 256)), dim3(256), 0, st, labels, N, V, ignore,
+                     label32, n_valid, status);
+  return hipGetLastError();
+}
+
+hipError_t launch_fwd_lse(const Shapes& s, const void* hidden, const void* weight, const void* bias,
+                          const int32_t* label32, float* part_m, float* part_s, float* zlab, hipStream_t st) {
+  const int n_mt = (int)(s.Np / TILE), n_vt = (int)(s.Vp / TILE);
+  hipLaunchKernelGGL(k_fwd_lse, dim3((unsigned)(n_mt * n_vt)), dim3(NTHREADS), 0, st, (const u16*)hidden,
+                     s.ldh, (const u16*)weight, s.ldw, (const u16*)bias, label32, s.N, s.Np, s.V, s.H, n_mt,
+                     n_vt, part_m, part_s, zlab);
+  return hipGetLastError();
+}
+
+hipError_t launch_finalize_rows(const Shapes& s, const float* part_m, const float* part_s, const float* zlab,
+                                const int32_t* label32, const int32_t* status, int reduction, float* lse_ws,
+                                float* lse_out, float* rowloss_out, double* chunk_acc, hipStream_t st) {
+  hipLaunchKernelGGL(k_finalize_rows, dim3((unsigned)(s.Np / 256)), dim3(256), 0, st, part_m, part_s, zlab,
+                     label32, s.N, s.Np, (int)(s.Vp / TILE), s.chunk_rows, status, reduction, lse_ws, lse_out,
+                     rowloss_out, chunk_acc);
+  return hipGetLastError();
+}
+
+hipError_t launch_finalize_loss(const double* chunk_acc, int64_t T, const unsigned long long* n_valid,
+                                const int32_t* status, int reduction, float* loss, float* chunk_out,
+                                hipStream_t st) {
+  hipLaunchKernelGGL(k_finalize_loss, dim3(1), dim3(256), 0, st, chunk_acc, T, n_valid, status, reduction,
+                     loss, chunk_out);
+  return hipGetLastError();
+}
+
+hipError_t launch_transpose(const void* in, int64_t ld_in, int64_t r0, int64_t R_valid, int64_t C, void* out,
+                            int64_t ld_out, int64_t R_pad, hipStream_t st) {
+  dim3 grid((unsigned)((C + 63) / 64), (unsigned)((R_pad + 63) / 64));
+  hipLaunchKernelGGL(k_transpose, grid, dim3(256), 0, st, (const u16*)in, ld_in, r0, R_valid, C, (u16*)out,
+                     ld_out, R_pad);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_dlogits(const Shapes& s, const void* hidden, const void* weight, const void* bias,
+                              const int32_t* label32, const float* lse_ws, const unsigned long long* n_valid,
+                              float grad_scale, int is_mean, int64_t g0, int64_t G, void* dlog, void* dlogT,
+                              float* gb_f32, hipStream_t st) {
+  const int n_mt = (int)(G / TILE), n_vt = (int)(s.Vp / TILE);
+  hipLaunchKernelGGL(k_bwd_dlogits, dim3((unsigned)(n_mt * n_vt)), dim3(NTHREADS), 0, st, (const u16*)hidden,
+                     s.ldh, (const u16*)weight, s.ldw, (const u16*)bias, label32, lse_ws, n_valid, grad_scale,
+                     is_mean, s.N, s.V, s.Vp, s.H, g0, G, n_mt, n_vt, (u16*)dlog, (u16*)dlogT, gb_f32);
+  return hipGetLastError();
+}
+
+hipError_t launch_grad_hidden(const Shapes& s, const void* dlog, const void* wT, int64_t g0, int64_t G,
+                              void* grad_hidden, hipStream_t st) {
+  const int n_mt = (int)(G / TILE), n_nt = (int)((s.H + TILE - 1) / TILE);
+  hipLaunchKernelGGL(k_gemm_grad_hidden, dim3((unsigned)(n_mt * n_nt)), dim3(NTHREADS), 0, st,
+                     (const u16*)dlog, (const u16*)wT, s.Vp, s.H, s.N, g0, G, n_mt, n_nt, (u16*)grad_hidden);
+  return hipGetLastError();
+}
+
+hipError_t launch_grad_weight(const Shapes& s, const void* dlogT, const void* hT, int64_t G, int first,
+                              float* gw_f32, hipStream_t st) {
+  const int n_mt = (int)(s.Vp / TILE), n_nt = (int)((s.H + TILE - 1) / TILE);
+  hipLaunchKernelGGL(k_gemm_grad_weight, dim3((unsigned)(n_mt * n_nt)), dim3(NTHREADS), 0, st,
+                     (const u16*)dlogT, (const u16*)hT, G, s.H, s.V, s.Vp, n_mt, n_nt, first, gw_f32);
+  return hipGetLastError();
+}
+
+hipError_t launch_cast(const float* in, void* out, int64_t n, hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_cast_bf16, dim3(grid_1d(n, 256, 16384)), dim3(256), 0, st, in, (u16*)out, n);
+  return hipGetLastError();
+}
+
+}  // namespace lce

@@ -80,14 +80,24 @@ WORKLOAD_ORDER = ["tiny", "qwen3_0p6b_head", "qwen3_4b_32k", "qwen3_4b_160k",
                   "qwen3_8b_1m_shard"]
 
 
-def bf16_bits(x: np.ndarray) -> np.ndarray:
-    """float32 -> bfloat16 bit patterns (uint16), round to nearest, ties to even.
-
-    Inputs here are finite draws, so no NaN handling is needed.
-    """
+def bf16_bits_reference(x: np.ndarray) -> np.ndarray:
+    """float32 -> bfloat16 bit patterns (uint16), round to nearest, ties to even,
+    on the bit pattern: add 0x7FFF plus the lowest kept bit, drop 16 bits.
+    Inputs here are finite draws, so no NaN handling is needed."""
     u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
     lsb = (u >> np.uint32(16)) & np.uint32(1)
     return ((u + np.uint32(0x7FFF) + lsb) >> np.uint32(16)).astype(np.uint16)
+
+
+def bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Same rounding as bf16_bits_reference, through torch's vectorised
+    float32 -> bfloat16 conversion (round to nearest even) when available."""
+    try:
+        import torch
+    except ImportError:  # pragma: no cover
+        return bf16_bits_reference(x)
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
+    return t.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
 
 
 def bits_to_f32(bits: np.ndarray) -> np.ndarray:

@@ -1,0 +1,243 @@
+"""GPU parity: the HIP path through the C ABI against the float64 oracle, on
+seeded inputs that span several 256 x 256 tiles with ragged row and
+vocabulary tails, plus the edge cases of the method."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import chunked_lm_head_lce_amd as lce
+from gpu_helpers import (assert_grad_close, assert_loss_close, assert_rows_close, np32, say, to_device)
+from lce_inputs import IGNORE_INDEX, make_case
+from oracle import lce_oracle as O
+
+pytestmark = pytest.mark.gpu
+
+
+def oracle_of(inp, reduction="sum", grad_scale=1.0, chunk_rows=256):
+    b = inp.bias_f32()
+    return O.forward_backward(inp.hidden_f32(), inp.weight_f32(), b, inp.labels, reduction=reduction,
+                              grad_scale=grad_scale, chunk_rows=chunk_rows)
+
+
+def check_all(out, ref, inp, reduction, grads=True):
+    assert int(out.n_valid.item()) == ref.n_valid
+    assert int(out.status.item()) == 0
+    if reduction == "none":
+        assert_rows_close(np32(out.loss), ref.row_loss, "row loss")
+    else:
+        assert_loss_close(float(out.loss.item()), ref.loss)
+    assert_rows_close(np32(out.lse), ref.lse, "lse")
+    if grads:
+        assert_grad_close(np32(out.grad_hidden), ref.grad_hidden, "grad_hidden")
+        assert_grad_close(np32(out.grad_weight), ref.grad_weight, "grad_weight")
+        if inp.bias_bits is not None:
+            assert_grad_close(np32(out.grad_bias), ref.grad_bias, "grad_bias")
+
+
+# (N, H, V): several tiles, ragged tails in rows and vocabulary, H not a
+# multiple of the 256 tile
+SHAPES = [(600, 256, 5000), (300, 128, 1000), (257, 64, 300), (512, 320, 4096), (40, 192, 130)]
+
+
+@pytest.mark.parametrize("shape", SHAPES)
+@pytest.mark.parametrize("bias", [False, True])
+def test_forward_backward_sum(cuda, shape, bias):
+    n, h, v = shape
+    say(f"[gpu] forward_backward sum shape={shape} bias={bias}")
+    inp = make_case(n, h, v, seed=n + v, bias_std=(0.05 if bias else None), ignore_frac=0.1, weight_std=0.05)
+    hd, wd, bd, yd = to_device(inp, cuda)
+    out = lce.lce_forward_backward(hd, wd, bd, yd, reduction="sum")
+    torch.cuda.synchronize()
+    check_all(out, oracle_of(inp, "sum"), inp, "sum")
+
+
+@pytest.mark.parametrize("reduction", ["mean", "sum"])
+def test_grad_scale_and_mean(cuda, reduction):
+    say(f"[gpu] grad_scale reduction={reduction}")
+    inp = make_case(700, 128, 2100, seed=5, bias_std=0.1, ignore_frac=0.3, weight_std=0.1)
+    hd, wd, bd, yd = to_device(inp, cuda)
+    out = lce.lce_forward_backward(hd, wd, bd, yd, reduction=reduction, grad_scale=0.37)
+    torch.cuda.synchronize()
+    check_all(out, oracle_of(inp, reduction, grad_scale=0.37), inp, reduction)
+
+
+def test_forward_only_all_reductions(cuda):
+    inp = make_case(520, 192, 3000, seed=9, bias_std=0.02, ignore_frac=0.15)
+    hd, wd, bd, yd = to_device(inp, cuda)
+    for reduction in ("none", "sum", "mean"):
+        say(f"[gpu] forward reduction={reduction}")
+        ref = O.forward(inp.hidden_f32(), inp.weight_f32(), inp.bias_f32(), inp.labels, reduction=reduction,
+                        chunk_rows=100)
+        out = lce.lce_forward(hd, wd, bd, yd, reduction=reduction, chunk_rows=100, want_chunk_loss=True)
+        torch.cuda.synchronize()
+        check_all(out, ref, inp, reduction, grads=False)
+        assert_rows_close(np32(out.chunk_loss), ref.chunk_loss, "chunk sums")
+        assert out.chunk_loss.numel() == math.ceil(520 / 100)
+
+
+def test_chunk_rows_invariance(cuda):
+    """Rows split cleanly: the chunk size only changes the chunk sums."""
+    inp = make_case(900, 128, 1500, seed=11, bias_std=0.05)
+    hd, wd, bd, yd = to_device(inp, cuda)
+    outs = {}
+    for c in (1, 100, 256, 900, 4096):
+        say(f"[gpu] chunk_rows={c}")
+        o = lce.lce_forward_backward(hd, wd, bd, yd, chunk_rows=c, want_chunk_loss=True)
+        torch.cuda.synchronize()
+        outs[c] = o
+        assert o.chunk_loss.numel() == math.ceil(900 / c)
+        assert abs(float(o.chunk_loss.double().sum()) - float(o.loss.item())) <= 1e-5 * abs(float(o.loss.item()))
+    ref = outs[256]
+    for c, o in outs.items():
+        assert int(o.n_valid.item()) == int(ref.n_valid.item())
+        assert_loss_close(float(o.loss.item()), float(ref.loss.item()))
+        assert torch.equal(o.grad_hidden, ref.grad_hidden)   # same kernels, same order: identical
+        assert_grad_close(np32(o.grad_weight), np32(ref.grad_weight), f"grad_weight c={c}")
+
+
+def test_row_groups_match(cuda):
+    """rows_in_flight only changes how many rows' dlogits are alive at once."""
+    inp = make_case(1100, 128, 1300, seed=12, bias_std=0.05, ignore_frac=0.05)
+    hd, wd, bd, yd = to_device(inp, cuda)
+    ref = oracle_of(inp)
+    for g in (256, 512, 0):
+        say(f"[gpu] rows_in_flight={g}")
+        out = lce.lce_forward_backward(hd, wd, bd, yd, rows_in_flight=g)
+        torch.cuda.synchronize()
+        check_all(out, ref, inp, "sum")
+
+
+def test_strided_hidden_and_weight(cuda):
+    inp = make_case(300, 128, 700, seed=13, bias_std=0.05)
+    hd, wd, bd, yd = to_device(inp, cuda)
+    hw = torch.zeros(300, 200, dtype=torch.bfloat16, device=cuda)
+    hw[:, :128] = hd
+    ww = torch.zeros(700, 136, dtype=torch.bfloat16, device=cuda)
+    ww[:, :128] = wd
+    say("[gpu] strided operands")
+    out = lce.lce_forward_backward(hw[:, :128], ww[:, :128], bd, yd)
+    torch.cuda.synchronize()
+    check_all(out, oracle_of(inp), inp, "sum")
+
+
+def test_optional_outputs_and_f32(cuda):
+    inp = make_case(400, 128, 900, seed=14, bias_std=0.05)
+    hd, wd, bd, yd = to_device(inp, cuda)
+    ref = oracle_of(inp)
+    say("[gpu] only grad_hidden")
+    o = lce.lce_forward_backward(hd, wd, bd, yd, want_grad_weight=False, want_grad_bias=False)
+    torch.cuda.synchronize()
+    assert o.grad_weight is None and o.grad_bias is None
+    assert_grad_close(np32(o.grad_hidden), ref.grad_hidden, "grad_hidden")
+    say("[gpu] only weight grads, fp32 exposed")
+    o = lce.lce_forward_backward(hd, wd, bd, yd, want_grad_hidden=False, want_f32=True)
+    torch.cuda.synchronize()
+    assert_grad_close(np32(o.grad_weight_f32), ref.grad_weight, "grad_weight_f32")
+    assert_grad_close(np32(o.grad_bias_f32), ref.grad_bias, "grad_bias_f32")
+    assert torch.equal(o.grad_weight, o.grad_weight_f32.to(torch.bfloat16))   # one RNE cast
+    assert torch.equal(o.grad_bias, o.grad_bias_f32.to(torch.bfloat16))
+    assert_loss_close(float(o.loss.item()), ref.loss)
+
+
+def test_zero_weight_closed_form(cuda):
+    """W = 0, b = 0: l_i = ln V; grad_hidden = 0; grad_bias_j = n_valid/V - count_j."""
+    n, h, v = 300, 64, 1000
+    inp = make_case(n, h, v, seed=15, bias_std=0.1, ignore_frac=0.2)
+    hd, _, _, yd = to_device(inp, cuda)
+    wd = torch.zeros(v, h, dtype=torch.bfloat16, device=cuda)
+    bd = torch.zeros(v, dtype=torch.bfloat16, device=cuda)
+    say("[gpu] zero weight closed form")
+    o = lce.lce_forward_backward(hd, wd, bd, yd, want_f32=True)
+    torch.cuda.synchronize()
+    nv = int((inp.labels != IGNORE_INDEX).sum())
+    assert int(o.n_valid.item()) == nv
+    assert abs(float(o.loss.item()) - nv * math.log(v)) <= 1e-6 * nv * math.log(v)
+    assert np.allclose(np32(o.lse), math.log(v), rtol=1e-6)
+    assert torch.count_nonzero(o.grad_hidden) == 0
+    counts = np.bincount(inp.labels[inp.labels >= 0], minlength=v)
+    np.testing.assert_allclose(np32(o.grad_bias_f32), nv / v - counts, atol=1e-5)
+
+
+def test_all_rows_ignored(cuda):
+    inp = make_case(300, 64, 500, seed=16, bias_std=0.1, ignore_frac=0.0)
+    hd, wd, bd, _ = to_device(inp, cuda)
+    yd = torch.full((300,), IGNORE_INDEX, dtype=torch.int64, device=cuda)
+    for reduction in ("mean", "sum"):
+        say(f"[gpu] all ignored {reduction}")
+        o = lce.lce_forward_backward(hd, wd, bd, yd, reduction=reduction)
+        torch.cuda.synchronize()
+        assert float(o.loss.item()) == 0.0 and int(o.n_valid.item()) == 0
+        assert torch.count_nonzero(o.grad_hidden) == 0
+        assert torch.count_nonzero(o.grad_weight) == 0 and torch.count_nonzero(o.grad_bias) == 0
+
+
+def test_custom_ignore_index(cuda):
+    inp = make_case(300, 64, 500, seed=17, ignore_frac=0.0)
+    y = inp.labels.copy()
+    y[::7] = 7          # rows labelled 7 are treated as ignored
+    ref = O.forward_backward(inp.hidden_f32(), inp.weight_f32(), None, y, ignore_index=7)
+    hd, wd, _, _ = to_device(inp, cuda)
+    say("[gpu] ignore_index=7")
+    o = lce.lce_forward_backward(hd, wd, None, torch.from_numpy(y).to(cuda), ignore_index=7)
+    torch.cuda.synchronize()
+    check_all(o, ref, inp, "sum")
+
+
+def test_label_out_of_range_sets_status(cuda):
+    inp = make_case(300, 64, 500, seed=18, ignore_frac=0.1)
+    y = inp.labels.copy()
+    y[5] = 500
+    y[17] = -3
+    hd, wd, _, _ = to_device(inp, cuda)
+    say("[gpu] label out of range")
+    o = lce.lce_forward_backward(hd, wd, None, torch.from_numpy(y).to(cuda))
+    torch.cuda.synchronize()
+    assert int(o.status.item()) == lce._lib.LCE_ERR_LABEL_RANGE
+    assert math.isnan(float(o.loss.item()))
+    assert int(o.n_valid.item()) == int(((y >= 0) & (y < 500)).sum())
+    with pytest.raises(lce.LceError):
+        o.check()
+    # the bad rows were treated as ignored: their grad_hidden rows are zero
+    assert torch.count_nonzero(o.grad_hidden[5]) == 0 and torch.count_nonzero(o.grad_hidden[17]) == 0
+    # and a clean call afterwards reports OK again
+    o2 = lce.lce_forward_backward(hd, wd, None, torch.from_numpy(inp.labels).to(cuda))
+    torch.cuda.synchronize()
+    assert int(o2.status.item()) == 0 and not math.isnan(float(o2.loss.item()))
+
+
+@pytest.mark.parametrize("shape", [(1, 64, 1), (1, 64, 7), (3, 64, 256), (256, 64, 256), (0, 64, 100)])
+def test_degenerate_shapes(cuda, shape):
+    n, h, v = shape
+    say(f"[gpu] degenerate {shape}")
+    inp = make_case(n, h, v, seed=19, bias_std=0.1, ignore_frac=0.0)
+    hd, wd, bd, yd = to_device(inp, cuda)
+    o = lce.lce_forward_backward(hd, wd, bd, yd)
+    torch.cuda.synchronize()
+    ref = oracle_of(inp)
+    assert int(o.n_valid.item()) == ref.n_valid
+    if n == 0:
+        assert float(o.loss.item()) == 0.0
+        assert torch.count_nonzero(o.grad_weight) == 0 and torch.count_nonzero(o.grad_bias) == 0
+        return
+    if v == 1:   # one class: lse = z, every loss and gradient is zero
+        assert abs(float(o.loss.item())) <= 1e-6
+    else:
+        assert_loss_close(float(o.loss.item()), ref.loss)
+    assert_grad_close(np32(o.grad_hidden), ref.grad_hidden, "grad_hidden")
+    assert_grad_close(np32(o.grad_weight), ref.grad_weight, "grad_weight")
+    assert_grad_close(np32(o.grad_bias), ref.grad_bias, "grad_bias")
+
+
+def test_repeatable(cuda):
+    inp = make_case(800, 128, 2000, seed=20, bias_std=0.05)
+    hd, wd, bd, yd = to_device(inp, cuda)
+    say("[gpu] repeatability")
+    a = lce.lce_forward_backward(hd, wd, bd, yd)
+    b = lce.lce_forward_backward(hd, wd, bd, yd)
+    torch.cuda.synchronize()
+    assert int(a.n_valid.item()) == int(b.n_valid.item())
+    assert torch.equal(a.grad_hidden, b.grad_hidden) and torch.equal(a.grad_weight, b.grad_weight)
+    assert torch.equal(a.lse, b.lse)
+    assert abs(float(a.loss.item()) - float(b.loss.item())) <= 1e-6 * abs(float(a.loss.item()))

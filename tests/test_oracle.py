@@ -334,3 +334,19 @@ def test_planted_mistakes_are_caught(monkeypatch, name):
     except AssertionError:
         caught = True
     assert caught, f"planted mistake {name} was not caught"
+
+
+def test_bf16_rounding_paths_agree():
+    """The fast (torch) and bit-pattern (numpy) round-to-nearest-even agree,
+    ties included; and a tie rounds to the even neighbour."""
+    from lce_inputs import bf16_bits, bf16_bits_reference, bits_to_f32
+    rng = np.random.default_rng(3)
+    x = rng.standard_normal(200_000).astype(np.float32)
+    u = x.view(np.uint32).copy()
+    u[:5000] = (u[:5000] & 0xFFFF0000) | 0x8000
+    x = u.view(np.float32)
+    assert np.array_equal(bf16_bits(x), bf16_bits_reference(x))
+    one_tie = np.array([1.0 + 2.0 ** -8], dtype=np.float32)        # halfway between 1 and 1 + 2^-7
+    assert bits_to_f32(bf16_bits(one_tie))[0] == 1.0
+    three_tie = np.array([1.0 + 3 * 2.0 ** -8], dtype=np.float32)  # halfway, odd lower neighbour
+    assert bits_to_f32(bf16_bits(three_tie))[0] == 1.0 + 2 * 2.0 ** -7
