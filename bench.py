@@ -141,6 +141,9 @@ def main() -> int:
     ap.add_argument("--fwd-steps", type=int, default=3)
     ap.add_argument("--cpu-rows", type=int, default=1024)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-gib", type=float, default=0.0,
+                    help="also run one plain device-to-device copy of this many GiB (a kernel of known "
+                         "traffic, used to calibrate the FETCH_SIZE / WRITE_SIZE counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print(f"bench.py measures one GPU only: the loss shards by rows with no exchange inside the kernels, "
@@ -207,22 +210,33 @@ def main() -> int:
     peak_extra = torch.cuda.max_memory_allocated(dev) - base_bytes - out_bytes
 
     # forward only
-    fout = lce.lce_forward(hd, wd, bd, yd, chunk_rows=w.chunk_rows, reduction=w.reduction)
-    torch.cuda.synchronize()
-    fws = torch.empty(fout.workspace_bytes, dtype=torch.uint8, device=dev)
-    s2, e2 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    s2.record(stream)
-    for _ in range(args.fwd_steps):
-        lce.lce_forward(hd, wd, bd, yd, chunk_rows=w.chunk_rows, reduction=w.reduction, workspace=fws, out=fout)
-    e2.record(stream)
-    torch.cuda.synchronize()
-    ms_fwd = s2.elapsed_time(e2) / max(1, args.fwd_steps)
+    ms_fwd = None
+    if args.fwd_steps > 0:
+        fout = lce.lce_forward(hd, wd, bd, yd, chunk_rows=w.chunk_rows, reduction=w.reduction)
+        torch.cuda.synchronize()
+        fws = torch.empty(fout.workspace_bytes, dtype=torch.uint8, device=dev)
+        s2, e2 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s2.record(stream)
+        for _ in range(args.fwd_steps):
+            lce.lce_forward(hd, wd, bd, yd, chunk_rows=w.chunk_rows, reduction=w.reduction, workspace=fws,
+                            out=fout)
+        e2.record(stream)
+        torch.cuda.synchronize()
+        ms_fwd = s2.elapsed_time(e2) / args.fwd_steps
     events.close()
+    if args.copy_gib > 0:
+        nbytes = int(args.copy_gib * (1 << 30))
+        src = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"[bench] copied {nbytes} bytes device to device (counter calibration)")
+        del src, dst
 
     N, H, V = w.n_rows, w.hidden, w.vocab
     tok_s = N / (ms_step * 1e-3)
     pct = 6.0 * N * H * V / (ms_step * 1e-3) / (PEAK_BF16_TFLOPS * 1e12)
-    pct_fwd = 2.0 * N * H * V / (ms_fwd * 1e-3) / (PEAK_BF16_TFLOPS * 1e12)
+    pct_fwd = 2.0 * N * H * V / (ms_fwd * 1e-3) / (PEAK_BF16_TFLOPS * 1e12) if ms_fwd else None
 
     dom_name = max(kernels, key=lambda k: kernels[k]["ms_per_step"])
     dom = kernels[dom_name]
@@ -247,7 +261,8 @@ def main() -> int:
                    "ignored_rows": w.n_ignored, "chunk_rows": w.chunk_rows, "reduction": w.reduction,
                    "rows_in_flight": rif or 16384, "parallelism": "single GPU"},
         "pct_peak_bf16": pct,
-        "fwd_tokens_per_s": N / (ms_fwd * 1e-3), "fwd_ms": ms_fwd, "fwd_pct_peak_bf16": pct_fwd,
+        "fwd_tokens_per_s": N / (ms_fwd * 1e-3) if ms_fwd else None, "fwd_ms": ms_fwd,
+        "fwd_pct_peak_bf16": pct_fwd,
         "peak_extra_hbm_gb": peak_extra / 1e9, "full_logits_fp32_gb": 4.0 * N * V / 1e9,
         "roofline": roofline,
         "cpu_baseline": cpu,

@@ -29,6 +29,8 @@ namespace lce {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint16_t u16;
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int TILE = 256;                 // output tile edge (rows and columns)
 constexpr int BK = 64;                    // K depth of one LDS stage
@@ -37,6 +39,10 @@ constexpr int OPERAND_STAGE = TILE * BK * 2;       // 32 KB: one operand, one st
 constexpr int STAGE = 2 * OPERAND_STAGE;           // 64 KB: both operands
 constexpr int MAINLOOP_LDS = 2 * STAGE;            // 128 KB: double buffered
 constexpr float LOG2E = 1.4426950408889634f;       // log2(e): exp(x) = 2^(x log2 e)
+// s_waitcnt immediates (gfx9 encoding: vmcnt [3:0]+[15:14], expcnt [6:4],
+// lgkmcnt [11:8]); the other counters are left at their maximum (no wait).
+constexpr int WAIT_LGKM0 = 0xC07F;   // lgkmcnt(0)
+constexpr int WAIT_VM0 = 0x0F70;     // vmcnt(0)
 
 __device__ __forceinline__ float bf2f(u16 u) { return __builtin_bit_cast(float, (uint32_t)u << 16); }
 __device__ __forceinline__ u16 f2bf(float x) {
@@ -122,8 +128,9 @@ __device__ __forceinline__ int acc_row(int wm, int i, int r, int lane) {
 __device__ __forceinline__ int acc_col(int wn, int j, int lane) { return wn * 128 + j * 32 + (lane & 31); }
 
 // C tile (256 x 256, fp32 in registers) = X[x_row0 : +256][0:K] * Y[y_row0 : +256][0:K]^T.
-// K % 64 == 0. smem must hold MAINLOOP_LDS bytes. Ends with a barrier, after
-// which smem may be reused.
+// K % 64 == 0 (BK/16 must be even). smem must hold MAINLOOP_LDS bytes. Every
+// LDS read of the stages precedes the final barrier, so smem may be reused
+// once the routine returns.
 __device__ __forceinline__ void gemm_tile(Acc& acc, const u16* __restrict__ X, int64_t ldx, int64_t x_row0,
                                           int64_t x_rows, const u16* __restrict__ Y, int64_t ldy,
                                           int64_t y_row0, int64_t y_rows, int64_t K, LDS_AS char* smem) {
@@ -137,33 +144,58 @@ __device__ __forceinline__ void gemm_tile(Acc& acc, const u16* __restrict__ X, i
       for (int r = 0; r < 16; ++r) acc.v[i][j][r] = 0.f;
 
   const int nk = (int)(K / BK);
+  const int rA = wm * 128 + (lane & 31), rB = wn * 128 + (lane & 31), hi = lane >> 5;
   stage_fill(X, ldx, x_row0, x_rows, 0, smem, wave, lane);
   stage_fill(Y, ldy, y_row0, y_rows, 0, smem + OPERAND_STAGE, wave, lane);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
+  // Two register sets of fragments: the set for sub-step kk+1 is read from
+  // LDS while the 16 MFMAs of sub-step kk run, so LDS latency stays hidden
+  // with one wave per SIMD. The stage barrier sits before the last sub-step's
+  // MFMAs, and the next stage's first set is read across it. The scheduling
+  // fences keep the compiler from sinking reads next to their first use.
+  bf16x8 a[2][4], b[2][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) a[0][i] = frag(smem, rA + i * 32, hi);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) b[0][j] = frag(smem + OPERAND_STAGE, rB + j * 32, hi);
   for (int kt = 0; kt < nk; ++kt) {
     LDS_AS char* cur = smem + (kt & 1) * STAGE;
+    LDS_AS char* nxt = smem + ((kt + 1) & 1) * STAGE;
+    // Safe to overwrite `nxt`: every wave passed the previous stage barrier
+    // after its last read of that buffer.
     if (kt + 1 < nk) {
-      LDS_AS char* nxt = smem + ((kt + 1) & 1) * STAGE;
       stage_fill(X, ldx, x_row0, x_rows, (int64_t)(kt + 1) * BK, nxt, wave, lane);
       stage_fill(Y, ldy, y_row0, y_rows, (int64_t)(kt + 1) * BK, nxt + OPERAND_STAGE, wave, lane);
     }
 #pragma unroll
     for (int kk = 0; kk < BK / 16; ++kk) {
-      const int c = kk * 2 + (lane >> 5);
-      bf16x8 a[4], b[4];
+      const int p = kk & 1;
+      __builtin_amdgcn_s_waitcnt(WAIT_LGKM0);               // set p landed (issued a sub-step ago)
+      if (kk + 1 < BK / 16) {
+        const int c = (kk + 1) * 2 + hi;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) a[i] = frag(cur, wm * 128 + i * 32 + (lane & 31), c);
+        for (int i = 0; i < 4; ++i) a[p ^ 1][i] = frag(cur, rA + i * 32, c);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) b[j] = frag(cur + OPERAND_STAGE, wn * 128 + j * 32 + (lane & 31), c);
+        for (int j = 0; j < 4; ++j) b[p ^ 1][j] = frag(cur + OPERAND_STAGE, rB + j * 32, c);
+      } else {
+        __builtin_amdgcn_s_waitcnt(WAIT_VM0);                 // next stage landed (this wave's part)
+        __syncthreads();                                      // ... and every wave's; `cur` fully read
+        if (kt + 1 < nk) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) a[p ^ 1][i] = frag(nxt, rA + i * 32, hi);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) b[p ^ 1][j] = frag(nxt + OPERAND_STAGE, rB + j * 32, hi);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-          acc.v[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc.v[i][j], 0, 0, 0);
+          acc.v[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[p][i], b[p][j], acc.v[i][j], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
     }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
   }
 }
 
@@ -358,7 +390,12 @@ __global__ void __launch_bounds__(256) k_transpose(const u16* __restrict__ in, i
 // G = s valid (softmax - onehot) in registers, add its column sums into the
 // FP32 bias gradient, and write G (bf16) in the two layouts the gradient
 // products read: dlog [G][Vp] (vocabulary contiguous) and dlogT [Vp][G]
-// (rows contiguous). Rows >= N and ids >= V get exact zeros.
+// (rows contiguous). Rows >= N and ids >= V get exact zeros. Both layouts go
+// out through an LDS staging tile so every global store is 16 bytes and
+// coalesced.
+constexpr int STAGE_LD = TILE + 8;                    // staging row stride (u16): 528 B, 16-B aligned
+constexpr int DLOG_LDS = TILE * STAGE_LD * 2;         // 135168 B
+
 __global__ void __launch_bounds__(NTHREADS, 1)
 k_bwd_dlogits(const u16* __restrict__ hidden, int64_t ldh, const u16* __restrict__ weight, int64_t ldw,
               const u16* __restrict__ bias, const int32_t* __restrict__ label32,
@@ -366,12 +403,13 @@ k_bwd_dlogits(const u16* __restrict__ hidden, int64_t ldh, const u16* __restrict
               float grad_scale, int is_mean, int64_t N, int64_t V, int64_t Vp, int64_t H, int64_t g0,
               int64_t G, int n_mt, int n_vt, u16* __restrict__ dlog, u16* __restrict__ dlogT,
               float* __restrict__ gb_f32) {
-  __shared__ __attribute__((aligned(16))) char smem_raw[MAINLOOP_LDS];
+  __shared__ __attribute__((aligned(16))) char smem_raw[DLOG_LDS];
   __shared__ float s_bias[TILE];
   __shared__ int s_lab[TILE];
   __shared__ float s_lse[TILE];
   __shared__ float s_gb[2][TILE];
   LDS_AS char* smem = (LDS_AS char*)smem_raw;
+  LDS_AS u16* stage = (LDS_AS u16*)smem_raw;
 
   int tm, tn;
   tile_coords(n_mt, n_vt, tm, tn);
@@ -392,41 +430,27 @@ k_bwd_dlogits(const u16* __restrict__ hidden, int64_t ldh, const u16* __restrict
     const unsigned long long nv = *n_valid;
     scale = grad_scale / (float)(nv > 0 ? nv : 1ull);
   }
+  // G in place of z; column sums for the bias gradient; bf16 G into the
+  // staging tile as [row][col].
   float colsum[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      float d[4][4];   // [j][r & 3]
+    for (int r = 0; r < 16; ++r) {
+      const int rl = acc_row(wm, i, r, lane);
+      const int lab = s_lab[rl];
+      const float lse = s_lse[rl];
 #pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        const int r = q * 4 + rr;
-        const int rl = acc_row(wm, i, r, lane);
-        const int lab = s_lab[rl];
-        const float lse = s_lse[rl];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int cl = acc_col(wn, j, lane);
-          const int64_t col = col0 + cl;
-          const float z = acc.v[i][j][r] + s_bias[cl];
-          const float p = exp_fast(z - lse);
-          float g = scale * (p - ((int64_t)lab == col ? 1.f : 0.f));
-          g = (lab >= 0 && col < V) ? g : 0.f;
-          d[j][rr] = g;
-          colsum[j] += g;
-          if (dlog) dlog[(lrow0 + rl) * Vp + col] = f2bf(g);
-        }
-      }
-      if (dlogT) {
-        const int rbase = acc_row(wm, i, q * 4, lane);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int64_t col = col0 + acc_col(wn, j, lane);
-          uint2 pk;
-          pk.x = (uint32_t)f2bf(d[j][0]) | ((uint32_t)f2bf(d[j][1]) << 16);
-          pk.y = (uint32_t)f2bf(d[j][2]) | ((uint32_t)f2bf(d[j][3]) << 16);
-          *(uint2*)(dlogT + col * G + lrow0 + rbase) = pk;
-        }
+      for (int j = 0; j < 4; ++j) {
+        const int cl = acc_col(wn, j, lane);
+        const int64_t col = col0 + cl;
+        const float z = acc.v[i][j][r] + s_bias[cl];
+        const float p = exp_fast(z - lse);
+        float g = scale * (p - ((int64_t)lab == col ? 1.f : 0.f));
+        g = (lab >= 0 && col < V) ? g : 0.f;
+        acc.v[i][j][r] = g;
+        colsum[j] += g;
+        if (dlog) stage[rl * STAGE_LD + cl] = f2bf(g);
       }
     }
   }
@@ -437,8 +461,43 @@ k_bwd_dlogits(const u16* __restrict__ hidden, int64_t ldh, const u16* __restrict
 #pragma unroll
       for (int j = 0; j < 4; ++j) s_gb[wm][acc_col(wn, j, lane)] = colsum[j];
     }
+  }
+  __syncthreads();
+  if (gb_f32 && col0 + tid < V) atomicAdd(gb_f32 + col0 + tid, s_gb[0][tid] + s_gb[1][tid]);
+  if (dlog) {
+    // 256 rows x 32 sixteen-byte chunks; lanes 0..31 cover one row.
+#pragma unroll 4
+    for (int it = 0; it < TILE * TILE / 8 / NTHREADS; ++it) {
+      const int id = it * NTHREADS + tid;
+      const int row = id >> 5, ch = id & 31;
+      const u32x4 v = *(const LDS_AS u32x4*)(stage + row * STAGE_LD + ch * 8);
+      *(u32x4*)(dlog + (lrow0 + row) * Vp + col0 + ch * 8) = v;
+    }
     __syncthreads();
-    if (col0 + tid < V) atomicAdd(gb_f32 + col0 + tid, s_gb[0][tid] + s_gb[1][tid]);
+  }
+  if (dlogT) {
+    // [col][row] staging: each lane holds 4 consecutive rows of one column.
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int rbase = acc_row(wm, i, q * 4, lane);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          u32x2 pk;
+          pk.x = (uint32_t)f2bf(acc.v[i][j][q * 4 + 0]) | ((uint32_t)f2bf(acc.v[i][j][q * 4 + 1]) << 16);
+          pk.y = (uint32_t)f2bf(acc.v[i][j][q * 4 + 2]) | ((uint32_t)f2bf(acc.v[i][j][q * 4 + 3]) << 16);
+          *(LDS_AS u32x2*)(stage + acc_col(wn, j, lane) * STAGE_LD + rbase) = pk;
+        }
+      }
+    __syncthreads();
+#pragma unroll 4
+    for (int it = 0; it < TILE * TILE / 8 / NTHREADS; ++it) {
+      const int id = it * NTHREADS + tid;
+      const int col = id >> 5, ch = id & 31;
+      const u32x4 v = *(const LDS_AS u32x4*)(stage + col * STAGE_LD + ch * 8);
+      *(u32x4*)(dlogT + (col0 + col) * G + lrow0 + ch * 8) = v;
+    }
   }
 }
 
