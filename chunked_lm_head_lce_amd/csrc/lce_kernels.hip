@@ -1,5 +1,5 @@
 // Device kernels of the chunked linear-cross-entropy library, written for
-// gfx950 (CDNA4, MI355X): 64-lane wavefronts, v_mfma_f32_32x32x16_bf16,
+// gfx950 (CDNA4, MI355X): 64-lane wavefronts, v_mfma_f32_16x16x32_bf16,
 // 160 KB of LDS per workgroup, direct global->LDS loads.
 //
 // What is computed (LlamaFactory PR #10762 analysis, section 4; TRL
@@ -27,7 +27,7 @@
 namespace lce {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint16_t u16;
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
@@ -35,6 +35,7 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 constexpr int TILE = 256;                 // output tile edge (rows and columns)
 constexpr int BK = 64;                    // K depth of one LDS stage
 constexpr int NTHREADS = 256;             // 4 waves, 2 x 2, each owns 128 x 128
+constexpr int NB = 8;                     // 16 x 16 MFMA blocks per wave edge (128 / 16)
 constexpr int OPERAND_STAGE = TILE * BK * 2;       // 32 KB: one operand, one stage
 constexpr int STAGE = 2 * OPERAND_STAGE;           // 64 KB: both operands
 constexpr int MAINLOOP_LDS = 2 * STAGE;            // 128 KB: double buffered
@@ -42,6 +43,7 @@ constexpr float LOG2E = 1.4426950408889634f;       // log2(e): exp(x) = 2^(x log
 // s_waitcnt immediates (gfx9 encoding: vmcnt [3:0]+[15:14], expcnt [6:4],
 // lgkmcnt [11:8]); the other counters are left at their maximum (no wait).
 constexpr int WAIT_LGKM0 = 0xC07F;   // lgkmcnt(0)
+#define WAIT_LGKM(n) (0xC07F | ((n) << 8))   // lgkmcnt(n), n <= 15
 constexpr int WAIT_VM0 = 0x0F70;     // vmcnt(0)
 
 __device__ __forceinline__ float bf2f(u16 u) { return __builtin_bit_cast(float, (uint32_t)u << 16); }
@@ -51,14 +53,15 @@ __device__ __forceinline__ u16 f2bf(float x) {
 }
 __device__ __forceinline__ float exp_fast(float x) { return __builtin_amdgcn_exp2f(x * LOG2E); }
 
-__device__ __forceinline__ float max32(float v) {
+// Reductions across the 16 lanes that hold one accumulator row.
+__device__ __forceinline__ float max16(float v) {
 #pragma unroll
-  for (int o = 16; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  for (int o = 8; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
   return v;
 }
-__device__ __forceinline__ float sum32(float v) {
+__device__ __forceinline__ float sum16(float v) {
 #pragma unroll
-  for (int o = 16; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+  for (int o = 8; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
   return v;
 }
 
@@ -85,30 +88,68 @@ __device__ __forceinline__ void tile_coords(int n_m, int n_n, int& tm, int& tn) 
 
 // ---------------------------------------------------------------------------
 // LDS stage layout: operand tile [256 rows][64 k] bf16, 128 B per row, the
-// eight 16-byte k-chunks of row r stored at chunk slot (c ^ (r & 7)) so that
-// the eight rows read together by a fragment load hit distinct banks.
+// eight 16-byte k-chunks of row r stored at chunk slot (c ^ swz(r)).
+// A fragment load reads one chunk from 32 consecutive rows; the LDS serves
+// 16 lanes x 16 B = 256 B per clock across 64 banks, where rows r and r+1
+// fall in opposite halves. swz(r) = (r >> 1) & 7 gives the 16 rows of each
+// group 16 distinct (half, slot) pairs, so the reads are conflict-free.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ int lds_off(int r, int c) { return r * 128 + ((c ^ (r & 7)) << 4); }
+#ifndef LCE_SWZ_SHIFT
+#define LCE_SWZ_SHIFT 1
+#endif
+__device__ __forceinline__ int swz(int r) { return (r >> LCE_SWZ_SHIFT) & 7; }
+__device__ __forceinline__ int lds_off(int r, int c) { return r * 128 + ((c ^ swz(r)) << 4); }
 
 // Direct global->LDS fill of one operand stage. One global_load_lds_dwordx4
 // writes 64 x 16 B contiguously (lane i at +16 i), i.e. 8 tile rows; lane i
-// therefore fetches logical chunk (i & 7) ^ (i >> 3) of row (i >> 3) of its
-// 8-row block. Rows past the operand's end are clamped to its last row (the
-// values are finite and the epilogues discard them).
-__device__ __forceinline__ void stage_fill(const u16* __restrict__ base, int64_t ld, int64_t row0,
-                                           int64_t nrows, int64_t k0, LDS_AS char* dst, int wave,
-                                           int lane) {
+// therefore fetches the logical chunk stored at slot (i & 7) of row (i >> 3)
+// of its 8-row block: c = (i & 7) ^ swz(row). Rows past the operand's end
+// are clamped to its last row (finite values the epilogues discard).
+//
+// The per-lane byte offsets inside the tile are fixed for the whole K loop
+// (StageOffsets, computed once); each stage only moves a wave-uniform base,
+// so the loads use the scalar-base + 32-bit-offset addressing form.
+struct StageOffsets {
+  uint32_t off[8];
+};
+__device__ __forceinline__ StageOffsets stage_offsets(int64_t ld, int64_t row0, int64_t nrows, int wave,
+                                                      int lane) {
+  StageOffsets o;
   const int r_in = lane >> 3;
-  const int c = (lane & 7) ^ r_in;
 #pragma unroll
   for (int b = 0; b < 8; ++b) {
     const int r = wave * 64 + b * 8 + r_in;
-    int64_t gr = row0 + r;
-    gr = gr < nrows ? gr : nrows - 1;
-    const u16* src = base + gr * ld + k0 + c * 8;
-    __builtin_amdgcn_global_load_lds((const void*)src, (LDS_AS void*)(dst + (wave * 64 + b * 8) * 128),
-                                     16, 0, 0);
+    const int c = (lane & 7) ^ swz(r);
+    int64_t lr = r;
+    if (row0 + lr > nrows - 1) lr = nrows - 1 - row0;
+    o.off[b] = (uint32_t)((lr * ld + c * 8) * 2);
   }
+  return o;
+}
+// One 16-byte-per-lane global->LDS load: lane i's 16 bytes from gbase + voff
+// land at LDS address lds_addr + 16 i (lds_addr in M0). Written as inline
+// assembly so the compiler does not treat the in-flight LDS writes as
+// possibly aliasing every later LDS read (it would wait for the loads to
+// complete before each read); the main loop orders them explicitly:
+// s_waitcnt vmcnt(0) and a barrier before any read of a refilled buffer.
+// M0 is used for nothing else in these kernels.
+__device__ __forceinline__ void lds_dma16(const void* gbase, uint32_t voff, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+               :: "s"(lds_addr), "v"(voff), "s"(gbase) : "memory", "m0");
+}
+
+// tile_base = operand + row0 * ld (elements); k0 in elements.
+__device__ __forceinline__ void stage_fill(const u16* __restrict__ tile_base, int64_t k0, const StageOffsets& o,
+                                           LDS_AS char* dst, int wave) {
+  // The base is wave-uniform; readfirstlane makes that visible to the
+  // compiler so it stays in the scalar registers the instruction needs.
+  const uint64_t b64 = (uint64_t)(uintptr_t)(tile_base + k0);
+  const uint64_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b64);
+  const uint64_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(b64 >> 32));
+  const void* base = (const void*)(uintptr_t)((hi << 32) | lo);
+  const uint32_t l0 = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)dst + (uint32_t)wave * 64 * 128);
+#pragma unroll
+  for (int b = 0; b < 8; ++b) lds_dma16(base, o.off[b], l0 + b * 1024);
 }
 
 __device__ __forceinline__ bf16x8 frag(const LDS_AS char* stage, int r, int c) {
@@ -116,84 +157,98 @@ __device__ __forceinline__ bf16x8 frag(const LDS_AS char* stage, int r, int c) {
 }
 
 struct Acc {
-  f32x16 v[4][4];   // [row block i][col block j], 32 x 32 each
+  f32x4 v[NB][NB];   // [row block i][col block j], 16 x 16 each
 };
 
-// Accumulator layout (v_mfma_f32_32x32x16_bf16): lane l, register r of block
-// (i, j) of wave (wm, wn) holds C[row][col] with
-//   row = wm*128 + i*32 + 8*(r/4) + 4*(l/32) + (r%4),   col = wn*128 + j*32 + (l%32).
+// Accumulator layout (v_mfma_f32_16x16x32_bf16): lane l, register r (0..3) of
+// block (i, j) of wave (wm, wn) holds C[row][col] with
+//   row = wm*128 + i*16 + 4*(l/16) + r,   col = wn*128 + j*16 + (l%16).
+// Operand fragments: lane l supplies row (l%16) of its 16-row block and the
+// 8 consecutive k at 8*(l/16) of the 32-deep step, for A and for B alike.
 __device__ __forceinline__ int acc_row(int wm, int i, int r, int lane) {
-  return wm * 128 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+  return wm * 128 + i * 16 + 4 * (lane >> 4) + r;
 }
-__device__ __forceinline__ int acc_col(int wn, int j, int lane) { return wn * 128 + j * 32 + (lane & 31); }
+__device__ __forceinline__ int acc_col(int wn, int j, int lane) { return wn * 128 + j * 16 + (lane & 15); }
 
 // C tile (256 x 256, fp32 in registers) = X[x_row0 : +256][0:K] * Y[y_row0 : +256][0:K]^T.
-// K % 64 == 0 (BK/16 must be even). smem must hold MAINLOOP_LDS bytes. Every
+// K % 64 == 0 (BK/32 must be even). smem must hold MAINLOOP_LDS bytes. Every
 // LDS read of the stages precedes the final barrier, so smem may be reused
 // once the routine returns.
 __device__ __forceinline__ void gemm_tile(Acc& acc, const u16* __restrict__ X, int64_t ldx, int64_t x_row0,
                                           int64_t x_rows, const u16* __restrict__ Y, int64_t ldy,
                                           int64_t y_row0, int64_t y_rows, int64_t K, LDS_AS char* smem) {
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < NB; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < NB; ++j)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc.v[i][j][r] = 0.f;
+      for (int r = 0; r < 4; ++r) acc.v[i][j][r] = 0.f;
 
   const int nk = (int)(K / BK);
-  const int rA = wm * 128 + (lane & 31), rB = wn * 128 + (lane & 31), hi = lane >> 5;
-  stage_fill(X, ldx, x_row0, x_rows, 0, smem, wave, lane);
-  stage_fill(Y, ldy, y_row0, y_rows, 0, smem + OPERAND_STAGE, wave, lane);
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  const int rA = wm * 128 + (lane & 15), rB = wn * 128 + (lane & 15), q = lane >> 4;
+  const StageOffsets ox = stage_offsets(ldx, x_row0, x_rows, wave, lane);
+  const StageOffsets oy = stage_offsets(ldy, y_row0, y_rows, wave, lane);
+  const u16* xt = X + x_row0 * ldx;
+  const u16* yt = Y + y_row0 * ldy;
+  // Stages 0 and 1 go out before the loop; stage kt+2 is issued right after
+  // the barrier of iteration kt (the moment buffer kt&1 is no longer read),
+  // so each stage has two sub-steps of MFMA work to arrive.
+  stage_fill(xt, 0, ox, smem, wave);
+  stage_fill(yt, 0, oy, smem + OPERAND_STAGE, wave);
+  if (nk > 1) {
+    stage_fill(xt, BK, ox, smem + STAGE, wave);
+    stage_fill(yt, BK, oy, smem + STAGE + OPERAND_STAGE, wave);
+  }
+  __builtin_amdgcn_s_waitcnt(WAIT_VM0);
   __syncthreads();
-  // Two register sets of fragments: the set for sub-step kk+1 is read from
-  // LDS while the 16 MFMAs of sub-step kk run, so LDS latency stays hidden
-  // with one wave per SIMD. The stage barrier sits before the last sub-step's
-  // MFMAs, and the next stage's first set is read across it. The scheduling
-  // fences keep the compiler from sinking reads next to their first use.
-  bf16x8 a[2][4], b[2][4];
+  // Fragment pipeline (one wave per SIMD, so the wave hides its own LDS
+  // latency): the B fragments of the next 32-deep sub-step are read into a
+  // second register set before the current 64 MFMAs; the A fragment of row
+  // block i is re-read for the next sub-step right after the 8 MFMAs that
+  // last use it, leaving 56 MFMAs for it to land. The stage barrier sits in
+  // the last sub-step, before the reads that cross into the next stage.
+  // Scheduling fences keep the compiler from moving reads or MFMAs across.
+  bf16x8 a[NB], b[2][NB];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) a[0][i] = frag(smem, rA + i * 32, hi);
+  for (int i = 0; i < NB; ++i) a[i] = frag(smem, rA + i * 16, q);
 #pragma unroll
-  for (int j = 0; j < 4; ++j) b[0][j] = frag(smem + OPERAND_STAGE, rB + j * 32, hi);
+  for (int j = 0; j < NB; ++j) b[0][j] = frag(smem + OPERAND_STAGE, rB + j * 16, q);
   for (int kt = 0; kt < nk; ++kt) {
     LDS_AS char* cur = smem + (kt & 1) * STAGE;
     LDS_AS char* nxt = smem + ((kt + 1) & 1) * STAGE;
-    // Safe to overwrite `nxt`: every wave passed the previous stage barrier
-    // after its last read of that buffer.
-    if (kt + 1 < nk) {
-      stage_fill(X, ldx, x_row0, x_rows, (int64_t)(kt + 1) * BK, nxt, wave, lane);
-      stage_fill(Y, ldy, y_row0, y_rows, (int64_t)(kt + 1) * BK, nxt + OPERAND_STAGE, wave, lane);
-    }
 #pragma unroll
-    for (int kk = 0; kk < BK / 16; ++kk) {
+    for (int kk = 0; kk < BK / 32; ++kk) {
       const int p = kk & 1;
-      __builtin_amdgcn_s_waitcnt(WAIT_LGKM0);               // set p landed (issued a sub-step ago)
-      if (kk + 1 < BK / 16) {
-        const int c = (kk + 1) * 2 + hi;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) a[p ^ 1][i] = frag(cur, rA + i * 32, c);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) b[p ^ 1][j] = frag(cur + OPERAND_STAGE, rB + j * 32, c);
-      } else {
-        __builtin_amdgcn_s_waitcnt(WAIT_VM0);                 // next stage landed (this wave's part)
+      const bool last = kk + 1 == BK / 32;
+      __builtin_amdgcn_s_waitcnt(WAIT_LGKM0);               // this sub-step's A and B landed
+      if (last) {
+        __builtin_amdgcn_s_waitcnt(WAIT_VM0);                 // stage kt+1 landed (this wave's part)
         __syncthreads();                                      // ... and every wave's; `cur` fully read
-        if (kt + 1 < nk) {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) a[p ^ 1][i] = frag(nxt, rA + i * 32, hi);
-#pragma unroll
-          for (int j = 0; j < 4; ++j) b[p ^ 1][j] = frag(nxt + OPERAND_STAGE, rB + j * 32, hi);
+        if (kt + 2 < nk) {                                    // `cur` is free: refill it with stage kt+2
+          stage_fill(xt, (int64_t)(kt + 2) * BK, ox, cur, wave);
+          stage_fill(yt, (int64_t)(kt + 2) * BK, oy, cur + OPERAND_STAGE, wave);
         }
       }
-      __builtin_amdgcn_sched_barrier(0);
+      // Source of the next sub-step's fragments: this stage, or the first
+      // sub-step of the next one. In the very last sub-step these reads
+      // fetch stale (but in-bounds) LDS that is never used; reading
+      // unconditionally keeps the loop free of branches.
+      LDS_AS char* src = last ? nxt : cur;
+      const int c = last ? q : (kk + 1) * 4 + q;
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int j = 0; j < NB; ++j) b[p ^ 1][j] = frag(src + OPERAND_STAGE, rB + j * 16, c);
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-          acc.v[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[p][i], b[p][j], acc.v[i][j], 0, 0, 0);
+      for (int i = 0; i < NB; ++i) {
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int j = 0; j < NB; ++j)
+          acc.v[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[p][j], acc.v[i][j], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        a[i] = frag(src, rA + i * 16, c);
+      }
       __builtin_amdgcn_sched_barrier(0);
     }
   }
@@ -260,15 +315,15 @@ k_fwd_lse(const u16* __restrict__ hidden, int64_t ldh, const u16* __restrict__ w
   gemm_tile(acc, hidden, ldh, row0, N, weight, ldw, col0, V, H, smem);
 
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < NB; ++i) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
+    for (int r = 0; r < 4; ++r) {
       const int rl = acc_row(wm, i, r, lane);
       const int lab = s_lab[rl];
-      float v[4];
+      float v[NB];
       float m = -INFINITY;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
+      for (int j = 0; j < NB; ++j) {
         const int cl = acc_col(wn, j, lane);
         const bool ok = col0 + cl < V;
         const float z = acc.v[i][j][r] + s_bias[cl];
@@ -276,14 +331,14 @@ k_fwd_lse(const u16* __restrict__ hidden, int64_t ldh, const u16* __restrict__ w
         m = fmaxf(m, v[j]);
         if (ok && (int64_t)lab == col0 + cl) zlab[row0 + rl] = z;
       }
-      m = max32(m);
+      m = max16(m);
       float s = 0.f;
       if (m != -INFINITY) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) s += exp_fast(v[j] - m);
+        for (int j = 0; j < NB; ++j) s += exp_fast(v[j] - m);
       }
-      s = sum32(s);
-      if ((lane & 31) == 0) {
+      s = sum16(s);
+      if ((lane & 15) == 0) {
         s_red_m[wn][rl] = m;
         s_red_s[wn][rl] = s;
       }
@@ -432,16 +487,18 @@ k_bwd_dlogits(const u16* __restrict__ hidden, int64_t ldh, const u16* __restrict
   }
   // G in place of z; column sums for the bias gradient; bf16 G into the
   // staging tile as [row][col].
-  float colsum[4] = {0.f, 0.f, 0.f, 0.f};
+  float colsum[NB];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int j = 0; j < NB; ++j) colsum[j] = 0.f;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
+  for (int i = 0; i < NB; ++i) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
       const int rl = acc_row(wm, i, r, lane);
       const int lab = s_lab[rl];
       const float lse = s_lse[rl];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
+      for (int j = 0; j < NB; ++j) {
         const int cl = acc_col(wn, j, lane);
         const int64_t col = col0 + cl;
         const float z = acc.v[i][j][r] + s_bias[cl];
@@ -455,11 +512,15 @@ k_bwd_dlogits(const u16* __restrict__ hidden, int64_t ldh, const u16* __restrict
     }
   }
   if (gb_f32) {
+    // lanes l, l^16, l^32, l^48 hold the same column
 #pragma unroll
-    for (int j = 0; j < 4; ++j) colsum[j] += __shfl_xor(colsum[j], 32, 64);
-    if (lane < 32) {
+    for (int j = 0; j < NB; ++j) {
+      colsum[j] += __shfl_xor(colsum[j], 16, 64);
+      colsum[j] += __shfl_xor(colsum[j], 32, 64);
+    }
+    if (lane < 16) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) s_gb[wm][acc_col(wn, j, lane)] = colsum[j];
+      for (int j = 0; j < NB; ++j) s_gb[wm][acc_col(wn, j, lane)] = colsum[j];
     }
   }
   __syncthreads();
@@ -478,18 +539,16 @@ k_bwd_dlogits(const u16* __restrict__ hidden, int64_t ldh, const u16* __restrict
   if (dlogT) {
     // [col][row] staging: each lane holds 4 consecutive rows of one column.
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < NB; ++i) {
+      const int rbase = acc_row(wm, i, 0, lane);
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int rbase = acc_row(wm, i, q * 4, lane);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          u32x2 pk;
-          pk.x = (uint32_t)f2bf(acc.v[i][j][q * 4 + 0]) | ((uint32_t)f2bf(acc.v[i][j][q * 4 + 1]) << 16);
-          pk.y = (uint32_t)f2bf(acc.v[i][j][q * 4 + 2]) | ((uint32_t)f2bf(acc.v[i][j][q * 4 + 3]) << 16);
-          *(LDS_AS u32x2*)(stage + acc_col(wn, j, lane) * STAGE_LD + rbase) = pk;
-        }
+      for (int j = 0; j < NB; ++j) {
+        u32x2 pk;
+        pk.x = (uint32_t)f2bf(acc.v[i][j][0]) | ((uint32_t)f2bf(acc.v[i][j][1]) << 16);
+        pk.y = (uint32_t)f2bf(acc.v[i][j][2]) | ((uint32_t)f2bf(acc.v[i][j][3]) << 16);
+        *(LDS_AS u32x2*)(stage + acc_col(wn, j, lane) * STAGE_LD + rbase) = pk;
       }
+    }
     __syncthreads();
 #pragma unroll 4
     for (int it = 0; it < TILE * TILE / 8 / NTHREADS; ++it) {
@@ -515,13 +574,13 @@ k_gemm_grad_hidden(const u16* __restrict__ dlog, const u16* __restrict__ wT, int
   Acc acc;
   gemm_tile(acc, dlog, Vp, lrow0, G, wT, Vp, col0, H, Vp, smem);
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < NB; ++i)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
+    for (int r = 0; r < 4; ++r) {
       const int64_t row = g0 + lrow0 + acc_row(wm, i, r, lane);
       if (row >= N) continue;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
+      for (int j = 0; j < NB; ++j) {
         const int64_t col = col0 + acc_col(wn, j, lane);
         if (col < H) grad_hidden[row * H + col] = f2bf(acc.v[i][j][r]);
       }
@@ -542,13 +601,13 @@ k_gemm_grad_weight(const u16* __restrict__ dlogT, const u16* __restrict__ hT, in
   Acc acc;
   gemm_tile(acc, dlogT, G, row0, Vp, hT, G, col0, H, G, smem);
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < NB; ++i)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
+    for (int r = 0; r < 4; ++r) {
       const int64_t v = row0 + acc_row(wm, i, r, lane);
       if (v >= V) continue;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
+      for (int j = 0; j < NB; ++j) {
         const int64_t col = col0 + acc_col(wn, j, lane);
         if (col < H) {
           float* p = gw_f32 + v * H + col;
