@@ -80,10 +80,14 @@ Layout make_layout(const lce_problem* p, int kind) {
   L.status = take(4);
   L.zlab = take((size_t)s.Np * 4);
   L.lse = take((size_t)s.Np * 4);
-  L.part_m = take((size_t)n_vt * s.Np * 4);
-  L.part_s = take((size_t)n_vt * s.Np * 4);
+  // (max, sumexp) partials per 128-column half tile: for every row in the
+  // forward, for one row group at a time in the backward.
+  const bool bwd = kind == LCE_WS_BACKWARD || kind == LCE_WS_BACKWARD_EXTERNAL_F32;
+  const int64_t part_rows = bwd ? group_rows(p, s) : s.Np;
+  L.part_m = take((size_t)2 * n_vt * part_rows * 4);
+  L.part_s = take((size_t)2 * n_vt * part_rows * 4);
   L.chunk_acc = take((size_t)n_chunks(p) * 8);
-  if (kind == LCE_WS_BACKWARD || kind == LCE_WS_BACKWARD_EXTERNAL_F32) {
+  if (bwd) {
     const int64_t G = group_rows(p, s);
     L.wT = take((size_t)s.H * s.Vp * 2);
     L.hT = take((size_t)s.H * G * 2);
@@ -143,6 +147,9 @@ struct Common {
   unsigned long long* n_valid;
   int32_t* status;
   float* lse_ws;
+  float* part_m;
+  float* part_s;
+  float* zlab;
   double* chunk_acc;
   int64_t T;
 };
@@ -167,10 +174,10 @@ int check_common(const lce_problem* p, const void* hidden, const void* weight, c
   return LCE_OK;
 }
 
-// Steps a1..a6 of the method: count and validate labels, logits tiles with the
-// online log-sum-exp epilogue, per-row lse / NLL / chunk sums.
-int run_forward(Common& c, const void* hidden, const void* weight, const void* bias, const int64_t* labels,
-                float* loss, float* lse_out, int64_t* n_valid_out, int32_t* status_out, hipStream_t st,
+// Zeroes the counters and validates the labels (label32, n_valid, status):
+// every later step, including the MEAN scale of the first row group's
+// gradients, sees the final n_valid.
+int run_prepare(Common& c, const int64_t* labels, int64_t* n_valid_out, int32_t* status_out, hipStream_t st,
                 Tracer& tr) {
   const Shapes& s = c.s;
   char* ws = c.ws;
@@ -179,10 +186,9 @@ int run_forward(Common& c, const void* hidden, const void* weight, const void* b
   c.status = status_out ? status_out : (int32_t*)(ws + c.L.status);
   c.lse_ws = (float*)(ws + c.L.lse);
   c.chunk_acc = (double*)(ws + c.L.chunk_acc);
-  float* part_m = (float*)(ws + c.L.part_m);
-  float* part_s = (float*)(ws + c.L.part_s);
-  float* zlab = (float*)(ws + c.L.zlab);
-
+  c.part_m = (float*)(ws + c.L.part_m);
+  c.part_s = (float*)(ws + c.L.part_s);
+  c.zlab = (float*)(ws + c.L.zlab);
   LCE_LAUNCH(tr, LCE_K_ZERO, 0, 0, 0, lce::launch_zero(c.n_valid, 8, st));
   LCE_LAUNCH(tr, LCE_K_ZERO, 0, 0, 0, lce::launch_zero(c.status, 4, st));
   LCE_LAUNCH(tr, LCE_K_ZERO, 0, 0, 0, lce::launch_zero(c.chunk_acc, c.T * 8, st));
@@ -190,12 +196,23 @@ int run_forward(Common& c, const void* hidden, const void* weight, const void* b
   LCE_LAUNCH(tr, LCE_K_PREPARE_LABELS, 0, 0, 0,
              lce::launch_prepare_labels(labels, s.N, s.Np, s.V, c.p->ignore_index, c.label32, c.n_valid,
                                         c.status, st));
-  LCE_LAUNCH(tr, LCE_K_FWD_LSE, s.N, s.V, s.H,
-             lce::launch_fwd_lse(s, hidden, weight, bias, c.label32, part_m, part_s, zlab, st));
+  return LCE_OK;
+}
+
+// Logits tiles with the online log-sum-exp epilogue for rows [g0, g0+rows),
+// then per-row lse / NLL / chunk sums. With p_out the tiles also leave
+// exp(z - max_half) behind for the gradient of the same rows.
+int run_rows(Common& c, const void* hidden, const void* weight, const void* bias, int64_t g0, int64_t rows,
+             void* p_out, float* loss, float* lse_out, hipStream_t st, Tracer& tr) {
+  const Shapes& s = c.s;
+  const int64_t rows_valid = (s.N - g0) < rows ? (s.N - g0) : rows;
+  LCE_LAUNCH(tr, LCE_K_FWD_LSE, rows_valid, s.V, s.H,
+             lce::launch_fwd_tiles(s, hidden, weight, bias, c.label32, g0, rows, c.part_m, c.part_s, c.zlab, p_out,
+                                   st));
   LCE_LAUNCH(tr, LCE_K_FINALIZE_ROWS, 0, 0, 0,
-             lce::launch_finalize_rows(s, part_m, part_s, zlab, c.label32, c.status, c.p->reduction, c.lse_ws,
-                                       lse_out, c.p->reduction == LCE_REDUCTION_NONE ? loss : nullptr,
-                                       c.chunk_acc, st));
+             lce::launch_finalize_rows(s, c.part_m, c.part_s, g0, rows, c.zlab, c.label32, c.status,
+                                       c.p->reduction, c.lse_ws, lse_out,
+                                       c.p->reduction == LCE_REDUCTION_NONE ? loss : nullptr, c.chunk_acc, st));
   return LCE_OK;
 }
 
@@ -234,8 +251,12 @@ int lce_forward_traced(const lce_problem* p, const void* hidden, const void* wei
   tr.t = trace;
   tr.st = stream;
   if (trace) trace->count = 0;
-  st = run_forward(c, hidden, weight, bias, labels, loss, lse, n_valid, status, stream, tr);
+  st = run_prepare(c, labels, n_valid, status, stream, tr);
   if (st != LCE_OK) return st;
+  if (c.s.N > 0) {
+    st = run_rows(c, hidden, weight, bias, 0, c.s.Np, nullptr, loss, lse, stream, tr);
+    if (st != LCE_OK) return st;
+  }
   LCE_LAUNCH(tr, LCE_K_FINALIZE_LOSS, 0, 0, 0,
              lce::launch_finalize_loss(c.chunk_acc, c.T, c.n_valid, c.status, p->reduction, loss, chunk_loss,
                                        stream));
@@ -272,7 +293,7 @@ int lce_forward_backward_traced(const lce_problem* p, const void* hidden, const 
   tr.t = trace;
   tr.st = stream;
   if (trace) trace->count = 0;
-  st = run_forward(c, hidden, weight, bias, labels, loss, lse, n_valid, status, stream, tr);
+  st = run_prepare(c, labels, n_valid, status, stream, tr);
   if (st != LCE_OK) return st;
 
   const Shapes& s = c.s;
@@ -282,23 +303,29 @@ int lce_forward_backward_traced(const lce_problem* p, const void* hidden, const 
   if (need_gb) LCE_LAUNCH(tr, LCE_K_ZERO, 0, 0, 0, lce::launch_zero(gb, s.V * 4, stream));
   if (s.N == 0) {
     if (need_gw) LCE_LAUNCH(tr, LCE_K_ZERO, 0, 0, 0, lce::launch_zero(gw, s.V * s.H * 4, stream));
-  } else if (need_gh || need_gw || need_gb) {
+  } else {
+    // Row groups: the logits of a group are computed once; the tiles leave
+    // exp(z - max_half) in dlog, the group's lse follows, and the dlogits
+    // pass turns dlog into G (and G^T) for the two gradient products.
     const int64_t G = group_rows(p, s);
     void* wT = ws + c.L.wT;
     void* hT = ws + c.L.hT;
     void* dlog = ws + c.L.dlog;
     void* dlogT = ws + c.L.dlogT;
     const int is_mean = p->reduction == LCE_REDUCTION_MEAN;
+    const bool any_grad = need_gh || need_gw || need_gb;
     if (need_gh)
       LCE_LAUNCH(tr, LCE_K_TRANSPOSE, 0, 0, 0,
                  lce::launch_transpose(weight, s.ldw, 0, s.V, s.H, wT, s.Vp, s.Vp, stream));
     for (int64_t g0 = 0; g0 < s.Np; g0 += G) {
       const int64_t Gc = (s.Np - g0) < G ? (s.Np - g0) : G;
       const int64_t rows_valid = (s.N - g0) < Gc ? (s.N - g0) : Gc;
-      LCE_LAUNCH(tr, LCE_K_BWD_DLOGITS, rows_valid, s.V, s.H,
-                 lce::launch_bwd_dlogits(s, hidden, weight, bias, c.label32, c.lse_ws, c.n_valid, grad_scale,
-                                         is_mean, g0, Gc, need_gh ? dlog : nullptr, need_gw ? dlogT : nullptr,
-                                         need_gb ? gb : nullptr, stream));
+      st = run_rows(c, hidden, weight, bias, g0, Gc, any_grad ? dlog : nullptr, loss, lse, stream, tr);
+      if (st != LCE_OK) return st;
+      if (!any_grad) continue;
+      LCE_LAUNCH(tr, LCE_K_BWD_DLOGITS, rows_valid, s.V, 0,
+                 lce::launch_dlogits(s, c.label32, c.part_m, c.lse_ws, c.n_valid, grad_scale, is_mean, g0, Gc, dlog,
+                                     need_gh ? 1 : 0, need_gw ? dlogT : nullptr, need_gb ? gb : nullptr, stream));
       if (need_gh)
         LCE_LAUNCH(tr, LCE_K_GRAD_HIDDEN, rows_valid, s.H, s.V,
                    lce::launch_grad_hidden(s, dlog, wT, g0, Gc, grad_hidden, stream));

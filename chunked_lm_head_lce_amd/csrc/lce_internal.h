@@ -18,20 +18,28 @@ hipError_t launch_zero(void* p, int64_t bytes, hipStream_t st);
 hipError_t launch_prepare_labels(const int64_t* labels, int64_t N, int64_t Np, int64_t V, int64_t ignore,
                                  int32_t* label32, unsigned long long* n_valid, int32_t* status,
                                  hipStream_t st);
-hipError_t launch_fwd_lse(const Shapes& s, const void* hidden, const void* weight, const void* bias,
-                          const int32_t* label32, float* part_m, float* part_s, float* zlab, hipStream_t st);
-hipError_t launch_finalize_rows(const Shapes& s, const float* part_m, const float* part_s, const float* zlab,
-                                const int32_t* label32, const int32_t* status, int reduction, float* lse_ws,
-                                float* lse_out, float* rowloss_out, double* chunk_acc, hipStream_t st);
+// Forward tiles for rows [g0, g0 + rows) (rows a multiple of 256): half-tile
+// (max, sumexp) partials into part_m/part_s [2 * Vp/256][rows], label logits
+// into zlab, and, when p_out is non-null, bf16 exp(z - max_half) into p_out
+// [rows][Vp].
+hipError_t launch_fwd_tiles(const Shapes& s, const void* hidden, const void* weight, const void* bias,
+                            const int32_t* label32, int64_t g0, int64_t rows, float* part_m, float* part_s,
+                            float* zlab, void* p_out, hipStream_t st);
+hipError_t launch_finalize_rows(const Shapes& s, const float* part_m, const float* part_s, int64_t g0,
+                                int64_t rows, const float* zlab, const int32_t* label32, const int32_t* status,
+                                int reduction, float* lse_ws, float* lse_out, float* rowloss_out,
+                                double* chunk_acc, hipStream_t st);
 hipError_t launch_finalize_loss(const double* chunk_acc, int64_t T, const unsigned long long* n_valid,
                                 const int32_t* status, int reduction, float* loss, float* chunk_out,
                                 hipStream_t st);
 hipError_t launch_transpose(const void* in, int64_t ld_in, int64_t r0, int64_t R_valid, int64_t C, void* out,
                             int64_t ld_out, int64_t R_pad, hipStream_t st);
-hipError_t launch_bwd_dlogits(const Shapes& s, const void* hidden, const void* weight, const void* bias,
-                              const int32_t* label32, const float* lse_ws, const unsigned long long* n_valid,
-                              float grad_scale, int is_mean, int64_t g0, int64_t G, void* dlog, void* dlogT,
-                              float* gb_f32, hipStream_t st);
+// dlogits of one row group from the stored exp(z - max_half) in dlog: G in
+// place (when write_dlog), G^T into dlogT [Vp][G] (when non-null), column
+// sums into gb_f32 (when non-null).
+hipError_t launch_dlogits(const Shapes& s, const int32_t* label32, const float* part_m, const float* lse_ws,
+                          const unsigned long long* n_valid, float grad_scale, int is_mean, int64_t g0, int64_t G,
+                          void* dlog, int write_dlog, void* dlogT, float* gb_f32, hipStream_t st);
 hipError_t launch_grad_hidden(const Shapes& s, const void* dlog, const void* wT, int64_t g0, int64_t G,
                               void* grad_hidden, hipStream_t st);
 hipError_t launch_grad_weight(const Shapes& s, const void* dlogT, const void* hT, int64_t G, int first,

@@ -288,24 +288,40 @@ __global__ void __launch_bounds__(256) k_prepare_labels(const int64_t* __restric
   }
 }
 
+// Staging tile for bf16 outputs that leave through LDS: 256 rows x 256
+// columns, rows padded to 528 B (16-B aligned) so that the epilogue's 2-byte
+// writes of lanes 0..31 and 32..63 (rows r and r+4) use different banks.
+constexpr int STAGE_LD = TILE + 8;                    // u16 per staged row
+constexpr int STAGE_LDS = TILE * STAGE_LD * 2;        // 135168 B
+
 // Forward tile: z = h W^T + b for 256 rows x 256 vocabulary ids, reduced in
-// the epilogue to each row's (max, sum exp(z - max)) over the tile, plus the
-// label logit for rows whose label falls in the tile. z never leaves registers.
+// the epilogue to each row's (max, sum exp(z - max)) over each wave's
+// 128-column half of the tile (part index 2*tile + half), plus the label
+// logit for rows whose label falls in the tile. z never leaves registers.
+// With STORE_P (backward row groups) the tile also writes the bf16
+// unnormalised softmax exp(z - max_half) into p [rows][Vp]; the dlogits pass
+// turns it into G once the row's lse is known, so the logits are computed
+// only once per call.
+template <bool STORE_P>
 __global__ void __launch_bounds__(NTHREADS, 1)
-k_fwd_lse(const u16* __restrict__ hidden, int64_t ldh, const u16* __restrict__ weight, int64_t ldw,
-          const u16* __restrict__ bias, const int32_t* __restrict__ label32, int64_t N, int64_t Np,
-          int64_t V, int64_t H, int n_mt, int n_vt, float* __restrict__ part_m,
-          float* __restrict__ part_s, float* __restrict__ zlab) {
-  __shared__ __attribute__((aligned(16))) char smem_raw[MAINLOOP_LDS];
+k_fwd_tile(const u16* __restrict__ hidden, int64_t ldh, const u16* __restrict__ weight, int64_t ldw,
+           const u16* __restrict__ bias, const int32_t* __restrict__ label32, int64_t N, int64_t V,
+           int64_t Vp, int64_t H, int64_t g0, int64_t ld_part, int n_mt, int n_vt,
+           float* __restrict__ part_m, float* __restrict__ part_s, float* __restrict__ zlab,
+           u16* __restrict__ p_out) {
+  __shared__ __attribute__((aligned(16))) char smem_raw[STORE_P ? STAGE_LDS : MAINLOOP_LDS];
   __shared__ float s_bias[TILE];
   __shared__ int s_lab[TILE];
   __shared__ float s_red_m[2][TILE];
   __shared__ float s_red_s[2][TILE];
   LDS_AS char* smem = (LDS_AS char*)smem_raw;
+  LDS_AS u16* stage = (LDS_AS u16*)smem_raw;
 
   int tm, tn;
   tile_coords(n_mt, n_vt, tm, tn);
-  const int64_t row0 = (int64_t)tm * TILE, col0 = (int64_t)tn * TILE;
+  const int64_t lrow0 = (int64_t)tm * TILE;       // row inside the group (or global row)
+  const int64_t row0 = g0 + lrow0;
+  const int64_t col0 = (int64_t)tn * TILE;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int wm = wave >> 1, wn = wave & 1;
   s_lab[tid] = label32[row0 + tid];
@@ -313,6 +329,7 @@ k_fwd_lse(const u16* __restrict__ hidden, int64_t ldh, const u16* __restrict__ w
 
   Acc acc;
   gemm_tile(acc, hidden, ldh, row0, N, weight, ldw, col0, V, H, smem);
+  if (STORE_P) __syncthreads();   // the staging tile overlays the mainloop's LDS
 
 #pragma unroll
   for (int i = 0; i < NB; ++i) {
@@ -335,7 +352,14 @@ k_fwd_lse(const u16* __restrict__ hidden, int64_t ldh, const u16* __restrict__ w
       float s = 0.f;
       if (m != -INFINITY) {
 #pragma unroll
-        for (int j = 0; j < NB; ++j) s += exp_fast(v[j] - m);
+        for (int j = 0; j < NB; ++j) {
+          const float e = exp_fast(v[j] - m);
+          s += e;
+          if (STORE_P) stage[rl * STAGE_LD + acc_col(wn, j, lane)] = f2bf(e);
+        }
+      } else if (STORE_P) {
+#pragma unroll
+        for (int j = 0; j < NB; ++j) stage[rl * STAGE_LD + acc_col(wn, j, lane)] = 0;
       }
       s = sum16(s);
       if ((lane & 15) == 0) {
@@ -345,34 +369,48 @@ k_fwd_lse(const u16* __restrict__ hidden, int64_t ldh, const u16* __restrict__ w
     }
   }
   __syncthreads();
-  {
-    const float m0 = s_red_m[0][tid], m1 = s_red_m[1][tid];
-    const float s0 = s_red_s[0][tid], s1 = s_red_s[1][tid];
-    const float M = fmaxf(m0, m1);   // m0 is finite: column 0 of every tile is < V
-    float S = s0 * exp_fast(m0 - M);
-    if (m1 != -INFINITY) S += s1 * exp_fast(m1 - M);
-    part_m[(int64_t)tn * Np + row0 + tid] = M;
-    part_s[(int64_t)tn * Np + row0 + tid] = S;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    part_m[(int64_t)(2 * tn + h) * ld_part + lrow0 + tid] = s_red_m[h][tid];
+    part_s[(int64_t)(2 * tn + h) * ld_part + lrow0 + tid] = s_red_s[h][tid];
+  }
+  if (STORE_P) {
+    // 256 rows x 32 sixteen-byte chunks; lanes 0..31 cover one row.
+#pragma unroll 4
+    for (int it = 0; it < TILE * TILE / 8 / NTHREADS; ++it) {
+      const int id = it * NTHREADS + tid;
+      const int row = id >> 5, ch = id & 31;
+      const u32x4 val = *(const LDS_AS u32x4*)(stage + row * STAGE_LD + ch * 8);
+      *(u32x4*)(p_out + (lrow0 + row) * Vp + col0 + ch * 8) = val;
+    }
   }
 }
 
-// Per row: merge the tiles' (max, sumexp) into lse, form l_i, write lse (and
-// l_i for reduction NONE), and add l_i into its chunk's float64 sum.
+// Per row i in [row_begin, row_end): merge the half-tile (max, sumexp)
+// partials into lse, form l_i, write lse (and l_i for reduction NONE), and
+// add l_i into its chunk's float64 sum. Partials of row i sit at
+// part[k * ld_part + (i - part_row0)], k < n_part. Rows in [N, row_end) only
+// get lse_ws = 0.
 __global__ void __launch_bounds__(256) k_finalize_rows(
-    const float* __restrict__ part_m, const float* __restrict__ part_s, const float* __restrict__ zlab,
-    const int32_t* __restrict__ label32, int64_t N, int64_t Np, int n_vt, int64_t chunk_rows,
-    const int32_t* __restrict__ status, int reduction, float* __restrict__ lse_ws,
-    float* __restrict__ lse_out, float* __restrict__ rowloss_out, double* __restrict__ chunk_acc) {
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i >= Np) return;
+    const float* __restrict__ part_m, const float* __restrict__ part_s, int64_t ld_part, int64_t part_row0,
+    int n_part, const float* __restrict__ zlab, const int32_t* __restrict__ label32, int64_t N,
+    int64_t row_begin, int64_t row_end, int64_t chunk_rows, const int32_t* __restrict__ status, int reduction,
+    float* __restrict__ lse_ws, float* __restrict__ lse_out, float* __restrict__ rowloss_out,
+    double* __restrict__ chunk_acc) {
+  const int64_t i = row_begin + (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= row_end) return;
   if (i >= N) {
     lse_ws[i] = 0.f;
     return;
   }
+  const int64_t pi = i - part_row0;
   float M = -INFINITY;
-  for (int t = 0; t < n_vt; ++t) M = fmaxf(M, part_m[(int64_t)t * Np + i]);
+  for (int k = 0; k < n_part; ++k) M = fmaxf(M, part_m[(int64_t)k * ld_part + pi]);
   float S = 0.f;
-  for (int t = 0; t < n_vt; ++t) S += part_s[(int64_t)t * Np + i] * exp_fast(part_m[(int64_t)t * Np + i] - M);
+  for (int k = 0; k < n_part; ++k) {
+    const float mk = part_m[(int64_t)k * ld_part + pi];
+    if (mk != -INFINITY) S += part_s[(int64_t)k * ld_part + pi] * exp_fast(mk - M);
+  }
   const float lse = M + logf(S);
   const int lab = label32[i];
   const float l = lab >= 0 ? lse - zlab[i] : 0.f;
@@ -441,120 +479,112 @@ __global__ void __launch_bounds__(256) k_transpose(const u16* __restrict__ in, i
   }
 }
 
-// Backward tile for one row group: recompute z for 256 rows x 256 ids, form
-// G = s valid (softmax - onehot) in registers, add its column sums into the
-// FP32 bias gradient, and write G (bf16) in the two layouts the gradient
-// products read: dlog [G][Vp] (vocabulary contiguous) and dlogT [Vp][G]
-// (rows contiguous). Rows >= N and ids >= V get exact zeros. Both layouts go
-// out through an LDS staging tile so every global store is 16 bytes and
-// coalesced.
-constexpr int STAGE_LD = TILE + 8;                    // staging row stride (u16): 528 B, 16-B aligned
-constexpr int DLOG_LDS = TILE * STAGE_LD * 2;         // 135168 B
+// dlogits for one 256 x 256 tile of a row group, from the stored
+// unnormalised softmax p~ = exp(z - max_half) (bf16, written by the forward
+// tile): G = s valid (p~ exp(max_half - lse) - [j == y]). G overwrites p~ in
+// dlog [G][Vp] (vocabulary contiguous) when `write_dlog`, and goes to dlogT
+// [Vp][G] (rows contiguous) when non-null; its column sums go into the FP32
+// bias gradient. Each thread owns 8 x 8 blocks: 8 rows of one 16-byte column
+// chunk, loaded and stored with coalesced 16-byte accesses, transposed in
+// registers and staged through LDS for dlogT.
+__device__ __forceinline__ int tswz(int col) { return (col >> 3) & 15; }
 
-__global__ void __launch_bounds__(NTHREADS, 1)
-k_bwd_dlogits(const u16* __restrict__ hidden, int64_t ldh, const u16* __restrict__ weight, int64_t ldw,
-              const u16* __restrict__ bias, const int32_t* __restrict__ label32,
-              const float* __restrict__ lse_ws, const unsigned long long* __restrict__ n_valid,
-              float grad_scale, int is_mean, int64_t N, int64_t V, int64_t Vp, int64_t H, int64_t g0,
-              int64_t G, int n_mt, int n_vt, u16* __restrict__ dlog, u16* __restrict__ dlogT,
-              float* __restrict__ gb_f32) {
-  __shared__ __attribute__((aligned(16))) char smem_raw[DLOG_LDS];
-  __shared__ float s_bias[TILE];
+__global__ void __launch_bounds__(256)
+k_dlogits_from_p(u16* __restrict__ dlog, u16* __restrict__ dlogT, const float* __restrict__ part_m,
+                 const int32_t* __restrict__ label32, const float* __restrict__ lse_ws,
+                 const unsigned long long* __restrict__ n_valid, float grad_scale, int is_mean, int64_t V,
+                 int64_t Vp, int64_t g0, int64_t G, int n_vt, int write_dlog, float* __restrict__ gb_f32) {
+  // transposed staging [256 cols][256 rows] bf16, 16-byte chunks of a column
+  // stored at slot (chunk ^ tswz(col)): conflict-free for both the column
+  // writes (16 lanes, 16 different columns) and the row-chunk reads.
+  __shared__ __attribute__((aligned(16))) u16 tst[TILE * TILE];
+  __shared__ float s_f[2][TILE];
   __shared__ int s_lab[TILE];
-  __shared__ float s_lse[TILE];
-  __shared__ float s_gb[2][TILE];
-  LDS_AS char* smem = (LDS_AS char*)smem_raw;
-  LDS_AS u16* stage = (LDS_AS u16*)smem_raw;
-
-  int tm, tn;
-  tile_coords(n_mt, n_vt, tm, tn);
-  const int64_t lrow0 = (int64_t)tm * TILE;       // row inside the group
-  const int64_t row0 = g0 + lrow0;                 // global row
-  const int64_t col0 = (int64_t)tn * TILE;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int wm = wave >> 1, wn = wave & 1;
-  s_lab[tid] = label32[row0 + tid];
-  s_lse[tid] = lse_ws[row0 + tid];
-  s_bias[tid] = (bias != nullptr && col0 + tid < V) ? bf2f(bias[col0 + tid]) : 0.f;
-
-  Acc acc;
-  gemm_tile(acc, hidden, ldh, row0, N, weight, ldw, col0, V, H, smem);
-
+  __shared__ float s_gb[8][TILE];
+  const int n_mt = (int)(G / TILE);
+  const int tm = blockIdx.x % n_mt, tn = blockIdx.x / n_mt;
+  const int64_t lrow0 = (int64_t)tm * TILE, col0 = (int64_t)tn * TILE;
+  const int tid = threadIdx.x;
   float scale = grad_scale;
   if (is_mean) {
     const unsigned long long nv = *n_valid;
     scale = grad_scale / (float)(nv > 0 ? nv : 1ull);
   }
-  // G in place of z; column sums for the bias gradient; bf16 G into the
-  // staging tile as [row][col].
-  float colsum[NB];
+  {
+    const int64_t row = g0 + lrow0 + tid;
+    const int lab = label32[row];
+    const float lse = lse_ws[row];
+    const bool valid = lab >= 0;
 #pragma unroll
-  for (int j = 0; j < NB; ++j) colsum[j] = 0.f;
+    for (int h = 0; h < 2; ++h) {
+      const float mh = part_m[(int64_t)(2 * tn + h) * G + lrow0 + tid];
+      s_f[h][tid] = (valid && mh != -INFINITY) ? scale * exp_fast(mh - lse) : 0.f;
+    }
+    const int64_t lc = valid ? (int64_t)lab - col0 : -1;
+    s_lab[tid] = (lc >= 0 && lc < TILE) ? (int)lc : -1;
+  }
+  __syncthreads();
+  const int cb = tid & 31;                 // column chunk (8 columns), fixed per thread
+  const int half = cb >> 4;
+  float colsum[8];
 #pragma unroll
-  for (int i = 0; i < NB; ++i) {
+  for (int e = 0; e < 8; ++e) colsum[e] = 0.f;
+#pragma unroll 1
+  for (int it = 0; it < 4; ++it) {
+    const int rb = it * 8 + (tid >> 5);    // row block (8 rows)
+    float d[8][8];                         // [row][col]
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int rl = acc_row(wm, i, r, lane);
-      const int lab = s_lab[rl];
-      const float lse = s_lse[rl];
+    for (int r = 0; r < 8; ++r) {
+      const int rl = rb * 8 + r;
+      u16* src = dlog + (lrow0 + rl) * Vp + col0 + cb * 8;
+      const u32x4 pv = *(const u32x4*)src;
+      const float f = s_f[half][rl];
+      const int lc = s_lab[rl];
+      const float hot = (lc >= 0) ? scale : 0.f;
 #pragma unroll
-      for (int j = 0; j < NB; ++j) {
-        const int cl = acc_col(wn, j, lane);
-        const int64_t col = col0 + cl;
-        const float z = acc.v[i][j][r] + s_bias[cl];
-        const float p = exp_fast(z - lse);
-        float g = scale * (p - ((int64_t)lab == col ? 1.f : 0.f));
-        g = (lab >= 0 && col < V) ? g : 0.f;
-        acc.v[i][j][r] = g;
-        colsum[j] += g;
-        if (dlog) stage[rl * STAGE_LD + cl] = f2bf(g);
+      for (int e = 0; e < 8; ++e) {
+        const uint32_t w = pv[e >> 1];
+        const float pe = bf2f((u16)((e & 1) ? (w >> 16) : (w & 0xFFFF)));
+        const float g = f * pe - ((lc == cb * 8 + e) ? hot : 0.f);
+        d[r][e] = g;
+        colsum[e] += g;
+      }
+      if (write_dlog) {
+        u32x4 o;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) o[w] = (uint32_t)f2bf(d[r][2 * w]) | ((uint32_t)f2bf(d[r][2 * w + 1]) << 16);
+        *(u32x4*)src = o;
+      }
+    }
+    if (dlogT) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int col = cb * 8 + e;
+        u32x4 o;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) o[w] = (uint32_t)f2bf(d[2 * w][e]) | ((uint32_t)f2bf(d[2 * w + 1][e]) << 16);
+        *(LDS_AS u32x4*)((LDS_AS u16*)tst + col * TILE + ((rb ^ tswz(col)) << 3)) = o;
       }
     }
   }
   if (gb_f32) {
-    // lanes l, l^16, l^32, l^48 hold the same column
 #pragma unroll
-    for (int j = 0; j < NB; ++j) {
-      colsum[j] += __shfl_xor(colsum[j], 16, 64);
-      colsum[j] += __shfl_xor(colsum[j], 32, 64);
-    }
-    if (lane < 16) {
-#pragma unroll
-      for (int j = 0; j < NB; ++j) s_gb[wm][acc_col(wn, j, lane)] = colsum[j];
-    }
+    for (int e = 0; e < 8; ++e) s_gb[tid >> 5][cb * 8 + e] = colsum[e];
   }
   __syncthreads();
-  if (gb_f32 && col0 + tid < V) atomicAdd(gb_f32 + col0 + tid, s_gb[0][tid] + s_gb[1][tid]);
-  if (dlog) {
-    // 256 rows x 32 sixteen-byte chunks; lanes 0..31 cover one row.
-#pragma unroll 4
-    for (int it = 0; it < TILE * TILE / 8 / NTHREADS; ++it) {
-      const int id = it * NTHREADS + tid;
-      const int row = id >> 5, ch = id & 31;
-      const u32x4 v = *(const LDS_AS u32x4*)(stage + row * STAGE_LD + ch * 8);
-      *(u32x4*)(dlog + (lrow0 + row) * Vp + col0 + ch * 8) = v;
-    }
-    __syncthreads();
+  if (gb_f32 && col0 + tid < V) {
+    float sum = 0.f;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) sum += s_gb[k][tid];
+    atomicAdd(gb_f32 + col0 + tid, sum);
   }
   if (dlogT) {
-    // [col][row] staging: each lane holds 4 consecutive rows of one column.
-#pragma unroll
-    for (int i = 0; i < NB; ++i) {
-      const int rbase = acc_row(wm, i, 0, lane);
-#pragma unroll
-      for (int j = 0; j < NB; ++j) {
-        u32x2 pk;
-        pk.x = (uint32_t)f2bf(acc.v[i][j][0]) | ((uint32_t)f2bf(acc.v[i][j][1]) << 16);
-        pk.y = (uint32_t)f2bf(acc.v[i][j][2]) | ((uint32_t)f2bf(acc.v[i][j][3]) << 16);
-        *(LDS_AS u32x2*)(stage + acc_col(wn, j, lane) * STAGE_LD + rbase) = pk;
-      }
-    }
-    __syncthreads();
+    // 256 columns x 32 sixteen-byte row chunks; lanes 0..31 cover one column.
 #pragma unroll 4
-    for (int it = 0; it < TILE * TILE / 8 / NTHREADS; ++it) {
-      const int id = it * NTHREADS + tid;
+    for (int it = 0; it < TILE * TILE / 8 / 256; ++it) {
+      const int id = it * 256 + tid;
       const int col = id >> 5, ch = id & 31;
-      const u32x4 v = *(const LDS_AS u32x4*)(stage + col * STAGE_LD + ch * 8);
+      const u32x4 v = *(const LDS_AS u32x4*)((LDS_AS u16*)tst + col * TILE + ((ch ^ tswz(col)) << 3));
       *(u32x4*)(dlogT + (col0 + col) * G + lrow0 + ch * 8) = v;
     }
   }
@@ -647,21 +677,29 @@ hipError_t launch_prepare_labels(const int64_t* labels, int64_t N, int64_t Np, i
   return hipGetLastError();
 }
 
-hipError_t launch_fwd_lse(const Shapes& s, const void* hidden, const void* weight, const void* bias,
-                          const int32_t* label32, float* part_m, float* part_s, float* zlab, hipStream_t st) {
-  const int n_mt = (int)(s.Np / TILE), n_vt = (int)(s.Vp / TILE);
-  hipLaunchKernelGGL(k_fwd_lse, dim3((unsigned)(n_mt * n_vt)), dim3(NTHREADS), 0, st, (const u16*)hidden,
-                     s.ldh, (const u16*)weight, s.ldw, (const u16*)bias, label32, s.N, s.Np, s.V, s.H, n_mt,
-                     n_vt, part_m, part_s, zlab);
+hipError_t launch_fwd_tiles(const Shapes& s, const void* hidden, const void* weight, const void* bias,
+                            const int32_t* label32, int64_t g0, int64_t rows, float* part_m, float* part_s,
+                            float* zlab, void* p_out, hipStream_t st) {
+  const int n_mt = (int)(rows / TILE), n_vt = (int)(s.Vp / TILE);
+  const dim3 grid((unsigned)(n_mt * n_vt)), block(NTHREADS);
+  if (p_out)
+    hipLaunchKernelGGL(k_fwd_tile<true>, grid, block, 0, st, (const u16*)hidden, s.ldh, (const u16*)weight, s.ldw,
+                       (const u16*)bias, label32, s.N, s.V, s.Vp, s.H, g0, rows, n_mt, n_vt, part_m, part_s, zlab,
+                       (u16*)p_out);
+  else
+    hipLaunchKernelGGL(k_fwd_tile<false>, grid, block, 0, st, (const u16*)hidden, s.ldh, (const u16*)weight,
+                       s.ldw, (const u16*)bias, label32, s.N, s.V, s.Vp, s.H, g0, rows, n_mt, n_vt, part_m,
+                       part_s, zlab, (u16*)nullptr);
   return hipGetLastError();
 }
 
-hipError_t launch_finalize_rows(const Shapes& s, const float* part_m, const float* part_s, const float* zlab,
-                                const int32_t* label32, const int32_t* status, int reduction, float* lse_ws,
-                                float* lse_out, float* rowloss_out, double* chunk_acc, hipStream_t st) {
-  hipLaunchKernelGGL(k_finalize_rows, dim3((unsigned)(s.Np / 256)), dim3(256), 0, st, part_m, part_s, zlab,
-                     label32, s.N, s.Np, (int)(s.Vp / TILE), s.chunk_rows, status, reduction, lse_ws, lse_out,
-                     rowloss_out, chunk_acc);
+hipError_t launch_finalize_rows(const Shapes& s, const float* part_m, const float* part_s, int64_t g0,
+                                int64_t rows, const float* zlab, const int32_t* label32, const int32_t* status,
+                                int reduction, float* lse_ws, float* lse_out, float* rowloss_out,
+                                double* chunk_acc, hipStream_t st) {
+  hipLaunchKernelGGL(k_finalize_rows, dim3((unsigned)(rows / 256)), dim3(256), 0, st, part_m, part_s, rows, g0,
+                     (int)(2 * (s.Vp / TILE)), zlab, label32, s.N, g0, g0 + rows, s.chunk_rows, status, reduction,
+                     lse_ws, lse_out, rowloss_out, chunk_acc);
   return hipGetLastError();
 }
 
@@ -681,14 +719,13 @@ hipError_t launch_transpose(const void* in, int64_t ld_in, int64_t r0, int64_t R
   return hipGetLastError();
 }
 
-hipError_t launch_bwd_dlogits(const Shapes& s, const void* hidden, const void* weight, const void* bias,
-                              const int32_t* label32, const float* lse_ws, const unsigned long long* n_valid,
-                              float grad_scale, int is_mean, int64_t g0, int64_t G, void* dlog, void* dlogT,
-                              float* gb_f32, hipStream_t st) {
+hipError_t launch_dlogits(const Shapes& s, const int32_t* label32, const float* part_m, const float* lse_ws,
+                          const unsigned long long* n_valid, float grad_scale, int is_mean, int64_t g0, int64_t G,
+                          void* dlog, int write_dlog, void* dlogT, float* gb_f32, hipStream_t st) {
   const int n_mt = (int)(G / TILE), n_vt = (int)(s.Vp / TILE);
-  hipLaunchKernelGGL(k_bwd_dlogits, dim3((unsigned)(n_mt * n_vt)), dim3(NTHREADS), 0, st, (const u16*)hidden,
-                     s.ldh, (const u16*)weight, s.ldw, (const u16*)bias, label32, lse_ws, n_valid, grad_scale,
-                     is_mean, s.N, s.V, s.Vp, s.H, g0, G, n_mt, n_vt, (u16*)dlog, (u16*)dlogT, gb_f32);
+  hipLaunchKernelGGL(k_dlogits_from_p, dim3((unsigned)(n_mt * n_vt)), dim3(256), 0, st, (u16*)dlog, (u16*)dlogT,
+                     part_m, label32, lse_ws, n_valid, grad_scale, is_mean, s.V, s.Vp, g0, G, n_vt, write_dlog,
+                     gb_f32);
   return hipGetLastError();
 }
 

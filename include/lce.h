@@ -125,7 +125,11 @@ int lce_forward_backward(const lce_problem* p, const void* hidden, const void* w
  * kernel launch on `stream`, sets kinds[i] to the launched kernel's
  * lce_kernel_kind, and stops recording (silently) once `capacity` pairs are
  * used; `count` returns the number of pairs recorded. Results are otherwise
- * identical to the untraced call. */
+ * identical to the untraced call.
+ * LCE_K_FWD_LSE is the logits-tile kernel with the log-sum-exp epilogue (in
+ * lce_forward_backward it also stores each row group's exp(z - max) tiles);
+ * LCE_K_BWD_DLOGITS turns those stored tiles into the bf16 dlogits of the
+ * group (an element-wise pass, no product). */
 typedef enum {
   LCE_K_ZERO = 0, LCE_K_PREPARE_LABELS = 1, LCE_K_FWD_LSE = 2, LCE_K_FINALIZE_ROWS = 3,
   LCE_K_FINALIZE_LOSS = 4, LCE_K_TRANSPOSE = 5, LCE_K_BWD_DLOGITS = 6, LCE_K_GRAD_HIDDEN = 7,
@@ -138,7 +142,8 @@ typedef struct {
   int32_t capacity;
   int32_t count;       /* written */
   /* For each recorded launch: rows, columns and depth of the product it
-   * computes (0 for non-product kernels), so throughput can be derived. */
+   * computes, so throughput can be derived; element-wise passes over a
+   * [rows, columns] block record depth 0; other kernels record zeros. */
   int64_t* dims;       /* [3 * capacity], written; nullable */
 } lce_trace;
 
