@@ -390,27 +390,43 @@ k_fwd_tile(const u16* __restrict__ hidden, int64_t ldh, const u16* __restrict__ 
 // partials into lse, form l_i, write lse (and l_i for reduction NONE), and
 // add l_i into its chunk's float64 sum. Partials of row i sit at
 // part[k * ld_part + (i - part_row0)], k < n_part. Rows in [N, row_end) only
-// get lse_ws = 0.
+// get lse_ws = 0. A block takes 64 rows; its 4 waves each merge every 4th
+// partial of those rows (256-byte coalesced reads), then combine in LDS.
+constexpr int FIN_ROWS = 64;
+
+__device__ __forceinline__ void merge_ms(float& M, float& S, float mk, float sk) {
+  if (mk == -INFINITY) return;
+  const float mn = fmaxf(M, mk);
+  S = S * exp_fast(M - mn) + sk * exp_fast(mk - mn);
+  M = mn;
+}
+
 __global__ void __launch_bounds__(256) k_finalize_rows(
     const float* __restrict__ part_m, const float* __restrict__ part_s, int64_t ld_part, int64_t part_row0,
     int n_part, const float* __restrict__ zlab, const int32_t* __restrict__ label32, int64_t N,
     int64_t row_begin, int64_t row_end, int64_t chunk_rows, const int32_t* __restrict__ status, int reduction,
     float* __restrict__ lse_ws, float* __restrict__ lse_out, float* __restrict__ rowloss_out,
     double* __restrict__ chunk_acc) {
-  const int64_t i = row_begin + (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i >= row_end) return;
+  __shared__ float s_m[4][FIN_ROWS], s_s[4][FIN_ROWS];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t i = row_begin + (int64_t)blockIdx.x * FIN_ROWS + lane;
+  const bool live = i < row_end && i < N;
+  float M = -INFINITY, S = 0.f;
+  if (live) {
+    const int64_t pi = i - part_row0;
+#pragma unroll 8
+    for (int k = wave; k < n_part; k += 4)
+      merge_ms(M, S, part_m[(int64_t)k * ld_part + pi], part_s[(int64_t)k * ld_part + pi]);
+  }
+  s_m[wave][lane] = M;
+  s_s[wave][lane] = S;
+  __syncthreads();
+  if (wave != 0 || i >= row_end) return;
   if (i >= N) {
     lse_ws[i] = 0.f;
     return;
   }
-  const int64_t pi = i - part_row0;
-  float M = -INFINITY;
-  for (int k = 0; k < n_part; ++k) M = fmaxf(M, part_m[(int64_t)k * ld_part + pi]);
-  float S = 0.f;
-  for (int k = 0; k < n_part; ++k) {
-    const float mk = part_m[(int64_t)k * ld_part + pi];
-    if (mk != -INFINITY) S += part_s[(int64_t)k * ld_part + pi] * exp_fast(mk - M);
-  }
+  for (int w = 1; w < 4; ++w) merge_ms(M, S, s_m[w][lane], s_s[w][lane]);
   const float lse = M + logf(S);
   const int lab = label32[i];
   const float l = lab >= 0 ? lse - zlab[i] : 0.f;
@@ -479,38 +495,39 @@ __global__ void __launch_bounds__(256) k_transpose(const u16* __restrict__ in, i
   }
 }
 
-// dlogits for one 256 x 256 tile of a row group, from the stored
-// unnormalised softmax p~ = exp(z - max_half) (bf16, written by the forward
-// tile): G = s valid (p~ exp(max_half - lse) - [j == y]). G overwrites p~ in
-// dlog [G][Vp] (vocabulary contiguous) when `write_dlog`, and goes to dlogT
-// [Vp][G] (rows contiguous) when non-null; its column sums go into the FP32
-// bias gradient. Each thread owns 8 x 8 blocks: 8 rows of one 16-byte column
-// chunk, loaded and stored with coalesced 16-byte accesses, transposed in
-// registers and staged through LDS for dlogT.
+// dlogits for one 128-row x 256-column block of a row group, from the
+// stored unnormalised softmax p~ = exp(z - max_half) (bf16, written by the
+// forward tile): G = s valid (p~ exp(max_half - lse) - [j == y]). G
+// overwrites p~ in dlog [G][Vp] (vocabulary contiguous) when `write_dlog`,
+// and goes to dlogT [Vp][G] (rows contiguous) when non-null; its column sums
+// go into the FP32 bias gradient. Each thread owns 8 x 8 blocks: 8 rows of
+// one 16-byte column chunk, all 8 loads issued before any use, transposed in
+// registers and staged through LDS for dlogT. 72 KB of LDS: two blocks per CU.
+constexpr int DL_ROWS = 128;
 __device__ __forceinline__ int tswz(int col) { return (col >> 3) & 15; }
 
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(256, 2)
 k_dlogits_from_p(u16* __restrict__ dlog, u16* __restrict__ dlogT, const float* __restrict__ part_m,
                  const int32_t* __restrict__ label32, const float* __restrict__ lse_ws,
                  const unsigned long long* __restrict__ n_valid, float grad_scale, int is_mean, int64_t V,
-                 int64_t Vp, int64_t g0, int64_t G, int n_vt, int write_dlog, float* __restrict__ gb_f32) {
-  // transposed staging [256 cols][256 rows] bf16, 16-byte chunks of a column
-  // stored at slot (chunk ^ tswz(col)): conflict-free for both the column
-  // writes (16 lanes, 16 different columns) and the row-chunk reads.
-  __shared__ __attribute__((aligned(16))) u16 tst[TILE * TILE];
-  __shared__ float s_f[2][TILE];
-  __shared__ int s_lab[TILE];
+                 int64_t Vp, int64_t g0, int64_t G, int write_dlog, float* __restrict__ gb_f32) {
+  // transposed staging [256 cols][128 rows] bf16; the 16-byte row chunk c of
+  // column col is stored at slot c ^ tswz(col): conflict-free for the column
+  // writes (16 lanes, 16 different columns) and for the chunk reads.
+  __shared__ __attribute__((aligned(16))) u16 tst[TILE * DL_ROWS];
+  __shared__ float s_f[2][DL_ROWS];
+  __shared__ int s_lab[DL_ROWS];
   __shared__ float s_gb[8][TILE];
-  const int n_mt = (int)(G / TILE);
+  const int n_mt = (int)(G / DL_ROWS);
   const int tm = blockIdx.x % n_mt, tn = blockIdx.x / n_mt;
-  const int64_t lrow0 = (int64_t)tm * TILE, col0 = (int64_t)tn * TILE;
+  const int64_t lrow0 = (int64_t)tm * DL_ROWS, col0 = (int64_t)tn * TILE;
   const int tid = threadIdx.x;
   float scale = grad_scale;
   if (is_mean) {
     const unsigned long long nv = *n_valid;
     scale = grad_scale / (float)(nv > 0 ? nv : 1ull);
   }
-  {
+  if (tid < DL_ROWS) {
     const int64_t row = g0 + lrow0 + tid;
     const int lab = label32[row];
     const float lse = lse_ws[row];
@@ -530,30 +547,34 @@ k_dlogits_from_p(u16* __restrict__ dlog, u16* __restrict__ dlogT, const float* _
 #pragma unroll
   for (int e = 0; e < 8; ++e) colsum[e] = 0.f;
 #pragma unroll 1
-  for (int it = 0; it < 4; ++it) {
+  for (int it = 0; it < DL_ROWS / 64; ++it) {
     const int rb = it * 8 + (tid >> 5);    // row block (8 rows)
+    u16* src = dlog + (lrow0 + rb * 8) * Vp + col0 + cb * 8;
+    u32x4 pv[8];
+#pragma unroll
+    for (int r = 0; r < 8; ++r) pv[r] = *(const u32x4*)(src + r * Vp);
     float d[8][8];                         // [row][col]
 #pragma unroll
     for (int r = 0; r < 8; ++r) {
       const int rl = rb * 8 + r;
-      u16* src = dlog + (lrow0 + rl) * Vp + col0 + cb * 8;
-      const u32x4 pv = *(const u32x4*)src;
       const float f = s_f[half][rl];
       const int lc = s_lab[rl];
-      const float hot = (lc >= 0) ? scale : 0.f;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const uint32_t w = pv[e >> 1];
+        const uint32_t w = pv[r][e >> 1];
         const float pe = bf2f((u16)((e & 1) ? (w >> 16) : (w & 0xFFFF)));
-        const float g = f * pe - ((lc == cb * 8 + e) ? hot : 0.f);
+        const float g = f * pe - ((lc == cb * 8 + e) ? scale : 0.f);
         d[r][e] = g;
         colsum[e] += g;
       }
-      if (write_dlog) {
+    }
+    if (write_dlog) {
+#pragma unroll
+      for (int r = 0; r < 8; ++r) {
         u32x4 o;
 #pragma unroll
         for (int w = 0; w < 4; ++w) o[w] = (uint32_t)f2bf(d[r][2 * w]) | ((uint32_t)f2bf(d[r][2 * w + 1]) << 16);
-        *(u32x4*)src = o;
+        *(u32x4*)(src + r * Vp) = o;
       }
     }
     if (dlogT) {
@@ -563,7 +584,7 @@ k_dlogits_from_p(u16* __restrict__ dlog, u16* __restrict__ dlogT, const float* _
         u32x4 o;
 #pragma unroll
         for (int w = 0; w < 4; ++w) o[w] = (uint32_t)f2bf(d[2 * w][e]) | ((uint32_t)f2bf(d[2 * w + 1][e]) << 16);
-        *(LDS_AS u32x4*)((LDS_AS u16*)tst + col * TILE + ((rb ^ tswz(col)) << 3)) = o;
+        *(LDS_AS u32x4*)((LDS_AS u16*)tst + col * DL_ROWS + ((rb ^ tswz(col)) << 3)) = o;
       }
     }
   }
@@ -579,12 +600,12 @@ k_dlogits_from_p(u16* __restrict__ dlog, u16* __restrict__ dlogT, const float* _
     atomicAdd(gb_f32 + col0 + tid, sum);
   }
   if (dlogT) {
-    // 256 columns x 32 sixteen-byte row chunks; lanes 0..31 cover one column.
+    // 256 columns x 16 sixteen-byte row chunks; 16 lanes cover one column.
 #pragma unroll 4
-    for (int it = 0; it < TILE * TILE / 8 / 256; ++it) {
+    for (int it = 0; it < TILE * DL_ROWS / 8 / 256; ++it) {
       const int id = it * 256 + tid;
-      const int col = id >> 5, ch = id & 31;
-      const u32x4 v = *(const LDS_AS u32x4*)((LDS_AS u16*)tst + col * TILE + ((ch ^ tswz(col)) << 3));
+      const int col = id >> 4, ch = id & 15;
+      const u32x4 v = *(const LDS_AS u32x4*)((LDS_AS u16*)tst + col * DL_ROWS + ((ch ^ tswz(col)) << 3));
       *(u32x4*)(dlogT + (col0 + col) * G + lrow0 + ch * 8) = v;
     }
   }
@@ -697,7 +718,7 @@ hipError_t launch_finalize_rows(const Shapes& s, const float* part_m, const floa
                                 int64_t rows, const float* zlab, const int32_t* label32, const int32_t* status,
                                 int reduction, float* lse_ws, float* lse_out, float* rowloss_out,
                                 double* chunk_acc, hipStream_t st) {
-  hipLaunchKernelGGL(k_finalize_rows, dim3((unsigned)(rows / 256)), dim3(256), 0, st, part_m, part_s, rows, g0,
+  hipLaunchKernelGGL(k_finalize_rows, dim3((unsigned)(rows / FIN_ROWS)), dim3(256), 0, st, part_m, part_s, rows, g0,
                      (int)(2 * (s.Vp / TILE)), zlab, label32, s.N, g0, g0 + rows, s.chunk_rows, status, reduction,
                      lse_ws, lse_out, rowloss_out, chunk_acc);
   return hipGetLastError();
@@ -722,10 +743,9 @@ hipError_t launch_transpose(const void* in, int64_t ld_in, int64_t r0, int64_t R
 hipError_t launch_dlogits(const Shapes& s, const int32_t* label32, const float* part_m, const float* lse_ws,
                           const unsigned long long* n_valid, float grad_scale, int is_mean, int64_t g0, int64_t G,
                           void* dlog, int write_dlog, void* dlogT, float* gb_f32, hipStream_t st) {
-  const int n_mt = (int)(G / TILE), n_vt = (int)(s.Vp / TILE);
+  const int n_mt = (int)(G / DL_ROWS), n_vt = (int)(s.Vp / TILE);
   hipLaunchKernelGGL(k_dlogits_from_p, dim3((unsigned)(n_mt * n_vt)), dim3(256), 0, st, (u16*)dlog, (u16*)dlogT,
-                     part_m, label32, lse_ws, n_valid, grad_scale, is_mean, s.V, s.Vp, g0, G, n_vt, write_dlog,
-                     gb_f32);
+                     part_m, label32, lse_ws, n_valid, grad_scale, is_mean, s.V, s.Vp, g0, G, write_dlog, gb_f32);
   return hipGetLastError();
 }
 
