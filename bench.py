@@ -15,7 +15,10 @@ chunk_rows=256, sum reduction), seeded synthetic inputs (lce_inputs recipe).
 The JSON line also carries:
   roofline      the dominant kernel's throughput from HIP events the library
                 records around each launch during the timed steps, against the
-                MI355X dense bf16 MFMA peak;
+                MI355X dense bf16 MFMA peak; `traffic` is the HBM bytes per
+                launch measured with rocprofv3 FETCH_SIZE / WRITE_SIZE counters
+                (profiles/<kernel>_<workload>_traffic.md), reported only while
+                the kernel source still has the hash recorded there;
   cpu_baseline  the float64 CPU oracle timed on a bounded row sample of the
                 same workload on this host's cores.
 """
@@ -131,6 +134,29 @@ def cpu_baseline(inp, w, rows: int) -> dict:
             "seconds": dt}
 
 
+KERNEL_SOURCE = os.path.join(ROOT, "chunked_lm_head_lce_amd", "csrc", "lce_kernels.hip")
+
+
+def measured_traffic(kernel: str, workload: str):
+    """HBM bytes per launch of `kernel` on `workload` from the committed
+    counter summary, or None when there is none or the kernel source changed
+    since the counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_traffic.md")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    for line in open(path):
+        if ":" in line and line.startswith("- "):
+            k, v = line[2:].split(":", 1)
+            fields[k.strip()] = v.strip().strip("`")
+    with open(KERNEL_SOURCE, "rb") as f:
+        digest = hashlib.sha256(f.read()).hexdigest()
+    if fields.get("kernel_source_sha256") != digest or "hbm_bytes_per_launch" not in fields:
+        return None
+    return float(fields["hbm_bytes_per_launch"])
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -139,7 +165,7 @@ def main() -> int:
     ap.add_argument("--workload", default="qwen3_8b_1m_shard")
     ap.add_argument("--rows-in-flight", type=int, default=0)
     ap.add_argument("--fwd-steps", type=int, default=3)
-    ap.add_argument("--cpu-rows", type=int, default=1024)
+    ap.add_argument("--cpu-rows", type=int, default=4096)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-gib", type=float, default=0.0,
                     help="also run one plain device-to-device copy of this many GiB (a kernel of known "
@@ -242,7 +268,8 @@ def main() -> int:
     dom = kernels[dom_name]
     achieved = dom["tflops"] or 0.0
     roofline = {"bound": "mfma", "kernel": dom_name, "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
-                "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None,
+                "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
+                "traffic": measured_traffic(dom_name, w.name), "traffic_unit": "bytes/launch",
                 "avg_launch_ms": dom["avg_launch_ms"], "launches_per_step": dom["launches_per_step"]}
 
     cpu = None

@@ -12,10 +12,11 @@
 //   C[m][n] = sum_k X[m][k] * Y[n][k]        (both operands K-contiguous)
 // for a 256 x 256 output tile, so the kernels differ only in their operands
 // and epilogues:
-//   forward   z tile   X = hidden rows,    Y = weight rows,      K = H
-//   backward  z tile   (same, recomputed), epilogue writes dlogits (bf16)
-//             grad_hidden  X = dlogits [G][Vp], Y = W^T [H][Vp],  K = Vp
-//             grad_weight  X = dlogits^T [Vp][G], Y = h^T [H][G], K = G
+//   z tile       X = hidden rows,       Y = weight rows,  K = H
+//                (per backward row group the epilogue also keeps bf16
+//                exp(z - max), which an element-wise pass turns into G)
+//   grad_hidden  X = dlogits [G][Vp],   Y = W^T [H][Vp],  K = Vp
+//   grad_weight  X = dlogits^T [Vp][G], Y = h^T [H][G],   K = G
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 #include <math.h>
