@@ -28,7 +28,7 @@ EXPORTED = ("lce_workspace_bytes", "lce_forward", "lce_forward_backward", "lce_f
             "lce_forward_backward_traced", "lce_status_string", "lce_abi_version")
 
 KERNEL_KINDS = ("zero", "prepare_labels", "fwd_lse", "finalize_rows", "finalize_loss", "transpose",
-                "bwd_dlogits", "grad_hidden", "grad_weight", "cast")
+                "bwd_dlogits", "grad_hidden", "grad_weight", "cast", "label_logit")
 
 
 class LceProblem(ctypes.Structure):

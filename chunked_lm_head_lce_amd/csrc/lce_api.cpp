@@ -15,6 +15,8 @@ using lce::Shapes;
 
 constexpr int64_t kTile = 256;
 constexpr int64_t kDefaultRowsInFlight = 16384;
+constexpr int64_t kMaxRowsInFlight = int64_t(1) << 20;
+constexpr int64_t kMaxStride = int64_t(1) << 22;
 
 int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -37,6 +39,8 @@ int validate_problem(const lce_problem* p) {
   if (p->dtype != LCE_DTYPE_BF16) return LCE_ERR_UNSUPPORTED;
   if (p->hidden % 64 != 0) return LCE_ERR_UNSUPPORTED;
   if (p->ld_hidden % 8 != 0 || p->ld_weight % 8 != 0) return LCE_ERR_UNSUPPORTED;
+  // 256 rows of any operand must span < 4 GiB (32-bit load offsets)
+  if (p->ld_hidden > kMaxStride || p->ld_weight > kMaxStride || p->vocab > kMaxStride) return LCE_ERR_UNSUPPORTED;
   // labels and tile indices are 32-bit on the device
   if (p->vocab > (int64_t)INT32_MAX - 1024 || p->n_rows > (int64_t)INT32_MAX - 1024) return LCE_ERR_UNSUPPORTED;
   const int64_t tiles = round_up(p->n_rows, kTile) / kTile * (round_up(p->vocab, kTile) / kTile);
@@ -59,7 +63,7 @@ Shapes shapes_of(const lce_problem* p) {
 
 int64_t group_rows(const lce_problem* p, const Shapes& s) {
   int64_t g = p->rows_in_flight > 0 ? p->rows_in_flight : kDefaultRowsInFlight;
-  g = round_up(g, kTile);
+  g = round_up(g < kMaxRowsInFlight ? g : kMaxRowsInFlight, kTile);
   return g < s.Np ? g : s.Np;
 }
 
@@ -199,6 +203,14 @@ int run_prepare(Common& c, const int64_t* labels, int64_t* n_valid_out, int32_t*
   return LCE_OK;
 }
 
+// Label logits of every valid row (the gather half of the NLL).
+int run_label_logits(Common& c, const void* hidden, const void* weight, const void* bias, hipStream_t st,
+                     Tracer& tr) {
+  LCE_LAUNCH(tr, LCE_K_LABEL_LOGIT, 0, 0, 0,
+             lce::launch_label_logit(c.s, hidden, weight, bias, c.label32, c.zlab, st));
+  return LCE_OK;
+}
+
 // Logits tiles with the online log-sum-exp epilogue for rows [g0, g0+rows),
 // then per-row lse / NLL / chunk sums. With p_out the tiles also leave
 // exp(z - max_half) behind for the gradient of the same rows.
@@ -207,8 +219,7 @@ int run_rows(Common& c, const void* hidden, const void* weight, const void* bias
   const Shapes& s = c.s;
   const int64_t rows_valid = (s.N - g0) < rows ? (s.N - g0) : rows;
   LCE_LAUNCH(tr, LCE_K_FWD_LSE, rows_valid, s.V, s.H,
-             lce::launch_fwd_tiles(s, hidden, weight, bias, c.label32, g0, rows, c.part_m, c.part_s, c.zlab, p_out,
-                                   st));
+             lce::launch_fwd_tiles(s, hidden, weight, bias, g0, rows, c.part_m, c.part_s, p_out, st));
   LCE_LAUNCH(tr, LCE_K_FINALIZE_ROWS, 0, 0, 0,
              lce::launch_finalize_rows(s, c.part_m, c.part_s, g0, rows, c.zlab, c.label32, c.status,
                                        c.p->reduction, c.lse_ws, lse_out,
@@ -220,7 +231,7 @@ int run_rows(Common& c, const void* hidden, const void* weight, const void* bias
 
 extern "C" {
 
-int lce_abi_version(void) { return 100; }
+int lce_abi_version(void) { return 101; }
 
 const char* lce_status_string(int status) {
   switch (status) {
@@ -254,6 +265,8 @@ int lce_forward_traced(const lce_problem* p, const void* hidden, const void* wei
   st = run_prepare(c, labels, n_valid, status, stream, tr);
   if (st != LCE_OK) return st;
   if (c.s.N > 0) {
+    st = run_label_logits(c, hidden, weight, bias, stream, tr);
+    if (st != LCE_OK) return st;
     st = run_rows(c, hidden, weight, bias, 0, c.s.Np, nullptr, loss, lse, stream, tr);
     if (st != LCE_OK) return st;
   }
@@ -304,6 +317,8 @@ int lce_forward_backward_traced(const lce_problem* p, const void* hidden, const 
   if (s.N == 0) {
     if (need_gw) LCE_LAUNCH(tr, LCE_K_ZERO, 0, 0, 0, lce::launch_zero(gw, s.V * s.H * 4, stream));
   } else {
+    st = run_label_logits(c, hidden, weight, bias, stream, tr);
+    if (st != LCE_OK) return st;
     // Row groups: the logits of a group are computed once; the tiles leave
     // exp(z - max_half) in dlog, the group's lse follows, and the dlogits
     // pass turns dlog into G (and G^T) for the two gradient products.

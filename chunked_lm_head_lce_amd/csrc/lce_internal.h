@@ -19,12 +19,13 @@ hipError_t launch_prepare_labels(const int64_t* labels, int64_t N, int64_t Np, i
                                  int32_t* label32, unsigned long long* n_valid, int32_t* status,
                                  hipStream_t st);
 // Forward tiles for rows [g0, g0 + rows) (rows a multiple of 256): half-tile
-// (max, sumexp) partials into part_m/part_s [2 * Vp/256][rows], label logits
-// into zlab, and, when p_out is non-null, bf16 exp(z - max_half) into p_out
-// [rows][Vp].
-hipError_t launch_fwd_tiles(const Shapes& s, const void* hidden, const void* weight, const void* bias,
-                            const int32_t* label32, int64_t g0, int64_t rows, float* part_m, float* part_s,
-                            float* zlab, void* p_out, hipStream_t st);
+// (max, sumexp) partials into part_m/part_s [2 * Vp/256][rows] and, when
+// p_out is non-null, bf16 exp(z - max_half) into p_out [rows][Vp].
+hipError_t launch_fwd_tiles(const Shapes& s, const void* hidden, const void* weight, const void* bias, int64_t g0,
+                            int64_t rows, float* part_m, float* part_s, void* p_out, hipStream_t st);
+// zlab[i] = h_i . W_{y_i} + b_{y_i} for valid rows.
+hipError_t launch_label_logit(const Shapes& s, const void* hidden, const void* weight, const void* bias,
+                              const int32_t* label32, float* zlab, hipStream_t st);
 hipError_t launch_finalize_rows(const Shapes& s, const float* part_m, const float* part_s, int64_t g0,
                                 int64_t rows, const float* zlab, const int32_t* label32, const int32_t* status,
                                 int reduction, float* lse_ws, float* lse_out, float* rowloss_out,

@@ -34,18 +34,20 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int TILE = 256;                 // output tile edge (rows and columns)
-constexpr int BK = 64;                    // K depth of one LDS stage
+constexpr int BK = 32;                    // K depth of one LDS stage (one MFMA step)
+constexpr int NBUF = 4;                   // LDS stage buffers (up to 3 stages in flight)
 constexpr int NTHREADS = 256;             // 4 waves, 2 x 2, each owns 128 x 128
 constexpr int NB = 8;                     // 16 x 16 MFMA blocks per wave edge (128 / 16)
-constexpr int OPERAND_STAGE = TILE * BK * 2;       // 32 KB: one operand, one stage
-constexpr int STAGE = 2 * OPERAND_STAGE;           // 64 KB: both operands
-constexpr int MAINLOOP_LDS = 2 * STAGE;            // 128 KB: double buffered
+constexpr int OPERAND_STAGE = TILE * BK * 2;       // 16 KB: one operand, one stage
+constexpr int STAGE = 2 * OPERAND_STAGE;           // 32 KB: both operands
+constexpr int MAINLOOP_LDS = NBUF * STAGE;         // 128 KB
 constexpr float LOG2E = 1.4426950408889634f;       // log2(e): exp(x) = 2^(x log2 e)
 // s_waitcnt immediates (gfx9 encoding: vmcnt [3:0]+[15:14], expcnt [6:4],
 // lgkmcnt [11:8]); the other counters are left at their maximum (no wait).
 constexpr int WAIT_LGKM0 = 0xC07F;   // lgkmcnt(0)
 #define WAIT_LGKM(n) (0xC07F | ((n) << 8))   // lgkmcnt(n), n <= 15
 constexpr int WAIT_VM0 = 0x0F70;     // vmcnt(0)
+#define WAIT_VM(n) (((n) & 15) | (((n) >> 4) << 14) | 0x0F70)   // vmcnt(n), n <= 63
 
 __device__ __forceinline__ float bf2f(u16 u) { return __builtin_bit_cast(float, (uint32_t)u << 16); }
 __device__ __forceinline__ u16 f2bf(float x) {
@@ -54,16 +56,30 @@ __device__ __forceinline__ u16 f2bf(float x) {
 }
 __device__ __forceinline__ float exp_fast(float x) { return __builtin_amdgcn_exp2f(x * LOG2E); }
 
-// Reductions across the 16 lanes that hold one accumulator row.
+// Reductions across the 16 lanes that hold one accumulator row, with DPP
+// lane permutations (plain VALU operations, no LDS round trip): swap lanes
+// within pairs, then within quads, then mirror each 8-lane half, then mirror
+// the 16-lane row; each step combines two disjoint groups, so after four
+// steps every lane holds the result over its 16 lanes.
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+constexpr int DPP_XOR1 = 0xB1;          // quad_perm [1,0,3,2]
+constexpr int DPP_XOR2 = 0x4E;          // quad_perm [2,3,0,1]
+constexpr int DPP_HALF_MIRROR = 0x141;  // lane i <- 7 - i within each 8 lanes
+constexpr int DPP_MIRROR = 0x140;       // lane i <- 15 - i within each 16 lanes
 __device__ __forceinline__ float max16(float v) {
-#pragma unroll
-  for (int o = 8; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-  return v;
+  v = fmaxf(v, dpp<DPP_XOR1>(v));
+  v = fmaxf(v, dpp<DPP_XOR2>(v));
+  v = fmaxf(v, dpp<DPP_HALF_MIRROR>(v));
+  return fmaxf(v, dpp<DPP_MIRROR>(v));
 }
 __device__ __forceinline__ float sum16(float v) {
-#pragma unroll
-  for (int o = 8; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
-  return v;
+  v += dpp<DPP_XOR1>(v);
+  v += dpp<DPP_XOR2>(v);
+  v += dpp<DPP_HALF_MIRROR>(v);
+  return v + dpp<DPP_MIRROR>(v);
 }
 
 // ---------------------------------------------------------------------------
@@ -88,39 +104,38 @@ __device__ __forceinline__ void tile_coords(int n_m, int n_n, int& tm, int& tn) 
 }
 
 // ---------------------------------------------------------------------------
-// LDS stage layout: operand tile [256 rows][64 k] bf16, 128 B per row, the
-// eight 16-byte k-chunks of row r stored at chunk slot (c ^ swz(r)).
-// A fragment load reads one chunk from 32 consecutive rows; the LDS serves
-// 16 lanes x 16 B = 256 B per clock across 64 banks, where rows r and r+1
-// fall in opposite halves. swz(r) = (r >> 1) & 7 gives the 16 rows of each
-// group 16 distinct (half, slot) pairs, so the reads are conflict-free.
+// LDS stage layout: operand tile [256 rows][32 k] bf16, 64 B per row, the
+// four 16-byte k-chunks of row r stored at chunk slot (c ^ swz(r)). A
+// fragment read (ds_read_b128) takes chunk q = lane/16 of rows r..r+15; the
+// LDS serves 16 lanes x 16 B per clock across 64 banks, and with 64-B rows
+// rows r and r+4 share banks: swz(r) = (r >> 2) & 3 gives the 16 lanes of
+// each quarter-wave 16 distinct 16-byte bank groups, so the reads are
+// conflict-free.
 // ---------------------------------------------------------------------------
-#ifndef LCE_SWZ_SHIFT
-#define LCE_SWZ_SHIFT 1
-#endif
-__device__ __forceinline__ int swz(int r) { return (r >> LCE_SWZ_SHIFT) & 7; }
-__device__ __forceinline__ int lds_off(int r, int c) { return r * 128 + ((c ^ swz(r)) << 4); }
+__device__ __forceinline__ int swz(int r) { return (r >> 2) & 3; }
+__device__ __forceinline__ int lds_off(int r, int c) { return r * 64 + ((c ^ swz(r)) << 4); }
 
-// Direct global->LDS fill of one operand stage. One global_load_lds_dwordx4
-// writes 64 x 16 B contiguously (lane i at +16 i), i.e. 8 tile rows; lane i
-// therefore fetches the logical chunk stored at slot (i & 7) of row (i >> 3)
-// of its 8-row block: c = (i & 7) ^ swz(row). Rows past the operand's end
-// are clamped to its last row (finite values the epilogues discard).
+// Direct global->LDS fills. One global_load_lds_dwordx4 writes 64 x 16 B
+// contiguously (lane i at +16 i), i.e. 16 tile rows of 64 B; lane i fetches
+// the logical chunk stored at slot (i & 3) of row (i >> 2) of its 16-row
+// block: c = (i & 3) ^ swz(row). A wave fills 64 rows of each operand per
+// stage (4 loads per operand). Rows past the operand's end are clamped to its
+// last row (finite values the epilogues discard).
 //
 // The per-lane byte offsets inside the tile are fixed for the whole K loop
 // (StageOffsets, computed once); each stage only moves a wave-uniform base,
 // so the loads use the scalar-base + 32-bit-offset addressing form.
+constexpr int FILLS = 4;                   // loads per wave per operand per stage
 struct StageOffsets {
-  uint32_t off[8];
+  uint32_t off[FILLS];
 };
 __device__ __forceinline__ StageOffsets stage_offsets(int64_t ld, int64_t row0, int64_t nrows, int wave,
                                                       int lane) {
   StageOffsets o;
-  const int r_in = lane >> 3;
 #pragma unroll
-  for (int b = 0; b < 8; ++b) {
-    const int r = wave * 64 + b * 8 + r_in;
-    const int c = (lane & 7) ^ swz(r);
+  for (int b = 0; b < FILLS; ++b) {
+    const int r = wave * 64 + b * 16 + (lane >> 2);
+    const int c = (lane & 3) ^ swz(r);
     int64_t lr = r;
     if (row0 + lr > nrows - 1) lr = nrows - 1 - row0;
     o.off[b] = (uint32_t)((lr * ld + c * 8) * 2);
@@ -131,26 +146,12 @@ __device__ __forceinline__ StageOffsets stage_offsets(int64_t ld, int64_t row0, 
 // land at LDS address lds_addr + 16 i (lds_addr in M0). Written as inline
 // assembly so the compiler does not treat the in-flight LDS writes as
 // possibly aliasing every later LDS read (it would wait for the loads to
-// complete before each read); the main loop orders them explicitly:
-// s_waitcnt vmcnt(0) and a barrier before any read of a refilled buffer.
+// complete before each read); the main loop orders them explicitly with
+// s_waitcnt vmcnt and a barrier before any read of a refilled buffer.
 // M0 is used for nothing else in these kernels.
 __device__ __forceinline__ void lds_dma16(const void* gbase, uint32_t voff, uint32_t lds_addr) {
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
                :: "s"(lds_addr), "v"(voff), "s"(gbase) : "memory", "m0");
-}
-
-// tile_base = operand + row0 * ld (elements); k0 in elements.
-__device__ __forceinline__ void stage_fill(const u16* __restrict__ tile_base, int64_t k0, const StageOffsets& o,
-                                           LDS_AS char* dst, int wave) {
-  // The base is wave-uniform; readfirstlane makes that visible to the
-  // compiler so it stays in the scalar registers the instruction needs.
-  const uint64_t b64 = (uint64_t)(uintptr_t)(tile_base + k0);
-  const uint64_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b64);
-  const uint64_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(b64 >> 32));
-  const void* base = (const void*)(uintptr_t)((hi << 32) | lo);
-  const uint32_t l0 = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)dst + (uint32_t)wave * 64 * 128);
-#pragma unroll
-  for (int b = 0; b < 8; ++b) lds_dma16(base, o.off[b], l0 + b * 1024);
 }
 
 __device__ __forceinline__ bf16x8 frag(const LDS_AS char* stage, int r, int c) {
@@ -171,10 +172,108 @@ __device__ __forceinline__ int acc_row(int wm, int i, int r, int lane) {
 }
 __device__ __forceinline__ int acc_col(int wn, int j, int lane) { return wn * 128 + j * 16 + (lane & 15); }
 
+// Operand tiles of one GEMM tile and where their stages go. The tile bases
+// are wave-uniform (scalar registers, set once); each load's address is the
+// base plus a 32-bit per-lane offset that advances by 64 bytes per stage.
+struct TileLoads {
+  const void* xbase;
+  const void* ybase;
+  StageOffsets ox, oy;
+  uint32_t lds_wave;     // LDS byte address of this wave's 64 rows in stage buffer 0
+};
+
+__device__ __forceinline__ const void* uniform_ptr(const void* p) {
+  const uint64_t b64 = (uint64_t)(uintptr_t)p;
+  const uint64_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b64);
+  const uint64_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(b64 >> 32));
+  return (const void*)(uintptr_t)((hi << 32) | lo);
+}
+
+// Issues load f (0..7) of stage s: f < 4 fill X rows, f >= 4 fill Y rows.
+__device__ __forceinline__ void stage_load(const TileLoads& t, int s, int f) {
+  const uint32_t buf = t.lds_wave + (uint32_t)((s & (NBUF - 1)) * STAGE);
+  const uint32_t koff = (uint32_t)s * (BK * 2);
+  if (f < FILLS)
+    lds_dma16(t.xbase, t.ox.off[f] + koff, buf + f * 1024);
+  else
+    lds_dma16(t.ybase, t.oy.off[f - FILLS] + koff, buf + OPERAND_STAGE + (f - FILLS) * 1024);
+}
+
+#define MFMA_IJ(i, j) acc.v[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[P][i], b[P][j], acc.v[i][j], 0, 0, 0)
+#define FENCE() __builtin_amdgcn_sched_barrier(0)
+
+// Workgroup barrier without the memory fence __syncthreads() adds (the fence
+// would drain every outstanding LDS read); the main loop orders its LDS
+// traffic itself with explicit s_waitcnt. The memory clobber keeps the
+// compiler from moving memory accesses across it.
+__device__ __forceinline__ void bare_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+// Fragment read number n (0..15) of the next stage: B blocks 0..7, then A
+// blocks 0..7, into the register set the next stage computes from.
+template <int P>
+__device__ __forceinline__ void next_frag(bf16x8 (&a)[2][NB], bf16x8 (&b)[2][NB], const LDS_AS char* nxt, int n,
+                                          int rA, int rB, int q) {
+  if (n < NB) b[P ^ 1][n] = frag(nxt + OPERAND_STAGE, rB + n * 16, q);
+  else a[P ^ 1][n - NB] = frag(nxt, rA + (n - NB) * 16, q);
+}
+
+// One K stage (32 deep) of the main loop, the stage's fragments in a[P],
+// b[P]. At entry: wait until stage kt+1 has landed (this wave's loads; stage
+// kt+2 may stay in flight) and this stage's fragments are in registers, then
+// a barrier makes stage kt+1 visible from every wave and frees buffer
+// (kt+3) % NBUF (last read two stages ago). With one wave per SIMD, every
+// instruction that is not an MFMA takes an issue slot the MFMA stream could
+// have used, so the other work is spread thinly over the 64 MFMAs: one
+// global->LDS load of stage kt+3 in each row block, and the 16 fragment reads
+// of stage kt+1 (double-buffered registers) three per block in blocks 0..3
+// and two in blocks 4 and 5, so the last of them lands under blocks 6 and 7.
+template <int P>
+__device__ __forceinline__ void mainloop_stage(Acc& acc, bf16x8 (&a)[2][NB], bf16x8 (&b)[2][NB], int kt, int nk,
+                                               LDS_AS char* smem, const TileLoads& t, int rA, int rB, int q) {
+  if (kt + 1 < nk) {
+    if (kt + 2 < nk) __builtin_amdgcn_s_waitcnt(WAIT_VM(2 * FILLS));
+    else __builtin_amdgcn_s_waitcnt(WAIT_VM0);
+  }
+  __builtin_amdgcn_s_waitcnt(WAIT_LGKM0);
+  bare_barrier();
+  // In the last stage these reads fetch stale (in-bounds) LDS that is never
+  // used; reading unconditionally keeps the body free of branches.
+  LDS_AS char* nxt = smem + ((kt + 1) & (NBUF - 1)) * STAGE;
+  const bool fill = kt + NBUF - 1 < nk;
+#pragma unroll
+  for (int i = 0; i < NB; ++i) {
+    const int r0 = i < 4 ? 3 * i : 12 + 2 * (i - 4);     // first fragment read of this block
+    FENCE();
+    MFMA_IJ(i, 0);
+    MFMA_IJ(i, 1);
+    FENCE();
+    if (fill) stage_load(t, kt + NBUF - 1, i);
+    FENCE();
+    MFMA_IJ(i, 2);
+    FENCE();
+    if (i < 6) next_frag<P>(a, b, nxt, r0, rA, rB, q);
+    FENCE();
+    MFMA_IJ(i, 3);
+    MFMA_IJ(i, 4);
+    FENCE();
+    if (i < 6) next_frag<P>(a, b, nxt, r0 + 1, rA, rB, q);
+    FENCE();
+    MFMA_IJ(i, 5);
+    MFMA_IJ(i, 6);
+    FENCE();
+    if (i < 4) next_frag<P>(a, b, nxt, r0 + 2, rA, rB, q);
+    FENCE();
+    MFMA_IJ(i, 7);
+  }
+  FENCE();
+}
+#undef MFMA_IJ
+
 // C tile (256 x 256, fp32 in registers) = X[x_row0 : +256][0:K] * Y[y_row0 : +256][0:K]^T.
-// K % 64 == 0 (BK/32 must be even). smem must hold MAINLOOP_LDS bytes. Every
-// LDS read of the stages precedes the final barrier, so smem may be reused
-// once the routine returns.
+// K % 64 == 0; 256 rows of either operand span < 4 GiB (row strides below
+// 2^22 elements). smem must hold MAINLOOP_LDS bytes. Every LDS access of the
+// stages (loads and reads) completes before the routine returns, but without
+// a final barrier: a caller that reuses smem must synchronise first.
 __device__ __forceinline__ void gemm_tile(Acc& acc, const u16* __restrict__ X, int64_t ldx, int64_t x_row0,
                                           int64_t x_rows, const u16* __restrict__ Y, int64_t ldy,
                                           int64_t y_row0, int64_t y_rows, int64_t K, LDS_AS char* smem) {
@@ -190,69 +289,33 @@ __device__ __forceinline__ void gemm_tile(Acc& acc, const u16* __restrict__ X, i
 
   const int nk = (int)(K / BK);
   const int rA = wm * 128 + (lane & 15), rB = wn * 128 + (lane & 15), q = lane >> 4;
-  const StageOffsets ox = stage_offsets(ldx, x_row0, x_rows, wave, lane);
-  const StageOffsets oy = stage_offsets(ldy, y_row0, y_rows, wave, lane);
-  const u16* xt = X + x_row0 * ldx;
-  const u16* yt = Y + y_row0 * ldy;
-  // Stages 0 and 1 go out before the loop; stage kt+2 is issued right after
-  // the barrier of iteration kt (the moment buffer kt&1 is no longer read),
-  // so each stage has two sub-steps of MFMA work to arrive.
-  stage_fill(xt, 0, ox, smem, wave);
-  stage_fill(yt, 0, oy, smem + OPERAND_STAGE, wave);
-  if (nk > 1) {
-    stage_fill(xt, BK, ox, smem + STAGE, wave);
-    stage_fill(yt, BK, oy, smem + STAGE + OPERAND_STAGE, wave);
-  }
-  __builtin_amdgcn_s_waitcnt(WAIT_VM0);
-  __syncthreads();
-  // Fragment pipeline (one wave per SIMD, so the wave hides its own LDS
-  // latency): the B fragments of the next 32-deep sub-step are read into a
-  // second register set before the current 64 MFMAs; the A fragment of row
-  // block i is re-read for the next sub-step right after the 8 MFMAs that
-  // last use it, leaving 56 MFMAs for it to land. The stage barrier sits in
-  // the last sub-step, before the reads that cross into the next stage.
-  // Scheduling fences keep the compiler from moving reads or MFMAs across.
-  bf16x8 a[NB], b[2][NB];
+  TileLoads t;
+  t.ox = stage_offsets(ldx, x_row0, x_rows, wave, lane);
+  t.oy = stage_offsets(ldy, y_row0, y_rows, wave, lane);
+  t.xbase = uniform_ptr(X + x_row0 * ldx);
+  t.ybase = uniform_ptr(Y + y_row0 * ldy);
+  t.lds_wave = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)smem + (uint32_t)wave * 64 * 64);
+  // Stages 0..NBUF-2 go out before the loop; stage kt+NBUF-1 is issued
+  // during stage kt, so every stage has one to two stages of MFMA work to
+  // arrive in.
+  const int pre = nk < NBUF - 1 ? nk : NBUF - 1;
+  for (int s = 0; s < pre; ++s)
 #pragma unroll
-  for (int i = 0; i < NB; ++i) a[i] = frag(smem, rA + i * 16, q);
+    for (int f = 0; f < 2 * FILLS; ++f) stage_load(t, s, f);
+  if (pre == 3) __builtin_amdgcn_s_waitcnt(WAIT_VM(2 * 2 * FILLS));
+  else if (pre == 2) __builtin_amdgcn_s_waitcnt(WAIT_VM(2 * FILLS));
+  else __builtin_amdgcn_s_waitcnt(WAIT_VM0);
+  __syncthreads();
+  bf16x8 a[2][NB], b[2][NB];
+#pragma unroll
+  for (int i = 0; i < NB; ++i) a[0][i] = frag(smem, rA + i * 16, q);
 #pragma unroll
   for (int j = 0; j < NB; ++j) b[0][j] = frag(smem + OPERAND_STAGE, rB + j * 16, q);
-  for (int kt = 0; kt < nk; ++kt) {
-    LDS_AS char* cur = smem + (kt & 1) * STAGE;
-    LDS_AS char* nxt = smem + ((kt + 1) & 1) * STAGE;
-#pragma unroll
-    for (int kk = 0; kk < BK / 32; ++kk) {
-      const int p = kk & 1;
-      const bool last = kk + 1 == BK / 32;
-      __builtin_amdgcn_s_waitcnt(WAIT_LGKM0);               // this sub-step's A and B landed
-      if (last) {
-        __builtin_amdgcn_s_waitcnt(WAIT_VM0);                 // stage kt+1 landed (this wave's part)
-        __syncthreads();                                      // ... and every wave's; `cur` fully read
-        if (kt + 2 < nk) {                                    // `cur` is free: refill it with stage kt+2
-          stage_fill(xt, (int64_t)(kt + 2) * BK, ox, cur, wave);
-          stage_fill(yt, (int64_t)(kt + 2) * BK, oy, cur + OPERAND_STAGE, wave);
-        }
-      }
-      // Source of the next sub-step's fragments: this stage, or the first
-      // sub-step of the next one. In the very last sub-step these reads
-      // fetch stale (but in-bounds) LDS that is never used; reading
-      // unconditionally keeps the loop free of branches.
-      LDS_AS char* src = last ? nxt : cur;
-      const int c = last ? q : (kk + 1) * 4 + q;
-#pragma unroll
-      for (int j = 0; j < NB; ++j) b[p ^ 1][j] = frag(src + OPERAND_STAGE, rB + j * 16, c);
-#pragma unroll
-      for (int i = 0; i < NB; ++i) {
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int j = 0; j < NB; ++j)
-          acc.v[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[p][j], acc.v[i][j], 0, 0, 0);
-        __builtin_amdgcn_sched_barrier(0);
-        a[i] = frag(src, rA + i * 16, c);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-    }
+  for (int kt = 0; kt < nk; kt += 2) {
+    mainloop_stage<0>(acc, a, b, kt, nk, smem, t, rA, rB, q);
+    mainloop_stage<1>(acc, a, b, kt + 1, nk, smem, t, rA, rB, q);
   }
+  __builtin_amdgcn_s_waitcnt(WAIT_LGKM0);
 }
 
 // ---------------------------------------------------------------------------
@@ -297,22 +360,19 @@ constexpr int STAGE_LDS = TILE * STAGE_LD * 2;        // 135168 B
 
 // Forward tile: z = h W^T + b for 256 rows x 256 vocabulary ids, reduced in
 // the epilogue to each row's (max, sum exp(z - max)) over each wave's
-// 128-column half of the tile (part index 2*tile + half), plus the label
-// logit for rows whose label falls in the tile. z never leaves registers.
-// With STORE_P (backward row groups) the tile also writes the bf16
+// 128-column half of the tile (part index 2*tile + half). z never leaves
+// registers. With STORE_P (backward row groups) the tile also writes the bf16
 // unnormalised softmax exp(z - max_half) into p [rows][Vp]; the dlogits pass
 // turns it into G once the row's lse is known, so the logits are computed
-// only once per call.
+// only once per call. Columns past V count as z = -inf (p = 0); a half tile
+// with no column below V stores max = -inf and sum = 0.
 template <bool STORE_P>
 __global__ void __launch_bounds__(NTHREADS, 1)
 k_fwd_tile(const u16* __restrict__ hidden, int64_t ldh, const u16* __restrict__ weight, int64_t ldw,
-           const u16* __restrict__ bias, const int32_t* __restrict__ label32, int64_t N, int64_t V,
-           int64_t Vp, int64_t H, int64_t g0, int64_t ld_part, int n_mt, int n_vt,
-           float* __restrict__ part_m, float* __restrict__ part_s, float* __restrict__ zlab,
-           u16* __restrict__ p_out) {
+           const u16* __restrict__ bias, int64_t N, int64_t V, int64_t Vp, int64_t H, int64_t g0, int64_t ld_part,
+           int n_mt, int n_vt, float* __restrict__ part_m, float* __restrict__ part_s, u16* __restrict__ p_out) {
   __shared__ __attribute__((aligned(16))) char smem_raw[STORE_P ? STAGE_LDS : MAINLOOP_LDS];
   __shared__ float s_bias[TILE];
-  __shared__ int s_lab[TILE];
   __shared__ float s_red_m[2][TILE];
   __shared__ float s_red_s[2][TILE];
   LDS_AS char* smem = (LDS_AS char*)smem_raw;
@@ -325,42 +385,36 @@ k_fwd_tile(const u16* __restrict__ hidden, int64_t ldh, const u16* __restrict__ 
   const int64_t col0 = (int64_t)tn * TILE;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int wm = wave >> 1, wn = wave & 1;
-  s_lab[tid] = label32[row0 + tid];
-  s_bias[tid] = (bias != nullptr && col0 + tid < V) ? bf2f(bias[col0 + tid]) : 0.f;
+  // bias, with -inf marking columns past V
+  s_bias[tid] = col0 + tid < V ? (bias != nullptr ? bf2f(bias[col0 + tid]) : 0.f) : -INFINITY;
 
   Acc acc;
   gemm_tile(acc, hidden, ldh, row0, N, weight, ldw, col0, V, H, smem);
-  if (STORE_P) __syncthreads();   // the staging tile overlays the mainloop's LDS
+  __syncthreads();   // s_bias visible; the staging tile overlays the mainloop's LDS
 
+  float cb[NB];
+#pragma unroll
+  for (int j = 0; j < NB; ++j) cb[j] = s_bias[acc_col(wn, j, lane)];
 #pragma unroll
   for (int i = 0; i < NB; ++i) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int rl = acc_row(wm, i, r, lane);
-      const int lab = s_lab[rl];
       float v[NB];
       float m = -INFINITY;
 #pragma unroll
       for (int j = 0; j < NB; ++j) {
-        const int cl = acc_col(wn, j, lane);
-        const bool ok = col0 + cl < V;
-        const float z = acc.v[i][j][r] + s_bias[cl];
-        v[j] = ok ? z : -INFINITY;
+        v[j] = acc.v[i][j][r] + cb[j];
         m = fmaxf(m, v[j]);
-        if (ok && (int64_t)lab == col0 + cl) zlab[row0 + rl] = z;
       }
       m = max16(m);
+      const float ms = m == -INFINITY ? 0.f : m;   // all columns past V: every e = 0
       float s = 0.f;
-      if (m != -INFINITY) {
 #pragma unroll
-        for (int j = 0; j < NB; ++j) {
-          const float e = exp_fast(v[j] - m);
-          s += e;
-          if (STORE_P) stage[rl * STAGE_LD + acc_col(wn, j, lane)] = f2bf(e);
-        }
-      } else if (STORE_P) {
-#pragma unroll
-        for (int j = 0; j < NB; ++j) stage[rl * STAGE_LD + acc_col(wn, j, lane)] = 0;
+      for (int j = 0; j < NB; ++j) {
+        const float e = exp_fast(v[j] - ms);
+        s += e;
+        if (STORE_P) stage[rl * STAGE_LD + acc_col(wn, j, lane)] = f2bf(e);
       }
       s = sum16(s);
       if ((lane & 15) == 0) {
@@ -385,6 +439,35 @@ k_fwd_tile(const u16* __restrict__ hidden, int64_t ldh, const u16* __restrict__ 
       *(u32x4*)(p_out + (lrow0 + row) * Vp + col0 + ch * 8) = val;
     }
   }
+}
+
+// Label logit z_{i,y_i} = h_i . W_{y_i} + b_{y_i} (FP32 accumulation of the
+// bf16 products) for every valid row; one wave per row, 16-byte loads.
+__global__ void __launch_bounds__(256) k_label_logit(const u16* __restrict__ hidden, int64_t ldh,
+                                                     const u16* __restrict__ weight, int64_t ldw,
+                                                     const u16* __restrict__ bias, const int32_t* __restrict__ label32,
+                                                     int64_t N, int64_t H, float* __restrict__ zlab) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= N) return;
+  const int lab = label32[row];
+  if (lab < 0) return;                     // wave-uniform
+  const u16* hr = hidden + row * ldh;
+  const u16* wr = weight + (int64_t)lab * ldw;
+  float acc = 0.f;
+  for (int64_t c = lane; c < H / 8; c += 64) {
+    const u32x4 hv = *(const u32x4*)(hr + c * 8);
+    const u32x4 wv = *(const u32x4*)(wr + c * 8);
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      acc += bf2f((u16)(hv[w] & 0xFFFF)) * bf2f((u16)(wv[w] & 0xFFFF));
+      acc += bf2f((u16)(hv[w] >> 16)) * bf2f((u16)(wv[w] >> 16));
+    }
+  }
+  acc = sum16(acc);
+  acc += __shfl_xor(acc, 16, 64);
+  acc += __shfl_xor(acc, 32, 64);
+  if (lane == 0) zlab[row] = acc + (bias != nullptr ? bf2f(bias[lab]) : 0.f);
 }
 
 // Per row i in [row_begin, row_end): merge the half-tile (max, sumexp)
@@ -640,6 +723,12 @@ k_gemm_grad_hidden(const u16* __restrict__ dlog, const u16* __restrict__ wT, int
 }
 
 // grad_weight FP32 accumulation for one group: gw[v][:] (+)= dlogT [Vp][G] * (h^T [H][G])^T.
+// The read-modify-write goes GW_RB 16-row blocks at a time with all their
+// reads issued before the adds and stores, so 32 * GW_RB reads per thread
+// are in flight together.
+#ifndef GW_RB
+#define GW_RB 2
+#endif
 __global__ void __launch_bounds__(NTHREADS, 1)
 k_gemm_grad_weight(const u16* __restrict__ dlogT, const u16* __restrict__ hT, int64_t G, int64_t H,
                    int64_t V, int64_t Vp, int n_mt, int n_nt, int first, float* __restrict__ gw_f32) {
@@ -653,20 +742,31 @@ k_gemm_grad_weight(const u16* __restrict__ dlogT, const u16* __restrict__ hT, in
   Acc acc;
   gemm_tile(acc, dlogT, G, row0, Vp, hT, G, col0, H, G, smem);
 #pragma unroll
-  for (int i = 0; i < NB; ++i)
+  for (int i0 = 0; i0 < NB; i0 += GW_RB) {
+    float old[GW_RB][4][NB];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int64_t v = row0 + acc_row(wm, i, r, lane);
-      if (v >= V) continue;
+    for (int di = 0; di < GW_RB; ++di)
 #pragma unroll
-      for (int j = 0; j < NB; ++j) {
-        const int64_t col = col0 + acc_col(wn, j, lane);
-        if (col < H) {
-          float* p = gw_f32 + v * H + col;
-          *p = first ? acc.v[i][j][r] : *p + acc.v[i][j][r];
+      for (int r = 0; r < 4; ++r) {
+        const int64_t v = row0 + acc_row(wm, i0 + di, r, lane);
+#pragma unroll
+        for (int j = 0; j < NB; ++j) {
+          const int64_t col = col0 + acc_col(wn, j, lane);
+          old[di][r][j] = (!first && v < V && col < H) ? gw_f32[v * H + col] : 0.f;
         }
       }
-    }
+#pragma unroll
+    for (int di = 0; di < GW_RB; ++di)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int64_t v = row0 + acc_row(wm, i0 + di, r, lane);
+#pragma unroll
+        for (int j = 0; j < NB; ++j) {
+          const int64_t col = col0 + acc_col(wn, j, lane);
+          if (v < V && col < H) gw_f32[v * H + col] = old[di][r][j] + acc.v[i0 + di][j][r];
+        }
+      }
+  }
 }
 
 __global__ void k_cast_bf16(const float* __restrict__ in, u16* __restrict__ out, int64_t n) {
@@ -699,19 +799,25 @@ hipError_t launch_prepare_labels(const int64_t* labels, int64_t N, int64_t Np, i
   return hipGetLastError();
 }
 
-hipError_t launch_fwd_tiles(const Shapes& s, const void* hidden, const void* weight, const void* bias,
-                            const int32_t* label32, int64_t g0, int64_t rows, float* part_m, float* part_s,
-                            float* zlab, void* p_out, hipStream_t st) {
+hipError_t launch_fwd_tiles(const Shapes& s, const void* hidden, const void* weight, const void* bias, int64_t g0,
+                            int64_t rows, float* part_m, float* part_s, void* p_out, hipStream_t st) {
   const int n_mt = (int)(rows / TILE), n_vt = (int)(s.Vp / TILE);
   const dim3 grid((unsigned)(n_mt * n_vt)), block(NTHREADS);
   if (p_out)
     hipLaunchKernelGGL(k_fwd_tile<true>, grid, block, 0, st, (const u16*)hidden, s.ldh, (const u16*)weight, s.ldw,
-                       (const u16*)bias, label32, s.N, s.V, s.Vp, s.H, g0, rows, n_mt, n_vt, part_m, part_s, zlab,
-                       (u16*)p_out);
+                       (const u16*)bias, s.N, s.V, s.Vp, s.H, g0, rows, n_mt, n_vt, part_m, part_s, (u16*)p_out);
   else
     hipLaunchKernelGGL(k_fwd_tile<false>, grid, block, 0, st, (const u16*)hidden, s.ldh, (const u16*)weight,
-                       s.ldw, (const u16*)bias, label32, s.N, s.V, s.Vp, s.H, g0, rows, n_mt, n_vt, part_m,
-                       part_s, zlab, (u16*)nullptr);
+                       s.ldw, (const u16*)bias, s.N, s.V, s.Vp, s.H, g0, rows, n_mt, n_vt, part_m, part_s,
+                       (u16*)nullptr);
+  return hipGetLastError();
+}
+
+hipError_t launch_label_logit(const Shapes& s, const void* hidden, const void* weight, const void* bias,
+                              const int32_t* label32, float* zlab, hipStream_t st) {
+  if (s.N <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_label_logit, dim3((unsigned)((s.N + 3) / 4)), dim3(256), 0, st, (const u16*)hidden, s.ldh,
+                     (const u16*)weight, s.ldw, (const u16*)bias, label32, s.N, s.H, zlab);
   return hipGetLastError();
 }
 

@@ -49,7 +49,8 @@ extern "C" {
 typedef enum {
   LCE_OK = 0,
   LCE_ERR_INVALID_ARG = 1,   /* bad sizes, strides, null required pointer, chunk_rows <= 0 */
-  LCE_ERR_UNSUPPORTED = 2,   /* dtype, H % 64 != 0, misaligned pointer/stride, NONE backward */
+  LCE_ERR_UNSUPPORTED = 2,   /* dtype, H % 64 != 0, misaligned pointer/stride, stride or V
+                                above 2^22, NONE backward */
   LCE_ERR_WORKSPACE = 3,     /* workspace null or smaller than lce_workspace_bytes() */
   LCE_ERR_HIP = 4,           /* a kernel launch failed */
   LCE_ERR_LABEL_RANGE = 5    /* device-side: a label outside [0,V) and != ignore_index */
@@ -74,14 +75,15 @@ typedef enum {
 typedef struct {
   int64_t n_rows;        /* N >= 0: flattened token rows */
   int64_t hidden;        /* H > 0, H % 64 == 0 */
-  int64_t vocab;         /* V > 0 */
-  int64_t ld_hidden;     /* row stride of hidden in elements, >= H, % 8 == 0 */
-  int64_t ld_weight;     /* row stride of weight in elements, >= H, % 8 == 0 */
+  int64_t vocab;         /* V > 0, V <= 2^22 */
+  int64_t ld_hidden;     /* row stride of hidden in elements, >= H, % 8 == 0, <= 2^22 */
+  int64_t ld_weight;     /* row stride of weight in elements, >= H, % 8 == 0, <= 2^22 */
   int64_t ignore_index;  /* label value that marks a row as ignored (pages: -100) */
   int64_t chunk_rows;    /* > 0: rows per loss chunk (chunk k = rows [k*c, min((k+1)c, N)));
                             LlamaFactory section 2 rejects <= 0, TRL's chunking uses 256 */
   int64_t rows_in_flight;/* backward row group: rows whose dlogits are alive at once;
-                            0 = library default (16384); rounded up to a multiple of 256 */
+                            0 = library default (16384); at most 2^20 (larger values
+                            are clamped); rounded up to a multiple of 256 */
   int32_t reduction;     /* lce_reduction */
   int32_t dtype;         /* lce_dtype; only LCE_DTYPE_BF16 */
 } lce_problem;
@@ -133,7 +135,7 @@ int lce_forward_backward(const lce_problem* p, const void* hidden, const void* w
 typedef enum {
   LCE_K_ZERO = 0, LCE_K_PREPARE_LABELS = 1, LCE_K_FWD_LSE = 2, LCE_K_FINALIZE_ROWS = 3,
   LCE_K_FINALIZE_LOSS = 4, LCE_K_TRANSPOSE = 5, LCE_K_BWD_DLOGITS = 6, LCE_K_GRAD_HIDDEN = 7,
-  LCE_K_GRAD_WEIGHT = 8, LCE_K_CAST = 9, LCE_K_COUNT = 10
+  LCE_K_GRAD_WEIGHT = 8, LCE_K_CAST = 9, LCE_K_LABEL_LOGIT = 10, LCE_K_COUNT = 11
 } lce_kernel_kind;
 
 typedef struct {

@@ -48,7 +48,7 @@ def test_exports_every_declared_function(lib):
 
 
 def test_version_and_strings(lib):
-    assert lib.lce_abi_version() == 100
+    assert lib.lce_abi_version() == 101
     for code in range(6):
         assert _lib.status_string(code) != "unknown status"
     assert _lib.status_string(99) == "unknown status"
@@ -95,13 +95,15 @@ def fwd(lib, p, hidden=FAKE, weight=FAKE, labels=FAKE, loss=FAKE, wsp=FAKE, wsb=
 @pytest.mark.parametrize("bad,code", [
     (dict(chunk_rows=0), 1), (dict(chunk_rows=-3), 1), (dict(ld_hidden=128), 1), (dict(ld_weight=8), 1),
     (dict(reduction=3), 1), (dict(dtype=1), 2), (dict(h=96, ld_hidden=96, ld_weight=96), 2),
-    (dict(ld_hidden=260), 2), (dict(rows_in_flight=-1), 1),
+    (dict(ld_hidden=260), 2), (dict(rows_in_flight=-1), 1), (dict(ld_hidden=(1 << 22) + 8), 2),
+    (dict(ld_weight=(1 << 22) + 8), 2), (dict(v=(1 << 22) + 1), 2),
 ])
 def test_forward_rejects_bad_problem(lib, bad, code):
     kw = dict(bad)
     n = kw.pop("n", 512)
     h = kw.pop("h", 256)
-    assert fwd(lib, prob(n, h, 4096, **kw)) == code
+    v = kw.pop("v", 4096)
+    assert fwd(lib, prob(n, h, v, **kw)) == code
 
 
 def test_forward_rejects_bad_pointers(lib):
