@@ -36,14 +36,15 @@ hipError_t launch_finalize_loss(const double* chunk_acc, int64_t T, const unsign
 hipError_t launch_transpose(const void* in, int64_t ld_in, int64_t r0, int64_t R_valid, int64_t C, void* out,
                             int64_t ld_out, int64_t R_pad, hipStream_t st);
 // dlogits of one row group from the stored exp(z - max_half) in dlog: G in
-// place (when write_dlog), G^T into dlogT [Vp][G] (when non-null), column
+// place (when write_dlog), G^T into dlogT [Vp][ld_t] (when non-null), column
 // sums into gb_f32 (when non-null).
 hipError_t launch_dlogits(const Shapes& s, const int32_t* label32, const float* part_m, const float* lse_ws,
                           const unsigned long long* n_valid, float grad_scale, int is_mean, int64_t g0, int64_t G,
-                          void* dlog, int write_dlog, void* dlogT, float* gb_f32, hipStream_t st);
+                          void* dlog, int write_dlog, void* dlogT, int64_t ld_t, float* gb_f32, hipStream_t st);
 hipError_t launch_grad_hidden(const Shapes& s, const void* dlog, const void* wT, int64_t g0, int64_t G,
                               void* grad_hidden, hipStream_t st);
-hipError_t launch_grad_weight(const Shapes& s, const void* dlogT, const void* hT, int64_t G, int first,
+// gw (+)= dlogT [Vp][ld] (first G columns) * (hT [H][ld])^T.
+hipError_t launch_grad_weight(const Shapes& s, const void* dlogT, const void* hT, int64_t G, int64_t ld, int first,
                               float* gw_f32, hipStream_t st);
 hipError_t launch_cast(const float* in, void* out, int64_t n, hipStream_t st);
 

@@ -594,7 +594,7 @@ __global__ void __launch_bounds__(256, 2)
 k_dlogits_from_p(u16* __restrict__ dlog, u16* __restrict__ dlogT, const float* __restrict__ part_m,
                  const int32_t* __restrict__ label32, const float* __restrict__ lse_ws,
                  const unsigned long long* __restrict__ n_valid, float grad_scale, int is_mean, int64_t V,
-                 int64_t Vp, int64_t g0, int64_t G, int write_dlog, float* __restrict__ gb_f32) {
+                 int64_t Vp, int64_t g0, int64_t G, int write_dlog, int64_t ld_t, float* __restrict__ gb_f32) {
   // transposed staging [256 cols][128 rows] bf16; the 16-byte row chunk c of
   // column col is stored at slot c ^ tswz(col): conflict-free for the column
   // writes (16 lanes, 16 different columns) and for the chunk reads.
@@ -690,7 +690,7 @@ k_dlogits_from_p(u16* __restrict__ dlog, u16* __restrict__ dlogT, const float* _
       const int id = it * 256 + tid;
       const int col = id >> 4, ch = id & 15;
       const u32x4 v = *(const LDS_AS u32x4*)((LDS_AS u16*)tst + col * DL_ROWS + ((ch ^ tswz(col)) << 3));
-      *(u32x4*)(dlogT + (col0 + col) * G + lrow0 + ch * 8) = v;
+      *(u32x4*)(dlogT + (col0 + col) * ld_t + lrow0 + ch * 8) = v;
     }
   }
 }
@@ -730,7 +730,7 @@ k_gemm_grad_hidden(const u16* __restrict__ dlog, const u16* __restrict__ wT, int
 #define GW_RB 2
 #endif
 __global__ void __launch_bounds__(NTHREADS, 1)
-k_gemm_grad_weight(const u16* __restrict__ dlogT, const u16* __restrict__ hT, int64_t G, int64_t H,
+k_gemm_grad_weight(const u16* __restrict__ dlogT, const u16* __restrict__ hT, int64_t G, int64_t ld, int64_t H,
                    int64_t V, int64_t Vp, int n_mt, int n_nt, int first, float* __restrict__ gw_f32) {
   __shared__ __attribute__((aligned(16))) char smem_raw[MAINLOOP_LDS];
   LDS_AS char* smem = (LDS_AS char*)smem_raw;
@@ -740,7 +740,7 @@ k_gemm_grad_weight(const u16* __restrict__ dlogT, const u16* __restrict__ hT, in
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int wm = wave >> 1, wn = wave & 1;
   Acc acc;
-  gemm_tile(acc, dlogT, G, row0, Vp, hT, G, col0, H, G, smem);
+  gemm_tile(acc, dlogT, ld, row0, Vp, hT, ld, col0, H, G, smem);
 #pragma unroll
   for (int i0 = 0; i0 < NB; i0 += GW_RB) {
     float old[GW_RB][4][NB];
@@ -849,10 +849,10 @@ hipError_t launch_transpose(const void* in, int64_t ld_in, int64_t r0, int64_t R
 
 hipError_t launch_dlogits(const Shapes& s, const int32_t* label32, const float* part_m, const float* lse_ws,
                           const unsigned long long* n_valid, float grad_scale, int is_mean, int64_t g0, int64_t G,
-                          void* dlog, int write_dlog, void* dlogT, float* gb_f32, hipStream_t st) {
+                          void* dlog, int write_dlog, void* dlogT, int64_t ld_t, float* gb_f32, hipStream_t st) {
   const int n_mt = (int)(G / DL_ROWS), n_vt = (int)(s.Vp / TILE);
   hipLaunchKernelGGL(k_dlogits_from_p, dim3((unsigned)(n_mt * n_vt)), dim3(256), 0, st, (u16*)dlog, (u16*)dlogT,
-                     part_m, label32, lse_ws, n_valid, grad_scale, is_mean, s.V, s.Vp, g0, G, write_dlog, gb_f32);
+                     part_m, label32, lse_ws, n_valid, grad_scale, is_mean, s.V, s.Vp, g0, G, write_dlog, ld_t, gb_f32);
   return hipGetLastError();
 }
 
@@ -864,11 +864,11 @@ hipError_t launch_grad_hidden(const Shapes& s, const void* dlog, const void* wT,
   return hipGetLastError();
 }
 
-hipError_t launch_grad_weight(const Shapes& s, const void* dlogT, const void* hT, int64_t G, int first,
+hipError_t launch_grad_weight(const Shapes& s, const void* dlogT, const void* hT, int64_t G, int64_t ld, int first,
                               float* gw_f32, hipStream_t st) {
   const int n_mt = (int)(s.Vp / TILE), n_nt = (int)((s.H + TILE - 1) / TILE);
   hipLaunchKernelGGL(k_gemm_grad_weight, dim3((unsigned)(n_mt * n_nt)), dim3(NTHREADS), 0, st,
-                     (const u16*)dlogT, (const u16*)hT, G, s.H, s.V, s.Vp, n_mt, n_nt, first, gw_f32);
+                     (const u16*)dlogT, (const u16*)hT, G, ld, s.H, s.V, s.Vp, n_mt, n_nt, first, gw_f32);
   return hipGetLastError();
 }
 
