@@ -34,13 +34,12 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int TILE = 256;                 // output tile edge (rows and columns)
-constexpr int BK = 32;                    // K depth of one LDS stage (one MFMA step)
-constexpr int NBUF = 4;                   // LDS stage buffers (up to 3 stages in flight)
+constexpr int BK = 64;                    // K depth of one LDS stage (two MFMA steps)
 constexpr int NTHREADS = 256;             // 4 waves, 2 x 2, each owns 128 x 128
 constexpr int NB = 8;                     // 16 x 16 MFMA blocks per wave edge (128 / 16)
-constexpr int OPERAND_STAGE = TILE * BK * 2;       // 16 KB: one operand, one stage
-constexpr int STAGE = 2 * OPERAND_STAGE;           // 32 KB: both operands
-constexpr int MAINLOOP_LDS = NBUF * STAGE;         // 128 KB
+constexpr int OPERAND_STAGE = TILE * BK * 2;       // 32 KB: one operand, one stage
+constexpr int STAGE = 2 * OPERAND_STAGE;           // 64 KB: both operands
+constexpr int MAINLOOP_LDS = 2 * STAGE;            // 128 KB: double buffered
 constexpr float LOG2E = 1.4426950408889634f;       // log2(e): exp(x) = 2^(x log2 e)
 // s_waitcnt immediates (gfx9 encoding: vmcnt [3:0]+[15:14], expcnt [6:4],
 // lgkmcnt [11:8]); the other counters are left at their maximum (no wait).
@@ -104,28 +103,28 @@ __device__ __forceinline__ void tile_coords(int n_m, int n_n, int& tm, int& tn) 
 }
 
 // ---------------------------------------------------------------------------
-// LDS stage layout: operand tile [256 rows][32 k] bf16, 64 B per row, the
-// four 16-byte k-chunks of row r stored at chunk slot (c ^ swz(r)). A
-// fragment read (ds_read_b128) takes chunk q = lane/16 of rows r..r+15; the
-// LDS serves 16 lanes x 16 B per clock across 64 banks, and with 64-B rows
-// rows r and r+4 share banks: swz(r) = (r >> 2) & 3 gives the 16 lanes of
-// each quarter-wave 16 distinct 16-byte bank groups, so the reads are
-// conflict-free.
+// LDS stage layout: operand tile [256 rows][64 k] bf16, 128 B per row (one
+// 128-byte line of the operand, so every line the loads touch is used
+// whole), the eight 16-byte k-chunks of row r stored at chunk slot
+// (c ^ swz(r)). A fragment read (ds_read_b128) takes chunk c of 16 rows; the
+// LDS serves 16 lanes x 16 B per clock across 64 banks and rows r and r+2
+// share banks: swz(r) = (r >> 1) & 7 gives the 16 lanes 16 distinct 16-byte
+// bank groups, so the reads are conflict-free.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ int swz(int r) { return (r >> 2) & 3; }
-__device__ __forceinline__ int lds_off(int r, int c) { return r * 64 + ((c ^ swz(r)) << 4); }
+__device__ __forceinline__ int swz(int r) { return (r >> 1) & 7; }
+__device__ __forceinline__ int lds_off(int r, int c) { return r * 128 + ((c ^ swz(r)) << 4); }
 
 // Direct global->LDS fills. One global_load_lds_dwordx4 writes 64 x 16 B
-// contiguously (lane i at +16 i), i.e. 16 tile rows of 64 B; lane i fetches
-// the logical chunk stored at slot (i & 3) of row (i >> 2) of its 16-row
-// block: c = (i & 3) ^ swz(row). A wave fills 64 rows of each operand per
-// stage (4 loads per operand). Rows past the operand's end are clamped to its
+// contiguously (lane i at +16 i), i.e. 8 tile rows of 128 B; lane i fetches
+// the logical chunk stored at slot (i & 7) of row (i >> 3) of its 8-row
+// block: c = (i & 7) ^ swz(row). A wave fills 64 rows of each operand per
+// stage (8 loads per operand). Rows past the operand's end are clamped to its
 // last row (finite values the epilogues discard).
 //
 // The per-lane byte offsets inside the tile are fixed for the whole K loop
-// (StageOffsets, computed once); each stage only moves a wave-uniform base,
-// so the loads use the scalar-base + 32-bit-offset addressing form.
-constexpr int FILLS = 4;                   // loads per wave per operand per stage
+// (StageOffsets, computed once); the tile base is wave-uniform (scalar
+// registers) and each stage only adds 128 bytes to the 32-bit offsets.
+constexpr int FILLS = 8;                   // loads per wave per operand per stage
 struct StageOffsets {
   uint32_t off[FILLS];
 };
@@ -134,8 +133,8 @@ __device__ __forceinline__ StageOffsets stage_offsets(int64_t ld, int64_t row0, 
   StageOffsets o;
 #pragma unroll
   for (int b = 0; b < FILLS; ++b) {
-    const int r = wave * 64 + b * 16 + (lane >> 2);
-    const int c = (lane & 3) ^ swz(r);
+    const int r = wave * 64 + b * 8 + (lane >> 3);
+    const int c = (lane & 7) ^ swz(r);
     int64_t lr = r;
     if (row0 + lr > nrows - 1) lr = nrows - 1 - row0;
     o.off[b] = (uint32_t)((lr * ld + c * 8) * 2);
@@ -172,9 +171,7 @@ __device__ __forceinline__ int acc_row(int wm, int i, int r, int lane) {
 }
 __device__ __forceinline__ int acc_col(int wn, int j, int lane) { return wn * 128 + j * 16 + (lane & 15); }
 
-// Operand tiles of one GEMM tile and where their stages go. The tile bases
-// are wave-uniform (scalar registers, set once); each load's address is the
-// base plus a 32-bit per-lane offset that advances by 64 bytes per stage.
+// Operand tiles of one GEMM tile and where their stages go.
 struct TileLoads {
   const void* xbase;
   const void* ybase;
@@ -189,9 +186,9 @@ __device__ __forceinline__ const void* uniform_ptr(const void* p) {
   return (const void*)(uintptr_t)((hi << 32) | lo);
 }
 
-// Issues load f (0..7) of stage s: f < 4 fill X rows, f >= 4 fill Y rows.
+// Issues load f (0..15) of stage s: f < 8 fill X rows, f >= 8 fill Y rows.
 __device__ __forceinline__ void stage_load(const TileLoads& t, int s, int f) {
-  const uint32_t buf = t.lds_wave + (uint32_t)((s & (NBUF - 1)) * STAGE);
+  const uint32_t buf = t.lds_wave + (uint32_t)((s & 1) * STAGE);
   const uint32_t koff = (uint32_t)s * (BK * 2);
   if (f < FILLS)
     lds_dma16(t.xbase, t.ox.off[f] + koff, buf + f * 1024);
@@ -199,7 +196,6 @@ __device__ __forceinline__ void stage_load(const TileLoads& t, int s, int f) {
     lds_dma16(t.ybase, t.oy.off[f - FILLS] + koff, buf + OPERAND_STAGE + (f - FILLS) * 1024);
 }
 
-#define MFMA_IJ(i, j) acc.v[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[P][i], b[P][j], acc.v[i][j], 0, 0, 0)
 #define FENCE() __builtin_amdgcn_sched_barrier(0)
 
 // Workgroup barrier without the memory fence __syncthreads() adds (the fence
@@ -208,66 +204,80 @@ __device__ __forceinline__ void stage_load(const TileLoads& t, int s, int f) {
 // compiler from moving memory accesses across it.
 __device__ __forceinline__ void bare_barrier() { asm volatile("s_barrier" ::: "memory"); }
 
-// Fragment read number n (0..15) of the next stage: B blocks 0..7, then A
-// blocks 0..7, into the register set the next stage computes from.
-template <int P>
-__device__ __forceinline__ void next_frag(bf16x8 (&a)[2][NB], bf16x8 (&b)[2][NB], const LDS_AS char* nxt, int n,
-                                          int rA, int rB, int q) {
-  if (n < NB) b[P ^ 1][n] = frag(nxt + OPERAND_STAGE, rB + n * 16, q);
-  else a[P ^ 1][n - NB] = frag(nxt, rA + (n - NB) * 16, q);
+// Fragments of one 32-deep sub-step: A row blocks 0..7, B column blocks 0..7.
+struct Frags {
+  bf16x8 a[NB], b[NB];
+};
+// Fragment read n (0..15) of sub-step `sub` (0, 1) of the stage in `buf`: B
+// blocks first (every MFMA of the first row block needs all of them), then A.
+__device__ __forceinline__ void read_frag(Frags& f, const LDS_AS char* buf, int sub, int n, int rA, int rB, int q) {
+  if (n < NB) f.b[n] = frag(buf + OPERAND_STAGE, rB + n * 16, sub * 4 + q);
+  else f.a[n - NB] = frag(buf, rA + (n - NB) * 16, sub * 4 + q);
 }
 
-// One K stage (32 deep) of the main loop, the stage's fragments in a[P],
-// b[P]. At entry: wait until stage kt+1 has landed (this wave's loads; stage
-// kt+2 may stay in flight) and this stage's fragments are in registers, then
-// a barrier makes stage kt+1 visible from every wave and frees buffer
-// (kt+3) % NBUF (last read two stages ago). With one wave per SIMD, every
-// instruction that is not an MFMA takes an issue slot the MFMA stream could
-// have used, so the other work is spread thinly over the 64 MFMAs: one
-// global->LDS load of stage kt+3 in each row block, and the 16 fragment reads
-// of stage kt+1 (double-buffered registers) three per block in blocks 0..3
-// and two in blocks 4 and 5, so the last of them lands under blocks 6 and 7.
-template <int P>
-__device__ __forceinline__ void mainloop_stage(Acc& acc, bf16x8 (&a)[2][NB], bf16x8 (&b)[2][NB], int kt, int nk,
-                                               LDS_AS char* smem, const TileLoads& t, int rA, int rB, int q) {
-  if (kt + 1 < nk) {
-    if (kt + 2 < nk) __builtin_amdgcn_s_waitcnt(WAIT_VM(2 * FILLS));
-    else __builtin_amdgcn_s_waitcnt(WAIT_VM0);
-  }
-  __builtin_amdgcn_s_waitcnt(WAIT_LGKM0);
-  bare_barrier();
-  // In the last stage these reads fetch stale (in-bounds) LDS that is never
-  // used; reading unconditionally keeps the body free of branches.
-  LDS_AS char* nxt = smem + ((kt + 1) & (NBUF - 1)) * STAGE;
-  const bool fill = kt + NBUF - 1 < nk;
+// Schedule of one 64-deep stage s, in 16 slots of 8 MFMAs (slots 0..7:
+// sub-step 0 from fragment set f0, slots 8..15: sub-step 1 from f1):
+//   slots 0..7    read f1 (stage s, sub-step 1), two fragments per slot
+//   slot 10       wait for this wave's loads of stage s+1 and its LDS reads,
+//                 barrier: stage s+1 is visible from every wave, and buffer
+//                 s&1 is no longer read (f0 and f1 of stage s are in registers)
+//   slots 10..14  read f0 of stage s+1 (3-4 fragments per slot)
+//   slots 10..15, and 0..2 of stage s+1: the 16 global->LDS loads of stage s+2
+//                 into buffer s&1 (two per slot in 10..14 and 0..2, none in 15)
+// so every load has at least seven slots to land before the barrier that
+// publishes it, and no instruction burst stalls the wave's MFMA issue.
+// At entry: f0 holds stage s sub-step 0; loads 0..9 of stage s+1 went out in
+// the previous stage (slots 10..14), loads 10..15 go out in slots 0..2 here.
+__device__ __forceinline__ void mainloop_stage(Acc& acc, Frags& f0, Frags& f1, int s, int nk, LDS_AS char* smem,
+                                               const TileLoads& t, int rA, int rB, int q) {
+  LDS_AS char* cur = smem + (s & 1) * STAGE;
+  LDS_AS char* nxt = smem + ((s + 1) & 1) * STAGE;
 #pragma unroll
-  for (int i = 0; i < NB; ++i) {
-    const int r0 = i < 4 ? 3 * i : 12 + 2 * (i - 4);     // first fragment read of this block
+  for (int slot = 0; slot < 16; ++slot) {
+    const int i = slot & 7;
+    Frags& f = slot < 8 ? f0 : f1;
+    if (slot == 10) {
+      if (s + 1 < nk) __builtin_amdgcn_s_waitcnt(WAIT_VM0);
+      __builtin_amdgcn_s_waitcnt(WAIT_LGKM0);
+      bare_barrier();
+    }
     FENCE();
-    MFMA_IJ(i, 0);
-    MFMA_IJ(i, 1);
+#pragma unroll
+    for (int j = 0; j < 3; ++j)
+      acc.v[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.a[i], f.b[j], acc.v[i][j], 0, 0, 0);
     FENCE();
-    if (fill) stage_load(t, kt + NBUF - 1, i);
+    // global->LDS loads: stage s+1's last six in slots 0..2, stage s+2's first ten in slots 10..14
+    if (slot < 3) {
+      if (s + 1 < nk) stage_load(t, s + 1, 10 + 2 * slot);
+    } else if (slot >= 10 && slot < 15) {
+      if (s + 2 < nk) stage_load(t, s + 2, 2 * (slot - 10));
+    }
     FENCE();
-    MFMA_IJ(i, 2);
+#pragma unroll
+    for (int j = 3; j < 6; ++j)
+      acc.v[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.a[i], f.b[j], acc.v[i][j], 0, 0, 0);
     FENCE();
-    if (i < 6) next_frag<P>(a, b, nxt, r0, rA, rB, q);
+    if (slot < 3) {
+      if (s + 1 < nk) stage_load(t, s + 1, 11 + 2 * slot);
+    } else if (slot >= 10 && slot < 15) {
+      if (s + 2 < nk) stage_load(t, s + 2, 2 * (slot - 10) + 1);
+    }
+    // fragment reads: f1 of this stage in slots 0..7, f0 of the next in 10..14
+    if (slot < 8) read_frag(f1, cur, 1, 2 * slot, rA, rB, q);
+    else if (slot >= 10 && slot < 15) {
+      const int n0 = (slot - 10) * 16 / 5, n1 = (slot - 9) * 16 / 5;
+#pragma unroll
+      for (int n = n0; n < n1; ++n) read_frag(f0, nxt, 0, n, rA, rB, q);
+    }
     FENCE();
-    MFMA_IJ(i, 3);
-    MFMA_IJ(i, 4);
+#pragma unroll
+    for (int j = 6; j < NB; ++j)
+      acc.v[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.a[i], f.b[j], acc.v[i][j], 0, 0, 0);
     FENCE();
-    if (i < 6) next_frag<P>(a, b, nxt, r0 + 1, rA, rB, q);
-    FENCE();
-    MFMA_IJ(i, 5);
-    MFMA_IJ(i, 6);
-    FENCE();
-    if (i < 4) next_frag<P>(a, b, nxt, r0 + 2, rA, rB, q);
-    FENCE();
-    MFMA_IJ(i, 7);
+    if (slot < 8) read_frag(f1, cur, 1, 2 * slot + 1, rA, rB, q);
   }
   FENCE();
 }
-#undef MFMA_IJ
 
 // C tile (256 x 256, fp32 in registers) = X[x_row0 : +256][0:K] * Y[y_row0 : +256][0:K]^T.
 // K % 64 == 0; 256 rows of either operand span < 4 GiB (row strides below
@@ -294,27 +304,21 @@ __device__ __forceinline__ void gemm_tile(Acc& acc, const u16* __restrict__ X, i
   t.oy = stage_offsets(ldy, y_row0, y_rows, wave, lane);
   t.xbase = uniform_ptr(X + x_row0 * ldx);
   t.ybase = uniform_ptr(Y + y_row0 * ldy);
-  t.lds_wave = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)smem + (uint32_t)wave * 64 * 64);
-  // Stages 0..NBUF-2 go out before the loop; stage kt+NBUF-1 is issued
-  // during stage kt, so every stage has one to two stages of MFMA work to
-  // arrive in.
-  const int pre = nk < NBUF - 1 ? nk : NBUF - 1;
-  for (int s = 0; s < pre; ++s)
+  t.lds_wave = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)smem + (uint32_t)wave * 64 * 128);
+  // Prologue: stage 0 whole, then the first ten loads of stage 1 (the rest
+  // go out in slots 0..2 of stage 0); f0 of stage 0 once stage 0 is visible.
 #pragma unroll
-    for (int f = 0; f < 2 * FILLS; ++f) stage_load(t, s, f);
-  if (pre == 3) __builtin_amdgcn_s_waitcnt(WAIT_VM(2 * 2 * FILLS));
-  else if (pre == 2) __builtin_amdgcn_s_waitcnt(WAIT_VM(2 * FILLS));
+  for (int f = 0; f < 2 * FILLS; ++f) stage_load(t, 0, f);
+  if (nk > 1)
+#pragma unroll
+    for (int f = 0; f < 10; ++f) stage_load(t, 1, f);
+  if (nk > 1) __builtin_amdgcn_s_waitcnt(WAIT_VM(10));
   else __builtin_amdgcn_s_waitcnt(WAIT_VM0);
   __syncthreads();
-  bf16x8 a[2][NB], b[2][NB];
+  Frags f0, f1;
 #pragma unroll
-  for (int i = 0; i < NB; ++i) a[0][i] = frag(smem, rA + i * 16, q);
-#pragma unroll
-  for (int j = 0; j < NB; ++j) b[0][j] = frag(smem + OPERAND_STAGE, rB + j * 16, q);
-  for (int kt = 0; kt < nk; kt += 2) {
-    mainloop_stage<0>(acc, a, b, kt, nk, smem, t, rA, rB, q);
-    mainloop_stage<1>(acc, a, b, kt + 1, nk, smem, t, rA, rB, q);
-  }
+  for (int n = 0; n < 2 * NB; ++n) read_frag(f0, smem, 0, n, rA, rB, q);
+  for (int s = 0; s < nk; ++s) mainloop_stage(acc, f0, f1, s, nk, smem, t, rA, rB, q);
   __builtin_amdgcn_s_waitcnt(WAIT_LGKM0);
 }
 
