@@ -89,6 +89,33 @@ def make_traces(lib_mod, events: HipEvents, steps: int, cap: int):
     return traces
 
 
+def step_times(events: HipEvents, traces, cap: int) -> list:
+    """Per-step device time: first launch's start event to the last launch's end event."""
+    out = []
+    for t, _, _, s in traces:
+        if t.count > 0:
+            out.append(events.elapsed_ms(2 * cap * s, 2 * cap * s + 2 * (t.count - 1) + 1))
+    return out
+
+
+def matmul_roof(torch, dev, H: int, V: int, rows: int = 16384, reps: int = 5) -> dict:
+    """torch.matmul (the vendor bf16 GEMM) on the forward logits shape of one row group."""
+    a = torch.randn(rows, H, device=dev).to(torch.bfloat16)
+    b = torch.randn(H, V, device=dev).to(torch.bfloat16)      # contiguous right operand
+    c = torch.matmul(a, b)
+    torch.cuda.synchronize()
+    s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s0.record()
+    for _ in range(reps):
+        torch.matmul(a, b, out=c)
+    s1.record()
+    torch.cuda.synchronize()
+    ms = s0.elapsed_time(s1) / reps
+    del a, b, c
+    return {"shape": [rows, H, V], "ms": ms, "tflops": 2.0 * rows * H * V / (ms * 1e-3) / 1e12,
+            "what": "torch.matmul bf16, [rows,H] x [H,V], same shape as one row group's logits product"}
+
+
 def summarize_traces(lib_mod, events: HipEvents, traces, cap: int) -> dict:
     per = {}
     for t, kinds, dims, s in traces:
@@ -167,6 +194,8 @@ def main() -> int:
     ap.add_argument("--fwd-steps", type=int, default=3)
     ap.add_argument("--cpu-rows", type=int, default=4096)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-matmul-roof", action="store_true",
+                    help="skip timing torch.matmul on the logits shape (context for the roofline)")
     ap.add_argument("--copy-gib", type=float, default=0.0,
                     help="also run one plain device-to-device copy of this many GiB (a kernel of known "
                          "traffic, used to calibrate the FETCH_SIZE / WRITE_SIZE counters)")
@@ -233,6 +262,7 @@ def main() -> int:
     out.check()
     log(f"[bench] timed {args.steps} steps: {ms_step:.2f} ms/step (wall {wall:.2f}s)")
     kernels = summarize_traces(_lib, events, traces, cap)
+    per_step = sorted(step_times(events, traces, cap))
     peak_extra = torch.cuda.max_memory_allocated(dev) - base_bytes - out_bytes
 
     # forward only
@@ -250,6 +280,10 @@ def main() -> int:
         torch.cuda.synchronize()
         ms_fwd = s2.elapsed_time(e2) / args.fwd_steps
     events.close()
+    roof = None
+    if not args.no_matmul_roof:
+        roof = matmul_roof(torch, dev, w.hidden, w.vocab)
+        log(f"[bench] torch.matmul on the logits shape: {roof['tflops']:.0f} TFLOP/s")
     if args.copy_gib > 0:
         nbytes = int(args.copy_gib * (1 << 30))
         src = torch.empty(nbytes, dtype=torch.uint8, device=dev)
@@ -288,6 +322,9 @@ def main() -> int:
                    "ignored_rows": w.n_ignored, "chunk_rows": w.chunk_rows, "reduction": w.reduction,
                    "rows_in_flight": rif or 16384, "parallelism": "single GPU"},
         "pct_peak_bf16": pct,
+        "step_ms_min": per_step[0] if per_step else None,
+        "step_ms_median": per_step[len(per_step) // 2] if per_step else None,
+        "vendor_gemm_same_shape": roof,
         "fwd_tokens_per_s": N / (ms_fwd * 1e-3) if ms_fwd else None, "fwd_ms": ms_fwd,
         "fwd_pct_peak_bf16": pct_fwd,
         "peak_extra_hbm_gb": peak_extra / 1e9, "full_logits_fp32_gb": 4.0 * N * V / 1e9,

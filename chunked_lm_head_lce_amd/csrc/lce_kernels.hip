@@ -478,9 +478,10 @@ __global__ void __launch_bounds__(256) k_label_logit(const u16* __restrict__ hid
 // partials into lse, form l_i, write lse (and l_i for reduction NONE), and
 // add l_i into its chunk's float64 sum. Partials of row i sit at
 // part[k * ld_part + (i - part_row0)], k < n_part. Rows in [N, row_end) only
-// get lse_ws = 0. A block takes 64 rows; its 4 waves each merge every 4th
+// get lse_ws = 0. A block takes 64 rows; its 16 waves each merge every 16th
 // partial of those rows (256-byte coalesced reads), then combine in LDS.
 constexpr int FIN_ROWS = 64;
+constexpr int FIN_WAVES = 16;
 
 __device__ __forceinline__ void merge_ms(float& M, float& S, float mk, float sk) {
   if (mk == -INFINITY) return;
@@ -489,13 +490,13 @@ __device__ __forceinline__ void merge_ms(float& M, float& S, float mk, float sk)
   M = mn;
 }
 
-__global__ void __launch_bounds__(256) k_finalize_rows(
+__global__ void __launch_bounds__(64 * FIN_WAVES) k_finalize_rows(
     const float* __restrict__ part_m, const float* __restrict__ part_s, int64_t ld_part, int64_t part_row0,
     int n_part, const float* __restrict__ zlab, const int32_t* __restrict__ label32, int64_t N,
     int64_t row_begin, int64_t row_end, int64_t chunk_rows, const int32_t* __restrict__ status, int reduction,
     float* __restrict__ lse_ws, float* __restrict__ lse_out, float* __restrict__ rowloss_out,
     double* __restrict__ chunk_acc) {
-  __shared__ float s_m[4][FIN_ROWS], s_s[4][FIN_ROWS];
+  __shared__ float s_m[FIN_WAVES][FIN_ROWS], s_s[FIN_WAVES][FIN_ROWS];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t i = row_begin + (int64_t)blockIdx.x * FIN_ROWS + lane;
   const bool live = i < row_end && i < N;
@@ -503,7 +504,7 @@ __global__ void __launch_bounds__(256) k_finalize_rows(
   if (live) {
     const int64_t pi = i - part_row0;
 #pragma unroll 8
-    for (int k = wave; k < n_part; k += 4)
+    for (int k = wave; k < n_part; k += FIN_WAVES)
       merge_ms(M, S, part_m[(int64_t)k * ld_part + pi], part_s[(int64_t)k * ld_part + pi]);
   }
   s_m[wave][lane] = M;
@@ -514,7 +515,7 @@ __global__ void __launch_bounds__(256) k_finalize_rows(
     lse_ws[i] = 0.f;
     return;
   }
-  for (int w = 1; w < 4; ++w) merge_ms(M, S, s_m[w][lane], s_s[w][lane]);
+  for (int w = 1; w < FIN_WAVES; ++w) merge_ms(M, S, s_m[w][lane], s_s[w][lane]);
   const float lse = M + logf(S);
   const int lab = label32[i];
   const float l = lab >= 0 ? lse - zlab[i] : 0.f;
@@ -553,32 +554,51 @@ __global__ void __launch_bounds__(256) k_finalize_loss(const double* __restrict_
   }
 }
 
-// out[c][r_out] = in[r0 + r_out][c] for r_out < R_valid (else 0), c < C, r_out < R_pad.
+// out[c][r_out] = in[r0 + r_out][c] for r_out < R_valid (else 0), c < C,
+// r_out < R_pad (C % 8 == 0, R_pad % 128 == 0, 16-byte aligned rows). One
+// block moves a 128 x 128 tile: each thread loads 8 rows of one 16-byte
+// column chunk (a quarter-wave reads 256 contiguous bytes of a row),
+// transposes the 8 x 8 block in registers, and stages it through LDS as
+// [column][row chunk] with the chunk slot XOR-swizzled by the column chunk
+// (16 writing lanes, 16 distinct slots), so the
+// output rows leave as 256-byte coalesced 16-byte stores.
+constexpr int TT = 128;
 __global__ void __launch_bounds__(256) k_transpose(const u16* __restrict__ in, int64_t ld_in, int64_t r0,
                                                    int64_t R_valid, int64_t C, u16* __restrict__ out,
                                                    int64_t ld_out, int64_t R_pad) {
-  __shared__ u16 t[64][66];
-  const int64_t cb = (int64_t)blockIdx.x * 64, rb = (int64_t)blockIdx.y * 64;
+  __shared__ __attribute__((aligned(16))) u16 t[TT * TT];
+  const int64_t cb = (int64_t)blockIdx.x * TT, rb = (int64_t)blockIdx.y * TT;
   const int tid = threadIdx.x;
-  {
-    const int rr = tid >> 2, cc = (tid & 3) * 16;
-    const int64_t r = rb + rr;
+  const int cc = tid & 15, rk = tid >> 4;   // column chunk (8 columns), row block (8 rows)
+  const int64_t c0 = cb + cc * 8;
+  u32x4 v[8];
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const int64_t c = cb + cc + e;
-      t[rr][cc + e] = (r < R_valid && c < C) ? in[(r0 + r) * ld_in + c] : (u16)0;
+  for (int r = 0; r < 8; ++r) {
+    const int64_t row = rb + rk * 8 + r;
+    v[r] = (row < R_valid && c0 < C) ? *(const u32x4*)(in + (r0 + row) * ld_in + c0) : (u32x4){0, 0, 0, 0};
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int col = cc * 8 + e;
+    u32x4 o;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const uint32_t lo = (v[2 * w][e >> 1] >> ((e & 1) * 16)) & 0xFFFF;
+      const uint32_t hi = (v[2 * w + 1][e >> 1] >> ((e & 1) * 16)) & 0xFFFF;
+      o[w] = lo | (hi << 16);
     }
+    *(LDS_AS u32x4*)((LDS_AS u16*)t + col * TT + ((rk ^ ((col >> 3) & 15)) << 3)) = o;
   }
   __syncthreads();
-  {
-    const int co = tid >> 2, ro = (tid & 3) * 16;
-    const int64_t c = cb + co;
-    if (c < C) {
+  // 128 output rows (columns of `in`) x 16 sixteen-byte chunks; 16 lanes per row.
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int64_t r = rb + ro + e;
-        if (r < R_pad) out[c * ld_out + r] = t[ro + e][co];
-      }
+  for (int it = 0; it < TT * TT / 8 / 256; ++it) {
+    const int id = it * 256 + tid;
+    const int col = id >> 4, ch = id & 15;
+    const int64_t c = cb + col, r = rb + ch * 8;
+    if (c < C && r < R_pad) {
+      const u32x4 val = *(const LDS_AS u32x4*)((LDS_AS u16*)t + col * TT + ((ch ^ ((col >> 3) & 15)) << 3));
+      *(u32x4*)(out + c * ld_out + r) = val;
     }
   }
 }
@@ -829,7 +849,7 @@ hipError_t launch_finalize_rows(const Shapes& s, const float* part_m, const floa
                                 int64_t rows, const float* zlab, const int32_t* label32, const int32_t* status,
                                 int reduction, float* lse_ws, float* lse_out, float* rowloss_out,
                                 double* chunk_acc, hipStream_t st) {
-  hipLaunchKernelGGL(k_finalize_rows, dim3((unsigned)(rows / FIN_ROWS)), dim3(256), 0, st, part_m, part_s, rows, g0,
+  hipLaunchKernelGGL(k_finalize_rows, dim3((unsigned)(rows / FIN_ROWS)), dim3(64 * FIN_WAVES), 0, st, part_m, part_s, rows, g0,
                      (int)(2 * (s.Vp / TILE)), zlab, label32, s.N, g0, g0 + rows, s.chunk_rows, status, reduction,
                      lse_ws, lse_out, rowloss_out, chunk_acc);
   return hipGetLastError();
@@ -845,7 +865,7 @@ hipError_t launch_finalize_loss(const double* chunk_acc, int64_t T, const unsign
 
 hipError_t launch_transpose(const void* in, int64_t ld_in, int64_t r0, int64_t R_valid, int64_t C, void* out,
                             int64_t ld_out, int64_t R_pad, hipStream_t st) {
-  dim3 grid((unsigned)((C + 63) / 64), (unsigned)((R_pad + 63) / 64));
+  dim3 grid((unsigned)((C + TT - 1) / TT), (unsigned)((R_pad + TT - 1) / TT));
   hipLaunchKernelGGL(k_transpose, grid, dim3(256), 0, st, (const u16*)in, ld_in, r0, R_valid, C, (u16*)out,
                      ld_out, R_pad);
   return hipGetLastError();
