@@ -7,6 +7,8 @@ runs in the library's HIP kernels; there is no fallback implementation.
 
     lce_forward(hidden, weight, bias, labels, ...)          -> LceOutput
     lce_forward_backward(hidden, weight, bias, labels, ...) -> LceOutput with grads
+    lce_scale(tensor, scale)                                -> tensor *= scale (in a library kernel)
+    linear_cross_entropy(hidden, weight, labels, bias=...)  -> loss with autograd (torch.autograd.Function)
 
 ``chunk_rows`` follows the pages' ``chunk_loss_size`` (LlamaFactory section 2):
 positive, ``None`` meaning one chunk of all rows, anything else a ValueError.
@@ -24,8 +26,8 @@ from ._lib import LceProblem
 IGNORE_INDEX = -100
 DEFAULT_CHUNK_ROWS = 256
 
-__all__ = ["lce_forward", "lce_forward_backward", "lce_workspace_bytes", "LceOutput", "LceError",
-           "IGNORE_INDEX", "DEFAULT_CHUNK_ROWS"]
+__all__ = ["lce_forward", "lce_forward_backward", "lce_workspace_bytes", "lce_scale", "linear_cross_entropy",
+           "LinearCrossEntropyFunction", "LceOutput", "LceError", "IGNORE_INDEX", "DEFAULT_CHUNK_ROWS"]
 
 
 class LceError(RuntimeError):
@@ -157,11 +159,17 @@ def lce_forward_backward(hidden: torch.Tensor, weight: torch.Tensor, bias: torch
                          want_grad_hidden: bool = True, want_grad_weight: bool = True,
                          want_grad_bias: bool | None = None, want_f32: bool = False, want_lse: bool = True,
                          want_chunk_loss: bool = False, rows_in_flight: int | None = None,
+                         row_scale: torch.Tensor | None = None, accumulate: bool = False,
                          workspace: torch.Tensor | None = None, out: LceOutput | None = None,
                          trace: "_lib.LceTrace | None" = None) -> LceOutput:
     """Loss and gradients in one call. grad_weight / grad_bias are accumulated
     in FP32 and cast to bf16 at the end; ``want_f32`` also returns the FP32
-    accumulators (and makes the call use them instead of workspace)."""
+    accumulators (and makes the call use them instead of workspace).
+
+    ``row_scale`` ([N] float32 on the GPU) multiplies row i's dlogits, e.g. the
+    per-token upstream gradient; ``reduction="none"`` requires it.
+    ``accumulate=True`` adds into ``out.grad_weight_f32`` / ``out.grad_bias_f32``
+    instead of overwriting them (fresh zeroed FP32 buffers when ``out`` is None)."""
     lib = _lib.load()
     _device_checks(hidden, weight, bias, labels)
     if want_grad_bias is None:
@@ -178,24 +186,118 @@ def lce_forward_backward(hidden: torch.Tensor, weight: torch.Tensor, bias: torch
             out.grad_hidden = torch.empty((n, h), dtype=torch.bfloat16, device=dev)
         if want_grad_weight:
             out.grad_weight = torch.empty((v, h), dtype=torch.bfloat16, device=dev)
-            if want_f32:
-                out.grad_weight_f32 = torch.empty((v, h), dtype=torch.float32, device=dev)
+            if want_f32 or accumulate:
+                out.grad_weight_f32 = (torch.zeros if accumulate else torch.empty)((v, h), dtype=torch.float32,
+                                                                                  device=dev)
         if want_grad_bias:
             out.grad_bias = torch.empty(v, dtype=torch.bfloat16, device=dev)
-            if want_f32:
-                out.grad_bias_f32 = torch.empty(v, dtype=torch.float32, device=dev)
+            if want_f32 or accumulate:
+                out.grad_bias_f32 = (torch.zeros if accumulate else torch.empty)(v, dtype=torch.float32, device=dev)
     external = out.grad_weight_f32 is not None or out.grad_weight is None
     kind = _lib.LCE_WS_BACKWARD_EXTERNAL_F32 if external else _lib.LCE_WS_BACKWARD
     nbytes = int(lib.lce_workspace_bytes(ctypes.byref(p), kind))
     if workspace is None or workspace.numel() < nbytes:
         workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
     out.workspace_bytes = nbytes
+    opts = None
+    if row_scale is not None or accumulate:
+        if row_scale is not None:
+            _device_checks(row_scale)
+            if row_scale.dtype != torch.float32 or row_scale.shape != (n,) or not row_scale.is_contiguous():
+                raise ValueError("row_scale must be a contiguous float32 [N] tensor")
+        opts = _lib.LceBackwardOptions()
+        opts.row_scale = _ptr(row_scale)
+        opts.accumulate = 1 if accumulate else 0
+        opts.reserved = 0
     stream = torch.cuda.current_stream(dev).cuda_stream
-    code = lib.lce_forward_backward_traced(
+    code = lib.lce_forward_backward_ex(
         ctypes.byref(p), _ptr(hidden), _ptr(weight), _ptr(bias), _ptr(labels), float(grad_scale), _ptr(out.loss),
         _ptr(out.lse), _ptr(out.chunk_loss), _ptr(out.n_valid), _ptr(out.grad_hidden), _ptr(out.grad_weight),
         _ptr(out.grad_bias), _ptr(out.grad_weight_f32), _ptr(out.grad_bias_f32), _ptr(out.status),
-        _ptr(workspace), workspace.numel(), stream, None if trace is None else ctypes.byref(trace))
+        _ptr(workspace), workspace.numel(), stream, None if opts is None else ctypes.byref(opts),
+        None if trace is None else ctypes.byref(trace))
     if code != _lib.LCE_OK:
         _raise(code, "lce_forward_backward")
     return out
+
+
+def lce_scale(t: torch.Tensor, scale: torch.Tensor) -> torch.Tensor:
+    """t *= scale in place, by a library kernel; ``scale`` is a one-element
+    float32 tensor on the GPU (read by the kernel, no host synchronisation)."""
+    lib = _lib.load()
+    _device_checks(t, scale)
+    if scale.dtype != torch.float32 or scale.numel() != 1:
+        raise ValueError("scale must be a one-element float32 tensor")
+    if not t.is_contiguous():
+        raise ValueError("t must be contiguous")
+    dtype = {torch.bfloat16: _lib.LCE_DTYPE_BF16, torch.float32: _lib.LCE_DTYPE_F32}.get(t.dtype)
+    if dtype is None:
+        raise ValueError("t must be bfloat16 or float32")
+    stream = torch.cuda.current_stream(t.device).cuda_stream
+    code = lib.lce_scale(_ptr(t), dtype, t.numel(), _ptr(scale), stream)
+    if code != _lib.LCE_OK:
+        _raise(code, "lce_scale")
+    return t
+
+
+class LinearCrossEntropyFunction(torch.autograd.Function):
+    """Drop-in output head + cross-entropy with the pages' autograd contract
+    (LlamaFactory PR #10762 analysis, section 4): for sum / mean the forward
+    computes the loss and, for the inputs that need them, the gradients in one
+    library call (``needs_input_grad`` plays the pages' needs_weight_grad);
+    backward multiplies them by ``grad_output`` in a library kernel. For
+    ``reduction="none"`` the per-token gradient is only known in backward, so
+    backward runs the fused call with it as the per-row scale."""
+
+    @staticmethod
+    def forward(ctx, hidden, weight, bias, labels, ignore_index, chunk_rows, reduction, rows_in_flight):
+        need_h, need_w, need_b = ctx.needs_input_grad[:3]
+        need_b = need_b and bias is not None
+        ctx.reduction = reduction
+        ctx.args = (ignore_index, chunk_rows, rows_in_flight)
+        ctx.need = (need_h, need_w, need_b)
+        if reduction == "none" or not (need_h or need_w or need_b):
+            out = lce_forward(hidden, weight, bias, labels, ignore_index=ignore_index, chunk_rows=chunk_rows,
+                              reduction=reduction, want_lse=False)
+            if reduction == "none":
+                ctx.save_for_backward(hidden, weight, bias, labels)
+            ctx.grads = None
+            return out.loss
+        out = lce_forward_backward(hidden, weight, bias, labels, ignore_index=ignore_index, chunk_rows=chunk_rows,
+                                   reduction=reduction, want_grad_hidden=need_h, want_grad_weight=need_w,
+                                   want_grad_bias=need_b, want_lse=False, rows_in_flight=rows_in_flight)
+        ctx.grads = (out.grad_hidden, out.grad_weight, out.grad_bias)
+        return out.loss
+
+    @staticmethod
+    def backward(ctx, grad_output):
+        need_h, need_w, need_b = ctx.need
+        if ctx.reduction == "none":
+            hidden, weight, bias, labels = ctx.saved_tensors
+            ignore_index, chunk_rows, rows_in_flight = ctx.args
+            out = lce_forward_backward(hidden, weight, bias, labels, ignore_index=ignore_index,
+                                       chunk_rows=chunk_rows, reduction="none", want_grad_hidden=need_h,
+                                       want_grad_weight=need_w, want_grad_bias=need_b, want_lse=False,
+                                       rows_in_flight=rows_in_flight,
+                                       row_scale=grad_output.detach().float().contiguous())
+            gh, gw, gb = out.grad_hidden, out.grad_weight, out.grad_bias
+        else:
+            gh, gw, gb = ctx.grads
+            ctx.grads = None
+            g = grad_output.detach().float().reshape(1).contiguous()
+            for t in (gh, gw, gb):
+                if t is not None:
+                    lce_scale(t, g)
+        return (gh if need_h else None, gw if need_w else None, gb if need_b else None,
+                None, None, None, None, None)
+
+
+def linear_cross_entropy(hidden: torch.Tensor, weight: torch.Tensor, labels: torch.Tensor,
+                         bias: torch.Tensor | None = None, *, ignore_index: int = IGNORE_INDEX,
+                         chunk_rows: int | None = DEFAULT_CHUNK_ROWS, reduction: str = "mean",
+                         rows_in_flight: int | None = None) -> torch.Tensor:
+    """Cross-entropy of ``hidden @ weight.T (+ bias)`` against ``labels`` without
+    the [N, V] logits, differentiable in hidden, weight and bias. Shapes as
+    :func:`lce_forward`; bf16 inputs, float32 loss, bf16 gradients."""
+    return LinearCrossEntropyFunction.apply(hidden, weight, bias, labels, ignore_index, chunk_rows, reduction,
+                                            rows_in_flight)

@@ -20,12 +20,14 @@ LCE_ERR_LABEL_RANGE = 5
 
 LCE_REDUCTION = {"none": 0, "sum": 1, "mean": 2}
 LCE_DTYPE_BF16 = 0
+LCE_DTYPE_F32 = 1
 LCE_WS_FORWARD = 0
 LCE_WS_BACKWARD = 1
 LCE_WS_BACKWARD_EXTERNAL_F32 = 2
 
 EXPORTED = ("lce_workspace_bytes", "lce_forward", "lce_forward_backward", "lce_forward_traced",
-            "lce_forward_backward_traced", "lce_status_string", "lce_abi_version")
+            "lce_forward_backward_traced", "lce_forward_backward_ex", "lce_scale", "lce_status_string",
+            "lce_abi_version")
 
 KERNEL_KINDS = ("zero", "prepare_labels", "fwd_lse", "finalize_rows", "finalize_loss", "transpose",
                 "bwd_dlogits", "grad_hidden", "grad_weight", "cast", "label_logit")
@@ -56,6 +58,14 @@ class LceTrace(ctypes.Structure):
     ]
 
 
+class LceBackwardOptions(ctypes.Structure):
+    _fields_ = [
+        ("row_scale", ctypes.c_void_p),
+        ("accumulate", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
+    ]
+
+
 _lib = None
 
 
@@ -81,6 +91,10 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.lce_forward_traced.restype = i32
     lib.lce_forward_backward_traced.argtypes = lib.lce_forward_backward.argtypes + [T]
     lib.lce_forward_backward_traced.restype = i32
+    lib.lce_forward_backward_ex.argtypes = lib.lce_forward_backward.argtypes + [ctypes.POINTER(LceBackwardOptions), T]
+    lib.lce_forward_backward_ex.restype = i32
+    lib.lce_scale.argtypes = [vp, i32, ctypes.c_int64, vp, vp]
+    lib.lce_scale.restype = i32
     lib.lce_status_string.argtypes = [i32]
     lib.lce_status_string.restype = ctypes.c_char_p
     lib.lce_abi_version.argtypes = []

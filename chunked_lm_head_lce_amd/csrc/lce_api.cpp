@@ -242,7 +242,7 @@ int run_rows(Common& c, const void* hidden, const void* weight, const void* bias
 
 extern "C" {
 
-int lce_abi_version(void) { return 101; }
+int lce_abi_version(void) { return 102; }
 
 const char* lce_status_string(int status) {
   switch (status) {
@@ -294,14 +294,19 @@ int lce_forward(const lce_problem* p, const void* hidden, const void* weight, co
                             workspace_bytes, stream, nullptr);
 }
 
-int lce_forward_backward_traced(const lce_problem* p, const void* hidden, const void* weight, const void* bias,
-                                const int64_t* labels, float grad_scale, float* loss, float* lse,
-                                float* chunk_loss, int64_t* n_valid, void* grad_hidden, void* grad_weight,
-                                void* grad_bias, float* grad_weight_f32, float* grad_bias_f32, int32_t* status,
-                                void* workspace, size_t workspace_bytes, hipStream_t stream, lce_trace* trace) {
+int lce_forward_backward_ex(const lce_problem* p, const void* hidden, const void* weight, const void* bias,
+                            const int64_t* labels, float grad_scale, float* loss, float* lse, float* chunk_loss,
+                            int64_t* n_valid, void* grad_hidden, void* grad_weight, void* grad_bias,
+                            float* grad_weight_f32, float* grad_bias_f32, int32_t* status, void* workspace,
+                            size_t workspace_bytes, hipStream_t stream, const lce_backward_options* options,
+                            lce_trace* trace) {
   int st = validate_problem(p);
   if (st != LCE_OK) return st;
-  if (p->reduction == LCE_REDUCTION_NONE) return LCE_ERR_UNSUPPORTED;
+  const float* row_scale = options ? options->row_scale : nullptr;
+  const bool accumulate = options && options->accumulate != 0;
+  if (options && options->reserved != 0) return LCE_ERR_INVALID_ARG;
+  if (p->reduction == LCE_REDUCTION_NONE && row_scale == nullptr) return LCE_ERR_UNSUPPORTED;
+  if (row_scale != nullptr && !aligned(row_scale, 4)) return LCE_ERR_UNSUPPORTED;
   if ((grad_bias != nullptr || grad_bias_f32 != nullptr) && bias == nullptr) return LCE_ERR_INVALID_ARG;
   if (!aligned(grad_hidden, 2) || !aligned(grad_weight, 2) || !aligned(grad_bias, 2) ||
       !aligned(grad_weight_f32, 4) || !aligned(grad_bias_f32, 4))
@@ -309,6 +314,9 @@ int lce_forward_backward_traced(const lce_problem* p, const void* hidden, const 
   const bool need_gh = grad_hidden != nullptr && p->n_rows > 0;
   const bool need_gw = grad_weight != nullptr || grad_weight_f32 != nullptr;
   const bool need_gb = grad_bias != nullptr || grad_bias_f32 != nullptr;
+  // accumulating needs the caller's FP32 totals for every requested weight / bias gradient
+  if (accumulate && ((need_gw && grad_weight_f32 == nullptr) || (need_gb && grad_bias_f32 == nullptr)))
+    return LCE_ERR_INVALID_ARG;
   const int kind = (need_gw && grad_weight_f32 == nullptr) ? LCE_WS_BACKWARD : LCE_WS_BACKWARD_EXTERNAL_F32;
   Common c;
   st = check_common(p, hidden, weight, bias, labels, loss, workspace, workspace_bytes, kind, c);
@@ -324,9 +332,9 @@ int lce_forward_backward_traced(const lce_problem* p, const void* hidden, const 
   char* ws = c.ws;
   float* gw = grad_weight_f32 ? grad_weight_f32 : (float*)(ws + c.L.gw_f32);
   float* gb = grad_bias_f32 ? grad_bias_f32 : (float*)(ws + c.L.gb_f32);
-  if (need_gb) LCE_LAUNCH(tr, LCE_K_ZERO, 0, 0, 0, lce::launch_zero(gb, s.V * 4, stream));
+  if (need_gb && !accumulate) LCE_LAUNCH(tr, LCE_K_ZERO, 0, 0, 0, lce::launch_zero(gb, s.V * 4, stream));
   if (s.N == 0) {
-    if (need_gw) LCE_LAUNCH(tr, LCE_K_ZERO, 0, 0, 0, lce::launch_zero(gw, s.V * s.H * 4, stream));
+    if (need_gw && !accumulate) LCE_LAUNCH(tr, LCE_K_ZERO, 0, 0, 0, lce::launch_zero(gw, s.V * s.H * 4, stream));
   } else {
     st = run_label_logits(c, hidden, weight, bias, stream, tr);
     if (st != LCE_OK) return st;
@@ -350,8 +358,8 @@ int lce_forward_backward_traced(const lce_problem* p, const void* hidden, const 
       if (st != LCE_OK) return st;
       if (!any_grad) continue;
       LCE_LAUNCH(tr, LCE_K_BWD_DLOGITS, rows_valid, s.V, 0,
-                 lce::launch_dlogits(s, c.label32, c.part_m, c.lse_ws, c.n_valid, grad_scale, is_mean, g0, Gc, dlog,
-                                     need_gh ? 1 : 0, need_gw ? dlogT : nullptr, Gc + kGroupPad,
+                 lce::launch_dlogits(s, c.label32, c.part_m, c.lse_ws, c.n_valid, grad_scale, is_mean, row_scale, g0,
+                                     Gc, dlog, need_gh ? 1 : 0, need_gw ? dlogT : nullptr, Gc + kGroupPad,
                                      need_gb ? gb : nullptr, stream));
       if (need_gh)
         LCE_LAUNCH(tr, LCE_K_GRAD_HIDDEN, rows_valid, s.H, s.V,
@@ -360,7 +368,8 @@ int lce_forward_backward_traced(const lce_problem* p, const void* hidden, const 
         LCE_LAUNCH(tr, LCE_K_TRANSPOSE, 0, 0, 0,
                    lce::launch_transpose(hidden, s.ldh, g0, rows_valid, s.H, hT, Gc + kGroupPad, Gc, stream));
         LCE_LAUNCH(tr, LCE_K_GRAD_WEIGHT, s.V, s.H, rows_valid,
-                   lce::launch_grad_weight(s, dlogT, hT, Gc, Gc + kGroupPad, g0 == 0 ? 1 : 0, gw, stream));
+                   lce::launch_grad_weight(s, dlogT, hT, Gc, Gc + kGroupPad, (g0 == 0 && !accumulate) ? 1 : 0, gw,
+                                           stream));
       }
     }
   }
@@ -371,6 +380,24 @@ int lce_forward_backward_traced(const lce_problem* p, const void* hidden, const 
              lce::launch_finalize_loss(c.chunk_acc, c.T, c.n_valid, c.status, p->reduction, loss, chunk_loss,
                                        stream));
   return LCE_OK;
+}
+
+int lce_forward_backward_traced(const lce_problem* p, const void* hidden, const void* weight, const void* bias,
+                                const int64_t* labels, float grad_scale, float* loss, float* lse,
+                                float* chunk_loss, int64_t* n_valid, void* grad_hidden, void* grad_weight,
+                                void* grad_bias, float* grad_weight_f32, float* grad_bias_f32, int32_t* status,
+                                void* workspace, size_t workspace_bytes, hipStream_t stream, lce_trace* trace) {
+  return lce_forward_backward_ex(p, hidden, weight, bias, labels, grad_scale, loss, lse, chunk_loss, n_valid,
+                                 grad_hidden, grad_weight, grad_bias, grad_weight_f32, grad_bias_f32, status,
+                                 workspace, workspace_bytes, stream, nullptr, trace);
+}
+
+int lce_scale(void* data, int32_t dtype, int64_t n, const float* scale, hipStream_t stream) {
+  if (n < 0) return LCE_ERR_INVALID_ARG;
+  if (n == 0) return LCE_OK;
+  if (data == nullptr || scale == nullptr) return LCE_ERR_INVALID_ARG;
+  if (dtype != LCE_DTYPE_BF16 && dtype != LCE_DTYPE_F32) return LCE_ERR_INVALID_ARG;
+  return lce::launch_scale(data, dtype == LCE_DTYPE_F32, n, scale, stream) == hipSuccess ? LCE_OK : LCE_ERR_HIP;
 }
 
 int lce_forward_backward(const lce_problem* p, const void* hidden, const void* weight, const void* bias,

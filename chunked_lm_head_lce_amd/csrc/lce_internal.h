@@ -37,10 +37,14 @@ hipError_t launch_transpose(const void* in, int64_t ld_in, int64_t r0, int64_t R
                             int64_t ld_out, int64_t R_pad, hipStream_t st);
 // dlogits of one row group from the stored exp(z - max_half) in dlog: G in
 // place (when write_dlog), G^T into dlogT [Vp][ld_t] (when non-null), column
-// sums into gb_f32 (when non-null).
+// sums into gb_f32 (when non-null); row i also scaled by row_scale[i] when
+// row_scale is non-null.
 hipError_t launch_dlogits(const Shapes& s, const int32_t* label32, const float* part_m, const float* lse_ws,
-                          const unsigned long long* n_valid, float grad_scale, int is_mean, int64_t g0, int64_t G,
-                          void* dlog, int write_dlog, void* dlogT, int64_t ld_t, float* gb_f32, hipStream_t st);
+                          const unsigned long long* n_valid, float grad_scale, int is_mean, const float* row_scale,
+                          int64_t g0, int64_t G, void* dlog, int write_dlog, void* dlogT, int64_t ld_t,
+                          float* gb_f32, hipStream_t st);
+// data[k] *= *scale (bf16 or f32 elements).
+hipError_t launch_scale(void* data, bool f32, int64_t n, const float* scale, hipStream_t st);
 hipError_t launch_grad_hidden(const Shapes& s, const void* dlog, const void* wT, int64_t g0, int64_t G,
                               void* grad_hidden, hipStream_t st);
 // gw (+)= dlogT [Vp][ld] (first G columns) * (hT [H][ld])^T.

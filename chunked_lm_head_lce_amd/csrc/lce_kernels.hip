@@ -617,14 +617,16 @@ __device__ __forceinline__ int tswz(int col) { return (col >> 3) & 15; }
 __global__ void __launch_bounds__(256, 2)
 k_dlogits_from_p(u16* __restrict__ dlog, u16* __restrict__ dlogT, const float* __restrict__ part_m,
                  const int32_t* __restrict__ label32, const float* __restrict__ lse_ws,
-                 const unsigned long long* __restrict__ n_valid, float grad_scale, int is_mean, int64_t V,
-                 int64_t Vp, int64_t g0, int64_t G, int write_dlog, int64_t ld_t, float* __restrict__ gb_f32) {
+                 const unsigned long long* __restrict__ n_valid, float grad_scale, int is_mean,
+                 const float* __restrict__ row_scale, int64_t V, int64_t Vp, int64_t g0, int64_t G, int write_dlog,
+                 int64_t ld_t, float* __restrict__ gb_f32) {
   // transposed staging [256 cols][128 rows] bf16; the 16-byte row chunk c of
   // column col is stored at slot c ^ tswz(col): conflict-free for the column
   // writes (16 lanes, 16 different columns) and for the chunk reads.
   __shared__ __attribute__((aligned(16))) u16 tst[TILE * DL_ROWS];
   __shared__ float s_f[2][DL_ROWS];
   __shared__ int s_lab[DL_ROWS];
+  __shared__ float s_hot[DL_ROWS];
   __shared__ float s_gb[8][TILE];
   const int n_mt = (int)(G / DL_ROWS);
   const int tm = blockIdx.x % n_mt, tn = blockIdx.x / n_mt;
@@ -639,14 +641,16 @@ k_dlogits_from_p(u16* __restrict__ dlog, u16* __restrict__ dlogT, const float* _
     const int64_t row = g0 + lrow0 + tid;
     const int lab = label32[row];
     const float lse = lse_ws[row];
-    const bool valid = lab >= 0;
+    const bool valid = lab >= 0;                 // false for rows past N
+    const float rs = valid ? scale * (row_scale != nullptr ? row_scale[row] : 1.f) : 0.f;
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const float mh = part_m[(int64_t)(2 * tn + h) * G + lrow0 + tid];
-      s_f[h][tid] = (valid && mh != -INFINITY) ? scale * exp_fast(mh - lse) : 0.f;
+      s_f[h][tid] = (valid && mh != -INFINITY) ? rs * exp_fast(mh - lse) : 0.f;
     }
     const int64_t lc = valid ? (int64_t)lab - col0 : -1;
     s_lab[tid] = (lc >= 0 && lc < TILE) ? (int)lc : -1;
+    s_hot[tid] = rs;
   }
   __syncthreads();
   const int cb = tid & 31;                 // column chunk (8 columns), fixed per thread
@@ -667,11 +671,12 @@ k_dlogits_from_p(u16* __restrict__ dlog, u16* __restrict__ dlogT, const float* _
       const int rl = rb * 8 + r;
       const float f = s_f[half][rl];
       const int lc = s_lab[rl];
+      const float hot = s_hot[rl];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const uint32_t w = pv[r][e >> 1];
         const float pe = bf2f((u16)((e & 1) ? (w >> 16) : (w & 0xFFFF)));
-        const float g = f * pe - ((lc == cb * 8 + e) ? scale : 0.f);
+        const float g = f * pe - ((lc == cb * 8 + e) ? hot : 0.f);
         d[r][e] = g;
         colsum[e] += g;
       }
@@ -793,6 +798,20 @@ k_gemm_grad_weight(const u16* __restrict__ dlogT, const u16* __restrict__ hT, in
   }
 }
 
+// data[k] *= *scale (the scale read from device memory).
+__global__ void k_scale_bf16(u16* __restrict__ data, int64_t n, const float* __restrict__ scale) {
+  const float sc = *scale;
+  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t st = (int64_t)gridDim.x * blockDim.x;
+  for (; i < n; i += st) data[i] = f2bf(bf2f(data[i]) * sc);
+}
+__global__ void k_scale_f32(float* __restrict__ data, int64_t n, const float* __restrict__ scale) {
+  const float sc = *scale;
+  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t st = (int64_t)gridDim.x * blockDim.x;
+  for (; i < n; i += st) data[i] *= sc;
+}
+
 __global__ void k_cast_bf16(const float* __restrict__ in, u16* __restrict__ out, int64_t n) {
   int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int64_t s = (int64_t)gridDim.x * blockDim.x;
@@ -872,11 +891,13 @@ hipError_t launch_transpose(const void* in, int64_t ld_in, int64_t r0, int64_t R
 }
 
 hipError_t launch_dlogits(const Shapes& s, const int32_t* label32, const float* part_m, const float* lse_ws,
-                          const unsigned long long* n_valid, float grad_scale, int is_mean, int64_t g0, int64_t G,
-                          void* dlog, int write_dlog, void* dlogT, int64_t ld_t, float* gb_f32, hipStream_t st) {
+                          const unsigned long long* n_valid, float grad_scale, int is_mean, const float* row_scale,
+                          int64_t g0, int64_t G, void* dlog, int write_dlog, void* dlogT, int64_t ld_t,
+                          float* gb_f32, hipStream_t st) {
   const int n_mt = (int)(G / DL_ROWS), n_vt = (int)(s.Vp / TILE);
   hipLaunchKernelGGL(k_dlogits_from_p, dim3((unsigned)(n_mt * n_vt)), dim3(256), 0, st, (u16*)dlog, (u16*)dlogT,
-                     part_m, label32, lse_ws, n_valid, grad_scale, is_mean, s.V, s.Vp, g0, G, write_dlog, ld_t, gb_f32);
+                     part_m, label32, lse_ws, n_valid, grad_scale, is_mean, row_scale, s.V, s.Vp, g0, G, write_dlog,
+                     ld_t, gb_f32);
   return hipGetLastError();
 }
 
@@ -893,6 +914,15 @@ hipError_t launch_grad_weight(const Shapes& s, const void* dlogT, const void* hT
   const int n_mt = (int)(s.Vp / TILE), n_nt = (int)((s.H + TILE - 1) / TILE);
   hipLaunchKernelGGL(k_gemm_grad_weight, dim3((unsigned)(n_mt * n_nt)), dim3(NTHREADS), 0, st,
                      (const u16*)dlogT, (const u16*)hT, G, ld, s.H, s.V, s.Vp, n_mt, n_nt, first, gw_f32);
+  return hipGetLastError();
+}
+
+hipError_t launch_scale(void* data, bool f32, int64_t n, const float* scale, hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  if (f32)
+    hipLaunchKernelGGL(k_scale_f32, dim3(grid_1d(n, 256, 16384)), dim3(256), 0, st, (float*)data, n, scale);
+  else
+    hipLaunchKernelGGL(k_scale_bf16, dim3(grid_1d(n, 256, 16384)), dim3(256), 0, st, (u16*)data, n, scale);
   return hipGetLastError();
 }
 

@@ -50,7 +50,7 @@ typedef enum {
   LCE_OK = 0,
   LCE_ERR_INVALID_ARG = 1,   /* bad sizes, strides, null required pointer, chunk_rows <= 0 */
   LCE_ERR_UNSUPPORTED = 2,   /* dtype, H % 64 != 0, misaligned pointer/stride, stride or V
-                                above 2^22, NONE backward */
+                                above 2^22, NONE backward without per-row scales */
   LCE_ERR_WORKSPACE = 3,     /* workspace null or smaller than lce_workspace_bytes() */
   LCE_ERR_HIP = 4,           /* a kernel launch failed */
   LCE_ERR_LABEL_RANGE = 5    /* device-side: a label outside [0,V) and != ignore_index */
@@ -62,7 +62,7 @@ typedef enum {
   LCE_REDUCTION_MEAN = 2     /* loss[0] = sum_i l_i / max(n_valid, 1); 0 when no row is valid */
 } lce_reduction;
 
-typedef enum { LCE_DTYPE_BF16 = 0 } lce_dtype;
+typedef enum { LCE_DTYPE_BF16 = 0, LCE_DTYPE_F32 = 1 } lce_dtype;   /* problems take BF16 only */
 
 /* What lce_workspace_bytes() sizes for. */
 typedef enum {
@@ -113,7 +113,8 @@ int lce_forward(const lce_problem* p, const void* hidden, const void* weight, co
  *   grad_bias_f32   [V] float; nullable; requires bias
  * When both grad_weight and grad_weight_f32 are NULL the G^T h product is
  * skipped (the pages' needs_weight_grad == False). reduction NONE is
- * LCE_ERR_UNSUPPORTED here. Other arguments as lce_forward. */
+ * LCE_ERR_UNSUPPORTED here (lce_forward_backward_ex accepts it with per-row
+ * upstream gradients). Other arguments as lce_forward. */
 int lce_forward_backward(const lce_problem* p, const void* hidden, const void* weight,
                          const void* bias, const int64_t* labels, float grad_scale,
                          float* loss, float* lse, float* chunk_loss, int64_t* n_valid,
@@ -161,6 +162,46 @@ int lce_forward_backward_traced(const lce_problem* p, const void* hidden, const 
                                 float* grad_weight_f32, float* grad_bias_f32, int32_t* status,
                                 void* workspace, size_t workspace_bytes, hipStream_t stream,
                                 lce_trace* trace);
+
+/* Options of lce_forward_backward_ex (zero-initialised = lce_forward_backward).
+ *
+ * row_scale: [N] float, device, nullable. Row i's dlogits are additionally
+ *   multiplied by row_scale[i]: G_i = s * row_scale[i] * valid_i *
+ *   (softmax_i - onehot_i). With reduction LCE_REDUCTION_NONE this is the
+ *   per-token upstream gradient dL/dl_i (the pages' autograd function
+ *   multiplies its saved gradients by grad_output in backward; LlamaFactory
+ *   PR #10762 analysis, section 4); NONE is accepted only with row_scale.
+ * accumulate: nonzero = grad_weight_f32 and grad_bias_f32 are added to
+ *   instead of overwritten (gradient accumulation across micro-batches; the
+ *   trainer contract of LlamaFactory section 3). The FP32 buffers must then
+ *   be given for every weight / bias gradient requested (else
+ *   LCE_ERR_INVALID_ARG); grad_weight / grad_bias, if also given, receive the
+ *   bf16 cast of the accumulated totals. A step-global mean over an
+ *   externally all-reduced valid count n is reduction SUM with
+ *   grad_scale = 1 / n. */
+typedef struct {
+  const float* row_scale;
+  int32_t accumulate;
+  int32_t reserved;      /* must be 0 */
+} lce_backward_options;
+
+/* lce_forward_backward with options (NULL = none) and an optional trace. */
+int lce_forward_backward_ex(const lce_problem* p, const void* hidden, const void* weight, const void* bias,
+                            const int64_t* labels, float grad_scale, float* loss, float* lse,
+                            float* chunk_loss, int64_t* n_valid, void* grad_hidden, void* grad_weight,
+                            void* grad_bias, float* grad_weight_f32, float* grad_bias_f32, int32_t* status,
+                            void* workspace, size_t workspace_bytes, hipStream_t stream,
+                            const lce_backward_options* options, lce_trace* trace);
+
+/* data[k] *= *scale for k < n, in place, on `stream`. data: device, dtype
+ * LCE_DTYPE_BF16 (round to nearest even) or LCE_DTYPE_F32; scale: one float
+ * in device memory (e.g. an autograd grad_output), read by the kernel, so no
+ * host synchronisation. Applies an upstream gradient to gradients computed
+ * ahead of time (the pages' autograd function scales its saved gradients by
+ * grad_output in backward; LlamaFactory PR #10762 analysis, section 4).
+ * Returns LCE_ERR_INVALID_ARG for n < 0, a NULL pointer with n > 0 or an
+ * unknown dtype. */
+int lce_scale(void* data, int32_t dtype, int64_t n, const float* scale, hipStream_t stream);
 
 /* Static string for an lce_status value (never NULL). */
 const char* lce_status_string(int status);

@@ -48,7 +48,7 @@ def test_exports_every_declared_function(lib):
 
 
 def test_version_and_strings(lib):
-    assert lib.lce_abi_version() == 101
+    assert lib.lce_abi_version() == 102
     for code in range(6):
         assert _lib.status_string(code) != "unknown status"
     assert _lib.status_string(99) == "unknown status"
@@ -147,3 +147,35 @@ def test_python_layer_mirrors_page_rules():
         lce._problem(h, w, y, -100, 256, "avg", None)
     with pytest.raises(ValueError):
         lce.lce_forward(h, w, None, y)  # CPU tensors are refused, nothing is launched
+
+
+def _opts(row_scale=None, accumulate=0, reserved=0):
+    o = _lib.LceBackwardOptions()
+    o.row_scale = row_scale
+    o.accumulate = accumulate
+    o.reserved = reserved
+    return o
+
+
+def _fbx(lib, p, opts, gw=None, gw32=None):
+    return lib.lce_forward_backward_ex(ctypes.byref(p), FAKE, FAKE, None, FAKE, 1.0, FAKE, None, None, None,
+                                       None, gw, None, gw32, None, None, FAKE, 1 << 40, None,
+                                       None if opts is None else ctypes.byref(opts), None)
+
+
+def test_forward_backward_ex_host_errors(lib):
+    """Rejected on the host, before anything is enqueued."""
+    assert _fbx(lib, prob(reduction=0), None) == 2                  # NONE needs per-row scales
+    assert _fbx(lib, prob(reduction=0), _opts()) == 2
+    assert _fbx(lib, prob(), _opts(reserved=1)) == 1
+    assert _fbx(lib, prob(), _opts(accumulate=1), gw=FAKE) == 1     # accumulate without FP32 totals
+    assert _fbx(lib, prob(), _opts(row_scale=FAKE + 2)) == 2        # misaligned row_scale
+    assert _fbx(lib, prob(chunk_rows=0), _opts()) == 1
+
+
+def test_scale_host_errors(lib):
+    assert lib.lce_scale(FAKE, 0, -1, FAKE, None) == 1
+    assert lib.lce_scale(None, 0, 10, FAKE, None) == 1
+    assert lib.lce_scale(FAKE, 0, 10, None, None) == 1
+    assert lib.lce_scale(FAKE, 7, 10, FAKE, None) == 1
+    assert lib.lce_scale(None, 0, 0, None, None) == 0                # nothing to do
