@@ -184,6 +184,96 @@ def measured_traffic(kernel: str, workload: str):
     return float(fields["hbm_bytes_per_launch"])
 
 
+def memory_sweep(torch, lce, dev) -> dict:
+    """Peak extra HBM and step time of lce_forward_backward against N at the
+    Qwen3-4B / 8B head shapes, beside a plain eager PyTorch loss (F.linear +
+    F.cross_entropy + autograd, [N, V] logits) where it fits in 200 GB;
+    then chunk_rows and rows_in_flight sweeps at N=32768, H=4096. Inputs are
+    seeded on the device (hidden ~ N(0,1), weight ~ 0.02 N(0,1), labels
+    uniform, 2% ignored), all bf16."""
+    import torch.nn.functional as F
+    V = 151936
+
+    def inputs(N, H):
+        g = torch.Generator(device=dev)
+        g.manual_seed(0)
+        h = torch.randn(N, H, device=dev, generator=g).to(torch.bfloat16)
+        w = (0.02 * torch.randn(V, H, device=dev, generator=g)).to(torch.bfloat16)
+        y = torch.randint(0, V, (N,), device=dev, generator=g)
+        y[torch.randperm(N, device=dev, generator=g)[: N // 50]] = -100
+        return h, w, y
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        r = fn()
+        b.record()
+        torch.cuda.synchronize()
+        return r, a.elapsed_time(b)
+
+    def lib_run(h, w, y, **kw):
+        torch.cuda.synchronize()
+        base = torch.cuda.memory_allocated(dev)
+        torch.cuda.reset_peak_memory_stats(dev)
+        out, ms = timed(lambda: lce.lce_forward_backward(h, w, None, y, want_lse=False, **kw))
+        outs = sum(t.numel() * t.element_size() for t in (out.loss, out.n_valid, out.status, out.grad_hidden,
+                                                          out.grad_weight) if t is not None)
+        extra = torch.cuda.max_memory_allocated(dev) - base - outs
+        del out
+        return extra / 1e9, ms
+
+    def eager_run(h, w, y):
+        hh = h.detach().clone().requires_grad_(True)
+        ww = w.detach().clone().requires_grad_(True)
+        torch.cuda.synchronize()
+        base = torch.cuda.memory_allocated(dev)
+        torch.cuda.reset_peak_memory_stats(dev)
+
+        def step():
+            hh.grad = None
+            ww.grad = None
+            loss = F.cross_entropy(F.linear(hh, ww).float(), y, ignore_index=-100, reduction="sum")
+            loss.backward()
+            return loss
+        _, ms = timed(step)
+        grads = hh.grad.numel() * 2 + ww.grad.numel() * 2
+        extra = torch.cuda.max_memory_allocated(dev) - base - grads
+        del hh, ww
+        return extra / 1e9, ms
+
+    rows = []
+    for H in (2560, 4096):
+        for N in (8192, 32768, 65536, 131072, 163840):
+            h, w, y = inputs(N, H)
+            lib_gb, lib_ms = lib_run(h, w, y)
+            rec = {"hidden": H, "n_rows": N, "lib_extra_gb": lib_gb, "lib_ms": lib_ms,
+                   "logits_fp32_gb": 4.0 * N * V / 1e9}
+            if 16.0 * N * V <= 200e9:
+                eg, ems = eager_run(h, w, y)
+                rec.update({"eager_extra_gb": eg, "eager_ms": ems})
+            else:
+                rec.update({"eager_extra_gb": None, "eager_ms": None,
+                            "eager_note": "not run: predicted > 200 GB ([N,V] logits in bf16 and fp32 with grads)"})
+            log(f"[sweep] H={H} N={N}: library {lib_gb:.1f} GB {lib_ms:.0f} ms; eager {rec['eager_extra_gb']}")
+            rows.append(rec)
+            del h, w, y
+            torch.cuda.empty_cache()
+    h, w, y = inputs(32768, 4096)
+    chunks = []
+    for c in (128, 256, 512, 1024, 2048):
+        gb, ms = lib_run(h, w, y, chunk_rows=c)
+        chunks.append({"chunk_rows": c, "lib_extra_gb": gb, "lib_ms": ms})
+    groups = []
+    for g in (4096, 8192, 16384, 32768):
+        gb, ms = lib_run(h, w, y, rows_in_flight=g)
+        groups.append({"rows_in_flight": g, "lib_extra_gb": gb, "lib_ms": ms})
+    return {"metric": "peak extra HBM (GB) and fwd+bwd time (ms) vs N; library vs eager [N,V] logits",
+            "vocab": V, "rows": rows, "chunk_rows_sweep_n32768_h4096": chunks,
+            "rows_in_flight_sweep_n32768_h4096": groups}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -194,6 +284,9 @@ def main() -> int:
     ap.add_argument("--fwd-steps", type=int, default=3)
     ap.add_argument("--cpu-rows", type=int, default=4096)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--memory-sweep", action="store_true",
+                    help="instead of the benchmark: peak extra HBM and time vs N, library vs eager, and "
+                         "chunk_rows / rows_in_flight sweeps (one JSON line)")
     ap.add_argument("--no-matmul-roof", action="store_true",
                     help="skip timing torch.matmul on the logits shape (context for the roofline)")
     ap.add_argument("--copy-gib", type=float, default=0.0,
@@ -213,6 +306,9 @@ def main() -> int:
 
     w = WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
+    if args.memory_sweep:
+        print(json.dumps(memory_sweep(torch, lce, dev)), flush=True)
+        return 0
     log(f"[bench] generating {w.name} inputs (N={w.n_rows}, H={w.hidden}, V={w.vocab})")
     t0 = time.perf_counter()
     inp = make_inputs(w)
