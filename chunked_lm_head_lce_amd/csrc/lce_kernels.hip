@@ -41,6 +41,7 @@ constexpr int OPERAND_STAGE = TILE * BK * 2;       // 32 KB: one operand, one st
 constexpr int STAGE = 2 * OPERAND_STAGE;           // 64 KB: both operands
 constexpr int MAINLOOP_LDS = 2 * STAGE;            // 128 KB: double buffered
 constexpr float LOG2E = 1.4426950408889634f;       // log2(e): exp(x) = 2^(x log2 e)
+constexpr float LN2 = 0.6931471805599453f;         // ln(2) = 1 / log2(e)
 // s_waitcnt immediates (gfx9 encoding: vmcnt [3:0]+[15:14], expcnt [6:4],
 // lgkmcnt [11:8]); the other counters are left at their maximum (no wait).
 constexpr int WAIT_LGKM0 = 0xC07F;   // lgkmcnt(0)
@@ -396,34 +397,56 @@ k_fwd_tile(const u16* __restrict__ hidden, int64_t ldh, const u16* __restrict__ 
   gemm_tile(acc, hidden, ldh, row0, N, weight, ldw, col0, V, H, smem);
   __syncthreads();   // s_bias visible; the staging tile overlays the mainloop's LDS
 
-  float cb[NB];
+  // Bias pre-scaled by log2(e): exp(z - m) = exp2(acc*L + b*L - m*L) is one
+  // FMA and one exp2 per element. The four rows r of a row block are reduced
+  // together so their DPP steps interleave instead of waiting on each other.
+  float cbl[NB];
 #pragma unroll
-  for (int j = 0; j < NB; ++j) cb[j] = s_bias[acc_col(wn, j, lane)];
+  for (int j = 0; j < NB; ++j) cbl[j] = s_bias[acc_col(wn, j, lane)] * LOG2E;
 #pragma unroll
   for (int i = 0; i < NB; ++i) {
+    float m[4];                               // row max of z * log2(e)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      m[r] = -INFINITY;
+#pragma unroll
+      for (int j = 0; j < NB; ++j) m[r] = fmaxf(m[r], fmaf(acc.v[i][j][r], LOG2E, cbl[j]));
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) m[r] = fmaxf(m[r], dpp<DPP_XOR1>(m[r]));
+#pragma unroll
+    for (int r = 0; r < 4; ++r) m[r] = fmaxf(m[r], dpp<DPP_XOR2>(m[r]));
+#pragma unroll
+    for (int r = 0; r < 4; ++r) m[r] = fmaxf(m[r], dpp<DPP_HALF_MIRROR>(m[r]));
+#pragma unroll
+    for (int r = 0; r < 4; ++r) m[r] = fmaxf(m[r], dpp<DPP_MIRROR>(m[r]));
+    float sm[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int rl = acc_row(wm, i, r, lane);
-      float v[NB];
-      float m = -INFINITY;
+      const float ms = m[r] == -INFINITY ? 0.f : m[r];   // all columns past V: every e = 0
+      sm[r] = 0.f;
 #pragma unroll
       for (int j = 0; j < NB; ++j) {
-        v[j] = acc.v[i][j][r] + cb[j];
-        m = fmaxf(m, v[j]);
-      }
-      m = max16(m);
-      const float ms = m == -INFINITY ? 0.f : m;   // all columns past V: every e = 0
-      float s = 0.f;
-#pragma unroll
-      for (int j = 0; j < NB; ++j) {
-        const float e = exp_fast(v[j] - ms);
-        s += e;
+        const float e = __builtin_amdgcn_exp2f(fmaf(acc.v[i][j][r], LOG2E, cbl[j] - ms));
+        sm[r] += e;
         if (STORE_P) stage[rl * STAGE_LD + acc_col(wn, j, lane)] = f2bf(e);
       }
-      s = sum16(s);
-      if ((lane & 15) == 0) {
-        s_red_m[wn][rl] = m;
-        s_red_s[wn][rl] = s;
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) sm[r] += dpp<DPP_XOR1>(sm[r]);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) sm[r] += dpp<DPP_XOR2>(sm[r]);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) sm[r] += dpp<DPP_HALF_MIRROR>(sm[r]);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) sm[r] += dpp<DPP_MIRROR>(sm[r]);
+    if ((lane & 15) == 0) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int rl = acc_row(wm, i, r, lane);
+        s_red_m[wn][rl] = m[r] * LN2;            // back to natural-log units
+        s_red_s[wn][rl] = sm[r];
       }
     }
   }
