@@ -463,7 +463,7 @@ k_fwd_tile(const u16* __restrict__ hidden, int64_t ldh, const u16* __restrict__ 
       const int id = it * NTHREADS + tid;
       const int row = id >> 5, ch = id & 31;
       const u32x4 val = *(const LDS_AS u32x4*)(stage + row * STAGE_LD + ch * 8);
-      *(u32x4*)(p_out + (lrow0 + row) * Vp + col0 + ch * 8) = val;
+      __builtin_nontemporal_store(val, (u32x4*)(p_out + (lrow0 + row) * Vp + col0 + ch * 8));   // streamed out
     }
   }
 }
@@ -634,6 +634,8 @@ __global__ void __launch_bounds__(256) k_transpose(const u16* __restrict__ in, i
 // go into the FP32 bias gradient. Each thread owns 8 x 8 blocks: 8 rows of
 // one 16-byte column chunk, all 8 loads issued before any use, transposed in
 // registers and staged through LDS for dlogT. 72 KB of LDS: two blocks per CU.
+// G and G^T are written with non-temporal stores (read once, by the next
+// product kernel), which keep them from evicting operand lines from L2.
 constexpr int DL_ROWS = 128;
 __device__ __forceinline__ int tswz(int col) { return (col >> 3) & 15; }
 
@@ -710,7 +712,7 @@ k_dlogits_from_p(u16* __restrict__ dlog, u16* __restrict__ dlogT, const float* _
         u32x4 o;
 #pragma unroll
         for (int w = 0; w < 4; ++w) o[w] = (uint32_t)f2bf(d[r][2 * w]) | ((uint32_t)f2bf(d[r][2 * w + 1]) << 16);
-        *(u32x4*)(src + r * Vp) = o;
+        __builtin_nontemporal_store(o, (u32x4*)(src + r * Vp));
       }
     }
     if (dlogT) {
@@ -742,7 +744,7 @@ k_dlogits_from_p(u16* __restrict__ dlog, u16* __restrict__ dlogT, const float* _
       const int id = it * 256 + tid;
       const int col = id >> 4, ch = id & 15;
       const u32x4 v = *(const LDS_AS u32x4*)((LDS_AS u16*)tst + col * DL_ROWS + ((ch ^ tswz(col)) << 3));
-      *(u32x4*)(dlogT + (col0 + col) * ld_t + lrow0 + ch * 8) = v;
+      __builtin_nontemporal_store(v, (u32x4*)(dlogT + (col0 + col) * ld_t + lrow0 + ch * 8));
     }
   }
 }
