@@ -132,7 +132,8 @@ int lce_forward_backward(const lce_problem* p, const void* hidden, const void* w
  * LCE_K_FWD_LSE is the logits-tile kernel with the log-sum-exp epilogue (in
  * lce_forward_backward it also stores each row group's exp(z - max) tiles);
  * LCE_K_BWD_DLOGITS turns those stored tiles into the bf16 dlogits of the
- * group (an element-wise pass, no product). */
+ * group (an element-wise pass, no product); LCE_K_LABEL_LOGIT gathers each
+ * valid row's label logit h_i . W_{y_i} + b_{y_i}. */
 typedef enum {
   LCE_K_ZERO = 0, LCE_K_PREPARE_LABELS = 1, LCE_K_FWD_LSE = 2, LCE_K_FINALIZE_ROWS = 3,
   LCE_K_FINALIZE_LOSS = 4, LCE_K_TRANSPOSE = 5, LCE_K_BWD_DLOGITS = 6, LCE_K_GRAD_HIDDEN = 7,
