@@ -31,7 +31,6 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint16_t u16;
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int TILE = 256;                 // output tile edge (rows and columns)
 constexpr int BK = 64;                    // K depth of one LDS stage (two MFMA steps)
@@ -45,7 +44,6 @@ constexpr float LN2 = 0.6931471805599453f;         // ln(2) = 1 / log2(e)
 // s_waitcnt immediates (gfx9 encoding: vmcnt [3:0]+[15:14], expcnt [6:4],
 // lgkmcnt [11:8]); the other counters are left at their maximum (no wait).
 constexpr int WAIT_LGKM0 = 0xC07F;   // lgkmcnt(0)
-#define WAIT_LGKM(n) (0xC07F | ((n) << 8))   // lgkmcnt(n), n <= 15
 constexpr int WAIT_VM0 = 0x0F70;     // vmcnt(0)
 #define WAIT_VM(n) (((n) & 15) | (((n) >> 4) << 14) | 0x0F70)   // vmcnt(n), n <= 63
 
@@ -69,12 +67,6 @@ constexpr int DPP_XOR1 = 0xB1;          // quad_perm [1,0,3,2]
 constexpr int DPP_XOR2 = 0x4E;          // quad_perm [2,3,0,1]
 constexpr int DPP_HALF_MIRROR = 0x141;  // lane i <- 7 - i within each 8 lanes
 constexpr int DPP_MIRROR = 0x140;       // lane i <- 15 - i within each 16 lanes
-__device__ __forceinline__ float max16(float v) {
-  v = fmaxf(v, dpp<DPP_XOR1>(v));
-  v = fmaxf(v, dpp<DPP_XOR2>(v));
-  v = fmaxf(v, dpp<DPP_HALF_MIRROR>(v));
-  return fmaxf(v, dpp<DPP_MIRROR>(v));
-}
 __device__ __forceinline__ float sum16(float v) {
   v += dpp<DPP_XOR1>(v);
   v += dpp<DPP_XOR2>(v);
@@ -223,12 +215,13 @@ __device__ __forceinline__ void read_frag(Frags& f, const LDS_AS char* buf, int 
 //                 barrier: stage s+1 is visible from every wave, and buffer
 //                 s&1 is no longer read (f0 and f1 of stage s are in registers)
 //   slots 10..14  read f0 of stage s+1 (3-4 fragments per slot)
-//   slots 10..15, and 0..2 of stage s+1: the 16 global->LDS loads of stage s+2
-//                 into buffer s&1 (two per slot in 10..14 and 0..2, none in 15)
-// so every load has at least seven slots to land before the barrier that
-// publishes it, and no instruction burst stalls the wave's MFMA issue.
-// At entry: f0 holds stage s sub-step 0; loads 0..9 of stage s+1 went out in
-// the previous stage (slots 10..14), loads 10..15 go out in slots 0..2 here.
+//   slots 10..15, and 0..1 of stage s+1: the 16 global->LDS loads of stage
+//                 s+2 into buffer s&1, two per slot (after MFMAs 3 and 6)
+// so every load has at least eight slots to land before the barrier that
+// publishes it. As early as the buffer allows wins (measured): spreading
+// the loads thinner and later lost 3-8%, three per slot stalled the issue.
+// At entry: f0 holds stage s sub-step 0; loads 0..11 of stage s+1 went out
+// in the previous stage (slots 10..15), loads 12..15 go out in slots 0..1.
 __device__ __forceinline__ void mainloop_stage(Acc& acc, Frags& f0, Frags& f1, int s, int nk, LDS_AS char* smem,
                                                const TileLoads& t, int rA, int rB, int q) {
   LDS_AS char* cur = smem + (s & 1) * STAGE;
@@ -247,10 +240,10 @@ __device__ __forceinline__ void mainloop_stage(Acc& acc, Frags& f0, Frags& f1, i
     for (int j = 0; j < 3; ++j)
       acc.v[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.a[i], f.b[j], acc.v[i][j], 0, 0, 0);
     FENCE();
-    // global->LDS loads: stage s+1's last six in slots 0..2, stage s+2's first ten in slots 10..14
-    if (slot < 3) {
-      if (s + 1 < nk) stage_load(t, s + 1, 10 + 2 * slot);
-    } else if (slot >= 10 && slot < 15) {
+    // global->LDS loads: stage s+1's last four in slots 0..1, stage s+2's first twelve in slots 10..15
+    if (slot < 2) {
+      if (s + 1 < nk) stage_load(t, s + 1, 12 + 2 * slot);
+    } else if (slot >= 10) {
       if (s + 2 < nk) stage_load(t, s + 2, 2 * (slot - 10));
     }
     FENCE();
@@ -258,9 +251,9 @@ __device__ __forceinline__ void mainloop_stage(Acc& acc, Frags& f0, Frags& f1, i
     for (int j = 3; j < 6; ++j)
       acc.v[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.a[i], f.b[j], acc.v[i][j], 0, 0, 0);
     FENCE();
-    if (slot < 3) {
-      if (s + 1 < nk) stage_load(t, s + 1, 11 + 2 * slot);
-    } else if (slot >= 10 && slot < 15) {
+    if (slot < 2) {
+      if (s + 1 < nk) stage_load(t, s + 1, 13 + 2 * slot);
+    } else if (slot >= 10) {
       if (s + 2 < nk) stage_load(t, s + 2, 2 * (slot - 10) + 1);
     }
     // fragment reads: f1 of this stage in slots 0..7, f0 of the next in 10..14
@@ -306,14 +299,15 @@ __device__ __forceinline__ void gemm_tile(Acc& acc, const u16* __restrict__ X, i
   t.xbase = uniform_ptr(X + x_row0 * ldx);
   t.ybase = uniform_ptr(Y + y_row0 * ldy);
   t.lds_wave = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)smem + (uint32_t)wave * 64 * 128);
-  // Prologue: stage 0 whole, then the first ten loads of stage 1 (the rest
-  // go out in slots 0..2 of stage 0); f0 of stage 0 once stage 0 is visible.
+  // Prologue: stage 0 whole, then the first twelve loads of stage 1 (the
+  // rest go out in slots 0..1 of stage 0); f0 of stage 0 once stage 0 is
+  // visible.
 #pragma unroll
   for (int f = 0; f < 2 * FILLS; ++f) stage_load(t, 0, f);
   if (nk > 1)
 #pragma unroll
-    for (int f = 0; f < 10; ++f) stage_load(t, 1, f);
-  if (nk > 1) __builtin_amdgcn_s_waitcnt(WAIT_VM(10));
+    for (int f = 0; f < 12; ++f) stage_load(t, 1, f);
+  if (nk > 1) __builtin_amdgcn_s_waitcnt(WAIT_VM(12));
   else __builtin_amdgcn_s_waitcnt(WAIT_VM0);
   __syncthreads();
   Frags f0, f1;
