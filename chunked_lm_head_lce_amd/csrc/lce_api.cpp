@@ -94,12 +94,12 @@ Layout make_layout(const lce_problem* p, int kind) {
   L.status = take(4);
   L.zlab = take((size_t)s.Np * 4);
   L.lse = take((size_t)s.Np * 4);
-  // (max, sumexp) partials per 128-column half tile: for every row in the
+  // (max, sumexp) partials per 64-column quarter tile: for every row in the
   // forward, for one row group at a time in the backward.
   const bool bwd = kind == LCE_WS_BACKWARD || kind == LCE_WS_BACKWARD_EXTERNAL_F32;
   const int64_t part_rows = bwd ? group_rows(p, s) : s.Np;
-  L.part_m = take((size_t)2 * n_vt * part_rows * 4);
-  L.part_s = take((size_t)2 * n_vt * part_rows * 4);
+  L.part_m = take((size_t)4 * n_vt * part_rows * 4);
+  L.part_s = take((size_t)4 * n_vt * part_rows * 4);
   L.chunk_acc = take((size_t)n_chunks(p) * 8);
   if (bwd) {
     const int64_t G = group_rows(p, s);
@@ -224,7 +224,7 @@ int run_label_logits(Common& c, const void* hidden, const void* weight, const vo
 
 // Logits tiles with the online log-sum-exp epilogue for rows [g0, g0+rows),
 // then per-row lse / NLL / chunk sums. With p_out the tiles also leave
-// exp(z - max_half) behind for the gradient of the same rows.
+// exp(z - max_quarter) behind for the gradient of the same rows.
 int run_rows(Common& c, const void* hidden, const void* weight, const void* bias, int64_t g0, int64_t rows,
              void* p_out, float* loss, float* lse_out, hipStream_t st, Tracer& tr) {
   const Shapes& s = c.s;
@@ -339,7 +339,7 @@ int lce_forward_backward_ex(const lce_problem* p, const void* hidden, const void
     st = run_label_logits(c, hidden, weight, bias, stream, tr);
     if (st != LCE_OK) return st;
     // Row groups: the logits of a group are computed once; the tiles leave
-    // exp(z - max_half) in dlog, the group's lse follows, and the dlogits
+    // exp(z - max_quarter) in dlog, the group's lse follows, and the dlogits
     // pass turns dlog into G (and G^T) for the two gradient products.
     const int64_t G = group_rows(p, s);
     void* wT = ws + c.L.wT;

@@ -18,9 +18,9 @@ hipError_t launch_zero(void* p, int64_t bytes, hipStream_t st);
 hipError_t launch_prepare_labels(const int64_t* labels, int64_t N, int64_t Np, int64_t V, int64_t ignore,
                                  int32_t* label32, unsigned long long* n_valid, int32_t* status,
                                  hipStream_t st);
-// Forward tiles for rows [g0, g0 + rows) (rows a multiple of 256): half-tile
-// (max, sumexp) partials into part_m/part_s [2 * Vp/256][rows] and, when
-// p_out is non-null, bf16 exp(z - max_half) into p_out [rows][Vp].
+// Forward tiles for rows [g0, g0 + rows) (rows a multiple of 256): quarter-tile
+// (max, sumexp) partials into part_m/part_s [4 * Vp/256][rows] and, when
+// p_out is non-null, bf16 exp(z - max_quarter) into p_out [rows][Vp].
 hipError_t launch_fwd_tiles(const Shapes& s, const void* hidden, const void* weight, const void* bias, int64_t g0,
                             int64_t rows, float* part_m, float* part_s, void* p_out, hipStream_t st);
 // zlab[i] = h_i . W_{y_i} + b_{y_i} for valid rows.
@@ -35,7 +35,7 @@ hipError_t launch_finalize_loss(const double* chunk_acc, int64_t T, const unsign
                                 hipStream_t st);
 hipError_t launch_transpose(const void* in, int64_t ld_in, int64_t r0, int64_t R_valid, int64_t C, void* out,
                             int64_t ld_out, int64_t R_pad, hipStream_t st);
-// dlogits of one row group from the stored exp(z - max_half) in dlog: G in
+// dlogits of one row group from the stored exp(z - max_quarter) in dlog: G in
 // place (when write_dlog), G^T into dlogT [Vp][ld_t] (when non-null), column
 // sums into gb_f32 (when non-null); row i also scaled by row_scale[i] when
 // row_scale is non-null.

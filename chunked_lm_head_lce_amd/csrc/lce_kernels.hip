@@ -34,8 +34,10 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int TILE = 256;                 // output tile edge (rows and columns)
 constexpr int BK = 64;                    // K depth of one LDS stage (two MFMA steps)
-constexpr int NTHREADS = 256;             // 4 waves, 2 x 2, each owns 128 x 128
-constexpr int NB = 8;                     // 16 x 16 MFMA blocks per wave edge (128 / 16)
+constexpr int NTHREADS = 512;             // 8 waves (two per SIMD), 2 x 4, each owns 128 x 64
+constexpr int NB = 8;                     // 16 x 16 MFMA row blocks per wave (128 / 16)
+constexpr int NBJ = 4;                    // 16 x 16 MFMA column blocks per wave (64 / 16)
+constexpr int NQ = TILE / 64;             // column quarters of a tile (one per wave column)
 constexpr int OPERAND_STAGE = TILE * BK * 2;       // 32 KB: one operand, one stage
 constexpr int STAGE = 2 * OPERAND_STAGE;           // 64 KB: both operands
 constexpr int MAINLOOP_LDS = 2 * STAGE;            // 128 KB: double buffered
@@ -110,14 +112,14 @@ __device__ __forceinline__ int lds_off(int r, int c) { return r * 128 + ((c ^ sw
 // Direct global->LDS fills. One global_load_lds_dwordx4 writes 64 x 16 B
 // contiguously (lane i at +16 i), i.e. 8 tile rows of 128 B; lane i fetches
 // the logical chunk stored at slot (i & 7) of row (i >> 3) of its 8-row
-// block: c = (i & 7) ^ swz(row). A wave fills 64 rows of each operand per
-// stage (8 loads per operand). Rows past the operand's end are clamped to its
-// last row (finite values the epilogues discard).
+// block: c = (i & 7) ^ swz(row). Each of the 8 waves fills 32 rows of each
+// operand per stage (4 loads per operand). Rows past the operand's end are
+// clamped to its last row (finite values the epilogues discard).
 //
 // The per-lane byte offsets inside the tile are fixed for the whole K loop
 // (StageOffsets, computed once); the tile base is wave-uniform (scalar
 // registers) and each stage only adds 128 bytes to the 32-bit offsets.
-constexpr int FILLS = 8;                   // loads per wave per operand per stage
+constexpr int FILLS = 4;                   // loads per wave per operand per stage
 struct StageOffsets {
   uint32_t off[FILLS];
 };
@@ -126,7 +128,7 @@ __device__ __forceinline__ StageOffsets stage_offsets(int64_t ld, int64_t row0, 
   StageOffsets o;
 #pragma unroll
   for (int b = 0; b < FILLS; ++b) {
-    const int r = wave * 64 + b * 8 + (lane >> 3);
+    const int r = wave * 32 + b * 8 + (lane >> 3);
     const int c = (lane & 7) ^ swz(r);
     int64_t lr = r;
     if (row0 + lr > nrows - 1) lr = nrows - 1 - row0;
@@ -151,25 +153,25 @@ __device__ __forceinline__ bf16x8 frag(const LDS_AS char* stage, int r, int c) {
 }
 
 struct Acc {
-  f32x4 v[NB][NB];   // [row block i][col block j], 16 x 16 each
+  f32x4 v[NB][NBJ];   // [row block i][col block j], 16 x 16 each
 };
 
 // Accumulator layout (v_mfma_f32_16x16x32_bf16): lane l, register r (0..3) of
 // block (i, j) of wave (wm, wn) holds C[row][col] with
-//   row = wm*128 + i*16 + 4*(l/16) + r,   col = wn*128 + j*16 + (l%16).
+//   row = wm*128 + i*16 + 4*(l/16) + r,   col = wn*64 + j*16 + (l%16).
 // Operand fragments: lane l supplies row (l%16) of its 16-row block and the
 // 8 consecutive k at 8*(l/16) of the 32-deep step, for A and for B alike.
 __device__ __forceinline__ int acc_row(int wm, int i, int r, int lane) {
   return wm * 128 + i * 16 + 4 * (lane >> 4) + r;
 }
-__device__ __forceinline__ int acc_col(int wn, int j, int lane) { return wn * 128 + j * 16 + (lane & 15); }
+__device__ __forceinline__ int acc_col(int wn, int j, int lane) { return wn * 64 + j * 16 + (lane & 15); }
 
 // Operand tiles of one GEMM tile and where their stages go.
 struct TileLoads {
   const void* xbase;
   const void* ybase;
   StageOffsets ox, oy;
-  uint32_t lds_wave;     // LDS byte address of this wave's 64 rows in stage buffer 0
+  uint32_t lds_wave;     // LDS byte address of this wave's 32 rows in stage buffer 0
 };
 
 __device__ __forceinline__ const void* uniform_ptr(const void* p) {
@@ -179,7 +181,7 @@ __device__ __forceinline__ const void* uniform_ptr(const void* p) {
   return (const void*)(uintptr_t)((hi << 32) | lo);
 }
 
-// Issues load f (0..15) of stage s: f < 8 fill X rows, f >= 8 fill Y rows.
+// Issues load f (0..7) of stage s: f < 4 fill X rows, f >= 4 fill Y rows.
 __device__ __forceinline__ void stage_load(const TileLoads& t, int s, int f) {
   const uint32_t buf = t.lds_wave + (uint32_t)((s & 1) * STAGE);
   const uint32_t koff = (uint32_t)s * (BK * 2);
@@ -197,31 +199,33 @@ __device__ __forceinline__ void stage_load(const TileLoads& t, int s, int f) {
 // compiler from moving memory accesses across it.
 __device__ __forceinline__ void bare_barrier() { asm volatile("s_barrier" ::: "memory"); }
 
-// Fragments of one 32-deep sub-step: A row blocks 0..7, B column blocks 0..7.
+// Fragments of one 32-deep sub-step: A row blocks 0..7, B column blocks 0..3.
 struct Frags {
-  bf16x8 a[NB], b[NB];
+  bf16x8 a[NB], b[NBJ];
 };
-// Fragment read n (0..15) of sub-step `sub` (0, 1) of the stage in `buf`: B
+// Fragment read n (0..11) of sub-step `sub` (0, 1) of the stage in `buf`: B
 // blocks first (every MFMA of the first row block needs all of them), then A.
 __device__ __forceinline__ void read_frag(Frags& f, const LDS_AS char* buf, int sub, int n, int rA, int rB, int q) {
-  if (n < NB) f.b[n] = frag(buf + OPERAND_STAGE, rB + n * 16, sub * 4 + q);
-  else f.a[n - NB] = frag(buf, rA + (n - NB) * 16, sub * 4 + q);
+  if (n < NBJ) f.b[n] = frag(buf + OPERAND_STAGE, rB + n * 16, sub * 4 + q);
+  else f.a[n - NBJ] = frag(buf, rA + (n - NBJ) * 16, sub * 4 + q);
 }
 
-// Schedule of one 64-deep stage s, in 16 slots of 8 MFMAs (slots 0..7:
-// sub-step 0 from fragment set f0, slots 8..15: sub-step 1 from f1):
-//   slots 0..7    read f1 (stage s, sub-step 1), two fragments per slot
+// Schedule of one 64-deep stage s, in 16 slots of 4 MFMAs (slots 0..7:
+// sub-step 0 from fragment set f0, slots 8..15: sub-step 1 from f1), two
+// waves per SIMD:
+//   slots 0..5    read f1 (stage s, sub-step 1), two fragments per slot
 //   slot 10       wait for this wave's loads of stage s+1 and its LDS reads,
 //                 barrier: stage s+1 is visible from every wave, and buffer
 //                 s&1 is no longer read (f0 and f1 of stage s are in registers)
-//   slots 10..14  read f0 of stage s+1 (3-4 fragments per slot)
-//   slots 10..15, and 0..1 of stage s+1: the 16 global->LDS loads of stage
-//                 s+2 into buffer s&1, two per slot (after MFMAs 3 and 6)
+//   slots 10..15  read f0 of stage s+1, two per slot
+//   slots 10..15, and 0..1 of stage s+1: the 8 global->LDS loads of stage s+2
+//                 into buffer s&1, one per slot (after the second MFMA)
 // so every load has at least eight slots to land before the barrier that
-// publishes it. As early as the buffer allows wins (measured): spreading
-// the loads thinner and later lost 3-8%, three per slot stalled the issue.
-// At entry: f0 holds stage s sub-step 0; loads 0..11 of stage s+1 went out
-// in the previous stage (slots 10..15), loads 12..15 go out in slots 0..1.
+// publishes it. (Measured: two waves per SIMD with this schedule beat one
+// wave per SIMD with 128 x 128 per wave by 1.5-5%; issuing the loads two per
+// slot was slower here.)
+// At entry: f0 holds stage s sub-step 0; loads 0..5 of stage s+1 went out in
+// the previous stage (slots 10..15), loads 6..7 go out in slots 0..1.
 __device__ __forceinline__ void mainloop_stage(Acc& acc, Frags& f0, Frags& f1, int s, int nk, LDS_AS char* smem,
                                                const TileLoads& t, int rA, int rB, int q) {
   LDS_AS char* cur = smem + (s & 1) * STAGE;
@@ -236,39 +240,23 @@ __device__ __forceinline__ void mainloop_stage(Acc& acc, Frags& f0, Frags& f1, i
       bare_barrier();
     }
     FENCE();
-#pragma unroll
-    for (int j = 0; j < 3; ++j)
-      acc.v[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.a[i], f.b[j], acc.v[i][j], 0, 0, 0);
-    FENCE();
-    // global->LDS loads: stage s+1's last four in slots 0..1, stage s+2's first twelve in slots 10..15
-    if (slot < 2) {
-      if (s + 1 < nk) stage_load(t, s + 1, 12 + 2 * slot);
-    } else if (slot >= 10) {
-      if (s + 2 < nk) stage_load(t, s + 2, 2 * (slot - 10));
-    }
-    FENCE();
-#pragma unroll
-    for (int j = 3; j < 6; ++j)
-      acc.v[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.a[i], f.b[j], acc.v[i][j], 0, 0, 0);
+    acc.v[i][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.a[i], f.b[0], acc.v[i][0], 0, 0, 0);
+    acc.v[i][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.a[i], f.b[1], acc.v[i][1], 0, 0, 0);
     FENCE();
     if (slot < 2) {
-      if (s + 1 < nk) stage_load(t, s + 1, 13 + 2 * slot);
+      if (s + 1 < nk) stage_load(t, s + 1, 6 + slot);
     } else if (slot >= 10) {
-      if (s + 2 < nk) stage_load(t, s + 2, 2 * (slot - 10) + 1);
+      if (s + 2 < nk) stage_load(t, s + 2, slot - 10);
     }
-    // fragment reads: f1 of this stage in slots 0..7, f0 of the next in 10..14
-    if (slot < 8) read_frag(f1, cur, 1, 2 * slot, rA, rB, q);
-    else if (slot >= 10 && slot < 15) {
-      const int n0 = (slot - 10) * 16 / 5, n1 = (slot - 9) * 16 / 5;
-#pragma unroll
-      for (int n = n0; n < n1; ++n) read_frag(f0, nxt, 0, n, rA, rB, q);
-    }
+    // fragment reads: f1 of this stage in slots 0..5, f0 of the next in 10..15
+    if (slot < 6) read_frag(f1, cur, 1, 2 * slot, rA, rB, q);
+    else if (slot >= 10) read_frag(f0, nxt, 0, 2 * (slot - 10), rA, rB, q);
     FENCE();
-#pragma unroll
-    for (int j = 6; j < NB; ++j)
-      acc.v[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.a[i], f.b[j], acc.v[i][j], 0, 0, 0);
+    acc.v[i][2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.a[i], f.b[2], acc.v[i][2], 0, 0, 0);
+    acc.v[i][3] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.a[i], f.b[3], acc.v[i][3], 0, 0, 0);
     FENCE();
-    if (slot < 8) read_frag(f1, cur, 1, 2 * slot + 1, rA, rB, q);
+    if (slot < 6) read_frag(f1, cur, 1, 2 * slot + 1, rA, rB, q);
+    else if (slot >= 10) read_frag(f0, nxt, 0, 2 * (slot - 10) + 1, rA, rB, q);
   }
   FENCE();
 }
@@ -283,36 +271,35 @@ __device__ __forceinline__ void gemm_tile(Acc& acc, const u16* __restrict__ X, i
                                           int64_t y_row0, int64_t y_rows, int64_t K, LDS_AS char* smem) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave >> 2, wn = wave & 3;
 #pragma unroll
   for (int i = 0; i < NB; ++i)
 #pragma unroll
-    for (int j = 0; j < NB; ++j)
+    for (int j = 0; j < NBJ; ++j)
 #pragma unroll
       for (int r = 0; r < 4; ++r) acc.v[i][j][r] = 0.f;
 
   const int nk = (int)(K / BK);
-  const int rA = wm * 128 + (lane & 15), rB = wn * 128 + (lane & 15), q = lane >> 4;
+  const int rA = wm * 128 + (lane & 15), rB = wn * 64 + (lane & 15), q = lane >> 4;
   TileLoads t;
   t.ox = stage_offsets(ldx, x_row0, x_rows, wave, lane);
   t.oy = stage_offsets(ldy, y_row0, y_rows, wave, lane);
   t.xbase = uniform_ptr(X + x_row0 * ldx);
   t.ybase = uniform_ptr(Y + y_row0 * ldy);
-  t.lds_wave = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)smem + (uint32_t)wave * 64 * 128);
-  // Prologue: stage 0 whole, then the first twelve loads of stage 1 (the
-  // rest go out in slots 0..1 of stage 0); f0 of stage 0 once stage 0 is
-  // visible.
+  t.lds_wave = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)smem + (uint32_t)wave * 32 * 128);
+  // Prologue: stage 0 whole, then the first six loads of stage 1 (the rest
+  // go out in slots 0..1 of stage 0); f0 of stage 0 once stage 0 is visible.
 #pragma unroll
   for (int f = 0; f < 2 * FILLS; ++f) stage_load(t, 0, f);
   if (nk > 1)
 #pragma unroll
-    for (int f = 0; f < 12; ++f) stage_load(t, 1, f);
-  if (nk > 1) __builtin_amdgcn_s_waitcnt(WAIT_VM(12));
+    for (int f = 0; f < 6; ++f) stage_load(t, 1, f);
+  if (nk > 1) __builtin_amdgcn_s_waitcnt(WAIT_VM(6));
   else __builtin_amdgcn_s_waitcnt(WAIT_VM0);
   __syncthreads();
   Frags f0, f1;
 #pragma unroll
-  for (int n = 0; n < 2 * NB; ++n) read_frag(f0, smem, 0, n, rA, rB, q);
+  for (int n = 0; n < NB + NBJ; ++n) read_frag(f0, smem, 0, n, rA, rB, q);
   for (int s = 0; s < nk; ++s) mainloop_stage(acc, f0, f1, s, nk, smem, t, rA, rB, q);
   __builtin_amdgcn_s_waitcnt(WAIT_LGKM0);
 }
@@ -359,12 +346,12 @@ constexpr int STAGE_LDS = TILE * STAGE_LD * 2;        // 135168 B
 
 // Forward tile: z = h W^T + b for 256 rows x 256 vocabulary ids, reduced in
 // the epilogue to each row's (max, sum exp(z - max)) over each wave's
-// 128-column half of the tile (part index 2*tile + half). z never leaves
-// registers. With STORE_P (backward row groups) the tile also writes the bf16
-// unnormalised softmax exp(z - max_half) into p [rows][Vp]; the dlogits pass
-// turns it into G once the row's lse is known, so the logits are computed
-// only once per call. Columns past V count as z = -inf (p = 0); a half tile
-// with no column below V stores max = -inf and sum = 0.
+// 64-column quarter of the tile (part index NQ*tile + quarter). z never
+// leaves registers. With STORE_P (backward row groups) the tile also writes
+// the bf16 unnormalised softmax exp(z - max_quarter) into p [rows][Vp]; the
+// dlogits pass turns it into G once the row's lse is known, so the logits are
+// computed only once per call. Columns past V count as z = -inf (p = 0); a
+// quarter with no column below V stores max = -inf and sum = 0.
 template <bool STORE_P>
 __global__ void __launch_bounds__(NTHREADS, 1)
 k_fwd_tile(const u16* __restrict__ hidden, int64_t ldh, const u16* __restrict__ weight, int64_t ldw,
@@ -372,8 +359,8 @@ k_fwd_tile(const u16* __restrict__ hidden, int64_t ldh, const u16* __restrict__ 
            int n_mt, int n_vt, float* __restrict__ part_m, float* __restrict__ part_s, u16* __restrict__ p_out) {
   __shared__ __attribute__((aligned(16))) char smem_raw[STORE_P ? STAGE_LDS : MAINLOOP_LDS];
   __shared__ float s_bias[TILE];
-  __shared__ float s_red_m[2][TILE];
-  __shared__ float s_red_s[2][TILE];
+  __shared__ float s_red_m[NQ][TILE];
+  __shared__ float s_red_s[NQ][TILE];
   LDS_AS char* smem = (LDS_AS char*)smem_raw;
   LDS_AS u16* stage = (LDS_AS u16*)smem_raw;
 
@@ -383,9 +370,9 @@ k_fwd_tile(const u16* __restrict__ hidden, int64_t ldh, const u16* __restrict__ 
   const int64_t row0 = g0 + lrow0;
   const int64_t col0 = (int64_t)tn * TILE;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave >> 2, wn = wave & 3;
   // bias, with -inf marking columns past V
-  s_bias[tid] = col0 + tid < V ? (bias != nullptr ? bf2f(bias[col0 + tid]) : 0.f) : -INFINITY;
+  if (tid < TILE) s_bias[tid] = col0 + tid < V ? (bias != nullptr ? bf2f(bias[col0 + tid]) : 0.f) : -INFINITY;
 
   Acc acc;
   gemm_tile(acc, hidden, ldh, row0, N, weight, ldw, col0, V, H, smem);
@@ -394,9 +381,9 @@ k_fwd_tile(const u16* __restrict__ hidden, int64_t ldh, const u16* __restrict__ 
   // Bias pre-scaled by log2(e): exp(z - m) = exp2(acc*L + b*L - m*L) is one
   // FMA and one exp2 per element. The four rows r of a row block are reduced
   // together so their DPP steps interleave instead of waiting on each other.
-  float cbl[NB];
+  float cbl[NBJ];
 #pragma unroll
-  for (int j = 0; j < NB; ++j) cbl[j] = s_bias[acc_col(wn, j, lane)] * LOG2E;
+  for (int j = 0; j < NBJ; ++j) cbl[j] = s_bias[acc_col(wn, j, lane)] * LOG2E;
 #pragma unroll
   for (int i = 0; i < NB; ++i) {
     float m[4];                               // row max of z * log2(e)
@@ -404,7 +391,7 @@ k_fwd_tile(const u16* __restrict__ hidden, int64_t ldh, const u16* __restrict__ 
     for (int r = 0; r < 4; ++r) {
       m[r] = -INFINITY;
 #pragma unroll
-      for (int j = 0; j < NB; ++j) m[r] = fmaxf(m[r], fmaf(acc.v[i][j][r], LOG2E, cbl[j]));
+      for (int j = 0; j < NBJ; ++j) m[r] = fmaxf(m[r], fmaf(acc.v[i][j][r], LOG2E, cbl[j]));
     }
 #pragma unroll
     for (int r = 0; r < 4; ++r) m[r] = fmaxf(m[r], dpp<DPP_XOR1>(m[r]));
@@ -421,7 +408,7 @@ k_fwd_tile(const u16* __restrict__ hidden, int64_t ldh, const u16* __restrict__ 
       const float ms = m[r] == -INFINITY ? 0.f : m[r];   // all columns past V: every e = 0
       sm[r] = 0.f;
 #pragma unroll
-      for (int j = 0; j < NB; ++j) {
+      for (int j = 0; j < NBJ; ++j) {
         const float e = __builtin_amdgcn_exp2f(fmaf(acc.v[i][j][r], LOG2E, cbl[j] - ms));
         sm[r] += e;
         if (STORE_P) stage[rl * STAGE_LD + acc_col(wn, j, lane)] = f2bf(e);
@@ -445,13 +432,13 @@ k_fwd_tile(const u16* __restrict__ hidden, int64_t ldh, const u16* __restrict__ 
     }
   }
   __syncthreads();
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    part_m[(int64_t)(2 * tn + h) * ld_part + lrow0 + tid] = s_red_m[h][tid];
-    part_s[(int64_t)(2 * tn + h) * ld_part + lrow0 + tid] = s_red_s[h][tid];
+  for (int idx = tid; idx < NQ * TILE; idx += NTHREADS) {
+    const int h = idx / TILE, row = idx % TILE;
+    part_m[(int64_t)(NQ * tn + h) * ld_part + lrow0 + row] = s_red_m[h][row];
+    part_s[(int64_t)(NQ * tn + h) * ld_part + lrow0 + row] = s_red_s[h][row];
   }
   if (STORE_P) {
-    // 256 rows x 32 sixteen-byte chunks; lanes 0..31 cover one row.
+    // 256 rows x 32 sixteen-byte chunks; 32 lanes cover one row.
 #pragma unroll 4
     for (int it = 0; it < TILE * TILE / 8 / NTHREADS; ++it) {
       const int id = it * NTHREADS + tid;
@@ -491,7 +478,7 @@ __global__ void __launch_bounds__(256) k_label_logit(const u16* __restrict__ hid
   if (lane == 0) zlab[row] = acc + (bias != nullptr ? bf2f(bias[lab]) : 0.f);
 }
 
-// Per row i in [row_begin, row_end): merge the half-tile (max, sumexp)
+// Per row i in [row_begin, row_end): merge the quarter-tile (max, sumexp)
 // partials into lse, form l_i, write lse (and l_i for reduction NONE), and
 // add l_i into its chunk's float64 sum. Partials of row i sit at
 // part[k * ld_part + (i - part_row0)], k < n_part. Rows in [N, row_end) only
@@ -621,8 +608,9 @@ __global__ void __launch_bounds__(256) k_transpose(const u16* __restrict__ in, i
 }
 
 // dlogits for one 128-row x 256-column block of a row group, from the
-// stored unnormalised softmax p~ = exp(z - max_half) (bf16, written by the
-// forward tile): G = s valid (p~ exp(max_half - lse) - [j == y]). G
+// stored unnormalised softmax p~ = exp(z - max_q) (bf16, written by the
+// forward tile, max_q over the 64-column quarter q of the tile):
+// G = s valid (p~ exp(max_q - lse) - [j == y]). G
 // overwrites p~ in dlog [G][Vp] (vocabulary contiguous) when `write_dlog`,
 // and goes to dlogT [Vp][G] (rows contiguous) when non-null; its column sums
 // go into the FP32 bias gradient. Each thread owns 8 x 8 blocks: 8 rows of
@@ -643,7 +631,7 @@ k_dlogits_from_p(u16* __restrict__ dlog, u16* __restrict__ dlogT, const float* _
   // column col is stored at slot c ^ tswz(col): conflict-free for the column
   // writes (16 lanes, 16 different columns) and for the chunk reads.
   __shared__ __attribute__((aligned(16))) u16 tst[TILE * DL_ROWS];
-  __shared__ float s_f[2][DL_ROWS];
+  __shared__ float s_f[NQ][DL_ROWS];
   __shared__ int s_lab[DL_ROWS];
   __shared__ float s_hot[DL_ROWS];
   __shared__ float s_gb[8][TILE];
@@ -663,8 +651,8 @@ k_dlogits_from_p(u16* __restrict__ dlog, u16* __restrict__ dlogT, const float* _
     const bool valid = lab >= 0;                 // false for rows past N
     const float rs = valid ? scale * (row_scale != nullptr ? row_scale[row] : 1.f) : 0.f;
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const float mh = part_m[(int64_t)(2 * tn + h) * G + lrow0 + tid];
+    for (int h = 0; h < NQ; ++h) {
+      const float mh = part_m[(int64_t)(NQ * tn + h) * G + lrow0 + tid];
       s_f[h][tid] = (valid && mh != -INFINITY) ? rs * exp_fast(mh - lse) : 0.f;
     }
     const int64_t lc = valid ? (int64_t)lab - col0 : -1;
@@ -673,7 +661,7 @@ k_dlogits_from_p(u16* __restrict__ dlog, u16* __restrict__ dlogT, const float* _
   }
   __syncthreads();
   const int cb = tid & 31;                 // column chunk (8 columns), fixed per thread
-  const int half = cb >> 4;
+  const int qtr = cb >> 3;                 // 64-column quarter of the chunk
   float colsum[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) colsum[e] = 0.f;
@@ -688,7 +676,7 @@ k_dlogits_from_p(u16* __restrict__ dlog, u16* __restrict__ dlogT, const float* _
 #pragma unroll
     for (int r = 0; r < 8; ++r) {
       const int rl = rb * 8 + r;
-      const float f = s_f[half][rl];
+      const float f = s_f[qtr][rl];
       const int lc = s_lab[rl];
       const float hot = s_hot[rl];
 #pragma unroll
@@ -753,7 +741,7 @@ k_gemm_grad_hidden(const u16* __restrict__ dlog, const u16* __restrict__ wT, int
   tile_coords(n_mt, n_nt, tm, tn);
   const int64_t lrow0 = (int64_t)tm * TILE, col0 = (int64_t)tn * TILE;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave >> 2, wn = wave & 3;
   Acc acc;
   gemm_tile(acc, dlog, Vp, lrow0, G, wT, Vp, col0, H, Vp, smem);
 #pragma unroll
@@ -763,7 +751,7 @@ k_gemm_grad_hidden(const u16* __restrict__ dlog, const u16* __restrict__ wT, int
       const int64_t row = g0 + lrow0 + acc_row(wm, i, r, lane);
       if (row >= N) continue;
 #pragma unroll
-      for (int j = 0; j < NB; ++j) {
+      for (int j = 0; j < NBJ; ++j) {
         const int64_t col = col0 + acc_col(wn, j, lane);
         if (col < H) grad_hidden[row * H + col] = f2bf(acc.v[i][j][r]);
       }
@@ -771,12 +759,9 @@ k_gemm_grad_hidden(const u16* __restrict__ dlog, const u16* __restrict__ wT, int
 }
 
 // grad_weight FP32 accumulation for one group: gw[v][:] (+)= dlogT [Vp][G] * (h^T [H][G])^T.
-// The read-modify-write goes GW_RB 16-row blocks at a time with all their
-// reads issued before the adds and stores, so 32 * GW_RB reads per thread
-// are in flight together.
-#ifndef GW_RB
-#define GW_RB 2
-#endif
+// The read-modify-write goes two 16-row blocks at a time with all their
+// reads issued before the adds and stores, so 32 reads per thread are in
+// flight together.
 __global__ void __launch_bounds__(NTHREADS, 1)
 k_gemm_grad_weight(const u16* __restrict__ dlogT, const u16* __restrict__ hT, int64_t G, int64_t ld, int64_t H,
                    int64_t V, int64_t Vp, int n_mt, int n_nt, int first, float* __restrict__ gw_f32) {
@@ -786,30 +771,30 @@ k_gemm_grad_weight(const u16* __restrict__ dlogT, const u16* __restrict__ hT, in
   tile_coords(n_mt, n_nt, tm, tn);
   const int64_t row0 = (int64_t)tm * TILE, col0 = (int64_t)tn * TILE;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave >> 2, wn = wave & 3;
   Acc acc;
   gemm_tile(acc, dlogT, ld, row0, Vp, hT, ld, col0, H, G, smem);
 #pragma unroll
-  for (int i0 = 0; i0 < NB; i0 += GW_RB) {
-    float old[GW_RB][4][NB];
+  for (int i0 = 0; i0 < NB; i0 += 2) {
+    float old[2][4][NBJ];
 #pragma unroll
-    for (int di = 0; di < GW_RB; ++di)
+    for (int di = 0; di < 2; ++di)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int64_t v = row0 + acc_row(wm, i0 + di, r, lane);
 #pragma unroll
-        for (int j = 0; j < NB; ++j) {
+        for (int j = 0; j < NBJ; ++j) {
           const int64_t col = col0 + acc_col(wn, j, lane);
           old[di][r][j] = (!first && v < V && col < H) ? gw_f32[v * H + col] : 0.f;
         }
       }
 #pragma unroll
-    for (int di = 0; di < GW_RB; ++di)
+    for (int di = 0; di < 2; ++di)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int64_t v = row0 + acc_row(wm, i0 + di, r, lane);
 #pragma unroll
-        for (int j = 0; j < NB; ++j) {
+        for (int j = 0; j < NBJ; ++j) {
           const int64_t col = col0 + acc_col(wn, j, lane);
           if (v < V && col < H) gw_f32[v * H + col] = old[di][r][j] + acc.v[i0 + di][j][r];
         }
@@ -888,7 +873,7 @@ hipError_t launch_finalize_rows(const Shapes& s, const float* part_m, const floa
                                 int reduction, float* lse_ws, float* lse_out, float* rowloss_out,
                                 double* chunk_acc, hipStream_t st) {
   hipLaunchKernelGGL(k_finalize_rows, dim3((unsigned)(rows / FIN_ROWS)), dim3(64 * FIN_WAVES), 0, st, part_m, part_s, rows, g0,
-                     (int)(2 * (s.Vp / TILE)), zlab, label32, s.N, g0, g0 + rows, s.chunk_rows, status, reduction,
+                     (int)(NQ * (s.Vp / TILE)), zlab, label32, s.N, g0, g0 + rows, s.chunk_rows, status, reduction,
                      lse_ws, lse_out, rowloss_out, chunk_acc);
   return hipGetLastError();
 }
