@@ -17,17 +17,6 @@ constexpr int64_t kTile = 256;
 constexpr int64_t kDefaultRowsInFlight = 16384;
 constexpr int64_t kMaxRowsInFlight = int64_t(1) << 20;
 constexpr int64_t kMaxStride = int64_t(1) << 22;
-// Row stride of the K-contiguous [.][G] buffers of a row group (G^T, h^T).
-// One direct load reads 16 rows at once; with G a multiple of 256 the rows
-// would be a power-of-two multiple of 512 bytes apart, share the address
-// bits that select a memory channel and queue on a few channels (measured:
-// grad_weight 20% slower). 64 elements (128 bytes) of padding per row
-// spread them.
-#ifndef LCE_GROUP_PAD
-#define LCE_GROUP_PAD 64
-#endif
-constexpr int64_t kGroupPad = LCE_GROUP_PAD;
-
 int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
@@ -103,10 +92,11 @@ Layout make_layout(const lce_problem* p, int kind) {
   L.chunk_acc = take((size_t)n_chunks(p) * 8);
   if (bwd) {
     const int64_t G = group_rows(p, s);
+    // the four backward operands, each stored as K-slabs [K/64][rows][64]
     L.wT = take((size_t)s.H * s.Vp * 2);
-    L.hT = take((size_t)s.H * (G + kGroupPad) * 2);
+    L.hT = take((size_t)s.H * G * 2);
     L.dlog = take((size_t)G * s.Vp * 2);
-    L.dlogT = take((size_t)s.Vp * (G + kGroupPad) * 2);
+    L.dlogT = take((size_t)s.Vp * G * 2);
     L.gb_f32 = take((size_t)s.Vp * 4);
     if (kind == LCE_WS_BACKWARD) L.gw_f32 = take((size_t)s.V * s.H * 4);
   }
@@ -350,7 +340,7 @@ int lce_forward_backward_ex(const lce_problem* p, const void* hidden, const void
     const bool any_grad = need_gh || need_gw || need_gb;
     if (need_gh)
       LCE_LAUNCH(tr, LCE_K_TRANSPOSE, 0, 0, 0,
-                 lce::launch_transpose(weight, s.ldw, 0, s.V, s.H, wT, s.Vp, s.Vp, stream));
+                 lce::launch_transpose(weight, s.ldw, 0, s.V, s.H, wT, s.Vp, stream));
     for (int64_t g0 = 0; g0 < s.Np; g0 += G) {
       const int64_t Gc = (s.Np - g0) < G ? (s.Np - g0) : G;
       const int64_t rows_valid = (s.N - g0) < Gc ? (s.N - g0) : Gc;
@@ -359,17 +349,16 @@ int lce_forward_backward_ex(const lce_problem* p, const void* hidden, const void
       if (!any_grad) continue;
       LCE_LAUNCH(tr, LCE_K_BWD_DLOGITS, rows_valid, s.V, 0,
                  lce::launch_dlogits(s, c.label32, c.part_m, c.lse_ws, c.n_valid, grad_scale, is_mean, row_scale, g0,
-                                     Gc, dlog, need_gh ? 1 : 0, need_gw ? dlogT : nullptr, Gc + kGroupPad,
-                                     need_gb ? gb : nullptr, stream));
+                                     Gc, dlog, need_gh ? 1 : 0, need_gw ? dlogT : nullptr, need_gb ? gb : nullptr,
+                                     stream));
       if (need_gh)
         LCE_LAUNCH(tr, LCE_K_GRAD_HIDDEN, rows_valid, s.H, s.V,
                    lce::launch_grad_hidden(s, dlog, wT, g0, Gc, grad_hidden, stream));
       if (need_gw) {
         LCE_LAUNCH(tr, LCE_K_TRANSPOSE, 0, 0, 0,
-                   lce::launch_transpose(hidden, s.ldh, g0, rows_valid, s.H, hT, Gc + kGroupPad, Gc, stream));
+                   lce::launch_transpose(hidden, s.ldh, g0, rows_valid, s.H, hT, Gc, stream));
         LCE_LAUNCH(tr, LCE_K_GRAD_WEIGHT, s.V, s.H, rows_valid,
-                   lce::launch_grad_weight(s, dlogT, hT, Gc, Gc + kGroupPad, (g0 == 0 && !accumulate) ? 1 : 0, gw,
-                                           stream));
+                   lce::launch_grad_weight(s, dlogT, hT, Gc, (g0 == 0 && !accumulate) ? 1 : 0, gw, stream));
       }
     }
   }

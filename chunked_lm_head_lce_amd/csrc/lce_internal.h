@@ -20,7 +20,8 @@ hipError_t launch_prepare_labels(const int64_t* labels, int64_t N, int64_t Np, i
                                  hipStream_t st);
 // Forward tiles for rows [g0, g0 + rows) (rows a multiple of 256): quarter-tile
 // (max, sumexp) partials into part_m/part_s [4 * Vp/256][rows] and, when
-// p_out is non-null, bf16 exp(z - max_quarter) into p_out [rows][Vp].
+// p_out is non-null, bf16 exp(z - max_quarter) into p_out, stored as K-slabs
+// [Vp/64][rows][64] (element (i, j) at ((j/64) * rows + i) * 64 + j % 64).
 hipError_t launch_fwd_tiles(const Shapes& s, const void* hidden, const void* weight, const void* bias, int64_t g0,
                             int64_t rows, float* part_m, float* part_s, void* p_out, hipStream_t st);
 // zlab[i] = h_i . W_{y_i} + b_{y_i} for valid rows.
@@ -33,22 +34,27 @@ hipError_t launch_finalize_rows(const Shapes& s, const float* part_m, const floa
 hipError_t launch_finalize_loss(const double* chunk_acc, int64_t T, const unsigned long long* n_valid,
                                 const int32_t* status, int reduction, float* loss, float* chunk_out,
                                 hipStream_t st);
+// out = rows [r0, r0 + R_valid) of in [.][ld_in] (first C columns), transposed
+// and stored as K-slabs [R_pad/64][C][64]: element (c, r) at
+// ((r/64) * C + c) * 64 + r % 64; rows R_valid..R_pad-1 are zero.
 hipError_t launch_transpose(const void* in, int64_t ld_in, int64_t r0, int64_t R_valid, int64_t C, void* out,
-                            int64_t ld_out, int64_t R_pad, hipStream_t st);
-// dlogits of one row group from the stored exp(z - max_quarter) in dlog: G in
-// place (when write_dlog), G^T into dlogT [Vp][ld_t] (when non-null), column
-// sums into gb_f32 (when non-null); row i also scaled by row_scale[i] when
-// row_scale is non-null.
+                            int64_t R_pad, hipStream_t st);
+// dlogits of one row group from the stored exp(z - max_quarter) in dlog
+// (K-slabs [Vp/64][G][64]): G in place (when write_dlog), G^T into dlogT as
+// K-slabs [G/64][Vp][64] (when non-null), column sums into gb_f32 (when
+// non-null); row i also scaled by row_scale[i] when row_scale is non-null.
 hipError_t launch_dlogits(const Shapes& s, const int32_t* label32, const float* part_m, const float* lse_ws,
                           const unsigned long long* n_valid, float grad_scale, int is_mean, const float* row_scale,
-                          int64_t g0, int64_t G, void* dlog, int write_dlog, void* dlogT, int64_t ld_t,
-                          float* gb_f32, hipStream_t st);
+                          int64_t g0, int64_t G, void* dlog, int write_dlog, void* dlogT, float* gb_f32,
+                          hipStream_t st);
 // data[k] *= *scale (bf16 or f32 elements).
 hipError_t launch_scale(void* data, bool f32, int64_t n, const float* scale, hipStream_t st);
+// grad_hidden rows [g0, g0 + G) = dlog * wT^T over K = Vp (dlog: K-slabs
+// [Vp/64][G][64], wT: [Vp/64][H][64]).
 hipError_t launch_grad_hidden(const Shapes& s, const void* dlog, const void* wT, int64_t g0, int64_t G,
                               void* grad_hidden, hipStream_t st);
-// gw (+)= dlogT [Vp][ld] (first G columns) * (hT [H][ld])^T.
-hipError_t launch_grad_weight(const Shapes& s, const void* dlogT, const void* hT, int64_t G, int64_t ld, int first,
+// gw (+)= dlogT * hT^T over K = G (dlogT: K-slabs [G/64][Vp][64], hT: [G/64][H][64]).
+hipError_t launch_grad_weight(const Shapes& s, const void* dlogT, const void* hT, int64_t G, int first,
                               float* gw_f32, hipStream_t st);
 hipError_t launch_cast(const float* in, void* out, int64_t n, hipStream_t st);
 

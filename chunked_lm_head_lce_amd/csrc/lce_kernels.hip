@@ -15,8 +15,12 @@
 //   z tile       X = hidden rows,       Y = weight rows,  K = H
 //                (per backward row group the epilogue also keeps bf16
 //                exp(z - max), which an element-wise pass turns into G)
-//   grad_hidden  X = dlogits [G][Vp],   Y = W^T [H][Vp],  K = Vp
-//   grad_weight  X = dlogits^T [Vp][G], Y = h^T [H][G],   K = G
+//   grad_hidden  X = dlogits,   Y = W^T,  K = Vp
+//   grad_weight  X = dlogits^T, Y = h^T,  K = G
+// The backward operands are written by this library's own passes, so they
+// are stored as K-slabs: [K/64][rows][64], each 64-deep stage of a 256-row
+// tile one contiguous 32 KB block (row-major operands with row strides of
+// 30-300 KB touch hundreds of DRAM pages per stage; measured 1-3% slower).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 #include <math.h>
@@ -166,10 +170,14 @@ __device__ __forceinline__ int acc_row(int wm, int i, int r, int lane) {
 }
 __device__ __forceinline__ int acc_col(int wn, int j, int lane) { return wn * 64 + j * 16 + (lane & 15); }
 
-// Operand tiles of one GEMM tile and where their stages go.
+// Operand tiles of one GEMM tile and where their stages go. Stage s of an
+// operand starts at base + s * kstride bytes: 128 for a row-major operand
+// (the next 64 k of the same rows), rows * 128 for one stored as K-slabs
+// [K/64][rows][64] (the next slab).
 struct TileLoads {
   const void* xbase;
   const void* ybase;
+  int64_t kx, ky;
   StageOffsets ox, oy;
   uint32_t lds_wave;     // LDS byte address of this wave's 32 rows in stage buffer 0
 };
@@ -184,11 +192,10 @@ __device__ __forceinline__ const void* uniform_ptr(const void* p) {
 // Issues load f (0..7) of stage s: f < 4 fill X rows, f >= 4 fill Y rows.
 __device__ __forceinline__ void stage_load(const TileLoads& t, int s, int f) {
   const uint32_t buf = t.lds_wave + (uint32_t)((s & 1) * STAGE);
-  const uint32_t koff = (uint32_t)s * (BK * 2);
   if (f < FILLS)
-    lds_dma16(t.xbase, t.ox.off[f] + koff, buf + f * 1024);
+    lds_dma16((const char*)t.xbase + s * t.kx, t.ox.off[f], buf + f * 1024);
   else
-    lds_dma16(t.ybase, t.oy.off[f - FILLS] + koff, buf + OPERAND_STAGE + (f - FILLS) * 1024);
+    lds_dma16((const char*)t.ybase + s * t.ky, t.oy.off[f - FILLS], buf + OPERAND_STAGE + (f - FILLS) * 1024);
 }
 
 #define FENCE() __builtin_amdgcn_sched_barrier(0)
@@ -262,13 +269,16 @@ __device__ __forceinline__ void mainloop_stage(Acc& acc, Frags& f0, Frags& f1, i
 }
 
 // C tile (256 x 256, fp32 in registers) = X[x_row0 : +256][0:K] * Y[y_row0 : +256][0:K]^T.
-// K % 64 == 0; 256 rows of either operand span < 4 GiB (row strides below
+// K % 64 == 0; ldx / ldy are the row strides in elements (64 for K-slab
+// operands) and kx / ky the bytes from one 64-deep stage to the next (see
+// TileLoads); 256 rows of either operand span < 4 GiB (row strides below
 // 2^22 elements). smem must hold MAINLOOP_LDS bytes. Every LDS access of the
 // stages (loads and reads) completes before the routine returns, but without
 // a final barrier: a caller that reuses smem must synchronise first.
-__device__ __forceinline__ void gemm_tile(Acc& acc, const u16* __restrict__ X, int64_t ldx, int64_t x_row0,
-                                          int64_t x_rows, const u16* __restrict__ Y, int64_t ldy,
-                                          int64_t y_row0, int64_t y_rows, int64_t K, LDS_AS char* smem) {
+__device__ __forceinline__ void gemm_tile(Acc& acc, const u16* __restrict__ X, int64_t ldx, int64_t kx,
+                                          int64_t x_row0, int64_t x_rows, const u16* __restrict__ Y, int64_t ldy,
+                                          int64_t ky, int64_t y_row0, int64_t y_rows, int64_t K,
+                                          LDS_AS char* smem) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 2, wn = wave & 3;
@@ -286,6 +296,8 @@ __device__ __forceinline__ void gemm_tile(Acc& acc, const u16* __restrict__ X, i
   t.oy = stage_offsets(ldy, y_row0, y_rows, wave, lane);
   t.xbase = uniform_ptr(X + x_row0 * ldx);
   t.ybase = uniform_ptr(Y + y_row0 * ldy);
+  t.kx = kx;
+  t.ky = ky;
   t.lds_wave = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)smem + (uint32_t)wave * 32 * 128);
   // Prologue: stage 0 whole, then the first six loads of stage 1 (the rest
   // go out in slots 0..1 of stage 0); f0 of stage 0 once stage 0 is visible.
@@ -375,7 +387,7 @@ k_fwd_tile(const u16* __restrict__ hidden, int64_t ldh, const u16* __restrict__ 
   if (tid < TILE) s_bias[tid] = col0 + tid < V ? (bias != nullptr ? bf2f(bias[col0 + tid]) : 0.f) : -INFINITY;
 
   Acc acc;
-  gemm_tile(acc, hidden, ldh, row0, N, weight, ldw, col0, V, H, smem);
+  gemm_tile(acc, hidden, ldh, BK * 2, row0, N, weight, ldw, BK * 2, col0, V, H, smem);
   __syncthreads();   // s_bias visible; the staging tile overlays the mainloop's LDS
 
   // Bias pre-scaled by log2(e): exp(z - m) = exp2(acc*L + b*L - m*L) is one
@@ -438,13 +450,15 @@ k_fwd_tile(const u16* __restrict__ hidden, int64_t ldh, const u16* __restrict__ 
     part_s[(int64_t)(NQ * tn + h) * ld_part + lrow0 + row] = s_red_s[h][row];
   }
   if (STORE_P) {
-    // 256 rows x 32 sixteen-byte chunks; 32 lanes cover one row.
+    // 256 rows x 32 sixteen-byte chunks; 32 lanes cover one row, 8 lanes
+    // one quarter (128 B of K-slab col0/64 + quarter).
+    u16* pq = p_out + (col0 >> 6) * ld_part * 64;
 #pragma unroll 4
     for (int it = 0; it < TILE * TILE / 8 / NTHREADS; ++it) {
       const int id = it * NTHREADS + tid;
       const int row = id >> 5, ch = id & 31;
       const u32x4 val = *(const LDS_AS u32x4*)(stage + row * STAGE_LD + ch * 8);
-      __builtin_nontemporal_store(val, (u32x4*)(p_out + (lrow0 + row) * Vp + col0 + ch * 8));   // streamed out
+      __builtin_nontemporal_store(val, (u32x4*)(pq + ((ch >> 3) * ld_part + lrow0 + row) * 64 + (ch & 7) * 8));
     }
   }
 }
@@ -569,7 +583,7 @@ __global__ void __launch_bounds__(256) k_finalize_loss(const double* __restrict_
 constexpr int TT = 128;
 __global__ void __launch_bounds__(256) k_transpose(const u16* __restrict__ in, int64_t ld_in, int64_t r0,
                                                    int64_t R_valid, int64_t C, u16* __restrict__ out,
-                                                   int64_t ld_out, int64_t R_pad) {
+                                                   int64_t R_pad) {
   __shared__ __attribute__((aligned(16))) u16 t[TT * TT];
   const int64_t cb = (int64_t)blockIdx.x * TT, rb = (int64_t)blockIdx.y * TT;
   const int tid = threadIdx.x;
@@ -594,7 +608,8 @@ __global__ void __launch_bounds__(256) k_transpose(const u16* __restrict__ in, i
     *(LDS_AS u32x4*)((LDS_AS u16*)t + col * TT + ((rk ^ ((col >> 3) & 15)) << 3)) = o;
   }
   __syncthreads();
-  // 128 output rows (columns of `in`) x 16 sixteen-byte chunks; 16 lanes per row.
+  // 128 output rows (columns of `in`) x 16 sixteen-byte chunks; 16 lanes per
+  // row, 8 per K-slab (out is [R_pad/64][C][64]).
 #pragma unroll
   for (int it = 0; it < TT * TT / 8 / 256; ++it) {
     const int id = it * 256 + tid;
@@ -602,7 +617,7 @@ __global__ void __launch_bounds__(256) k_transpose(const u16* __restrict__ in, i
     const int64_t c = cb + col, r = rb + ch * 8;
     if (c < C && r < R_pad) {
       const u32x4 val = *(const LDS_AS u32x4*)((LDS_AS u16*)t + col * TT + ((ch ^ ((col >> 3) & 15)) << 3));
-      *(u32x4*)(out + c * ld_out + r) = val;
+      *(u32x4*)(out + ((r >> 6) * C + c) * 64 + (r & 63)) = val;
     }
   }
 }
@@ -611,8 +626,8 @@ __global__ void __launch_bounds__(256) k_transpose(const u16* __restrict__ in, i
 // stored unnormalised softmax p~ = exp(z - max_q) (bf16, written by the
 // forward tile, max_q over the 64-column quarter q of the tile):
 // G = s valid (p~ exp(max_q - lse) - [j == y]). G
-// overwrites p~ in dlog [G][Vp] (vocabulary contiguous) when `write_dlog`,
-// and goes to dlogT [Vp][G] (rows contiguous) when non-null; its column sums
+// overwrites p~ in dlog (K-slabs [Vp/64][G][64]) when `write_dlog`, and goes
+// to dlogT (K-slabs [G/64][Vp][64]) when non-null; its column sums
 // go into the FP32 bias gradient. Each thread owns 8 x 8 blocks: 8 rows of
 // one 16-byte column chunk, all 8 loads issued before any use, transposed in
 // registers and staged through LDS for dlogT. 72 KB of LDS: two blocks per CU.
@@ -626,7 +641,7 @@ k_dlogits_from_p(u16* __restrict__ dlog, u16* __restrict__ dlogT, const float* _
                  const int32_t* __restrict__ label32, const float* __restrict__ lse_ws,
                  const unsigned long long* __restrict__ n_valid, float grad_scale, int is_mean,
                  const float* __restrict__ row_scale, int64_t V, int64_t Vp, int64_t g0, int64_t G, int write_dlog,
-                 int64_t ld_t, float* __restrict__ gb_f32) {
+                 float* __restrict__ gb_f32) {
   // transposed staging [256 cols][128 rows] bf16; the 16-byte row chunk c of
   // column col is stored at slot c ^ tswz(col): conflict-free for the column
   // writes (16 lanes, 16 different columns) and for the chunk reads.
@@ -668,10 +683,10 @@ k_dlogits_from_p(u16* __restrict__ dlog, u16* __restrict__ dlogT, const float* _
 #pragma unroll 1
   for (int it = 0; it < DL_ROWS / 64; ++it) {
     const int rb = it * 8 + (tid >> 5);    // row block (8 rows)
-    u16* src = dlog + (lrow0 + rb * 8) * Vp + col0 + cb * 8;
+    u16* src = dlog + (((col0 >> 6) + qtr) * G + lrow0 + rb * 8) * 64 + (cb & 7) * 8;
     u32x4 pv[8];
 #pragma unroll
-    for (int r = 0; r < 8; ++r) pv[r] = *(const u32x4*)(src + r * Vp);
+    for (int r = 0; r < 8; ++r) pv[r] = *(const u32x4*)(src + r * 64);
     float d[8][8];                         // [row][col]
 #pragma unroll
     for (int r = 0; r < 8; ++r) {
@@ -694,7 +709,7 @@ k_dlogits_from_p(u16* __restrict__ dlog, u16* __restrict__ dlogT, const float* _
         u32x4 o;
 #pragma unroll
         for (int w = 0; w < 4; ++w) o[w] = (uint32_t)f2bf(d[r][2 * w]) | ((uint32_t)f2bf(d[r][2 * w + 1]) << 16);
-        __builtin_nontemporal_store(o, (u32x4*)(src + r * Vp));
+        __builtin_nontemporal_store(o, (u32x4*)(src + r * 64));
       }
     }
     if (dlogT) {
@@ -720,18 +735,21 @@ k_dlogits_from_p(u16* __restrict__ dlog, u16* __restrict__ dlogT, const float* _
     atomicAdd(gb_f32 + col0 + tid, sum);
   }
   if (dlogT) {
-    // 256 columns x 16 sixteen-byte row chunks; 16 lanes cover one column.
+    // 256 columns x 16 sixteen-byte row chunks; 16 lanes cover one column,
+    // 8 lanes its 128 B in one K-slab.
 #pragma unroll 4
     for (int it = 0; it < TILE * DL_ROWS / 8 / 256; ++it) {
       const int id = it * 256 + tid;
       const int col = id >> 4, ch = id & 15;
       const u32x4 v = *(const LDS_AS u32x4*)((LDS_AS u16*)tst + col * DL_ROWS + ((ch ^ tswz(col)) << 3));
-      __builtin_nontemporal_store(v, (u32x4*)(dlogT + (col0 + col) * ld_t + lrow0 + ch * 8));
+      __builtin_nontemporal_store(
+          v, (u32x4*)(dlogT + (((lrow0 >> 6) + (ch >> 3)) * Vp + col0 + col) * 64 + (ch & 7) * 8));
     }
   }
 }
 
-// grad_hidden rows of one group: C = dlog [G][Vp] * (W^T [H][Vp])^T, cast to bf16.
+// grad_hidden rows of one group: C = dlog * (W^T)^T over K = Vp, cast to bf16;
+// dlog is stored as K-slabs [Vp/64][G][64], W^T as [Vp/64][H][64].
 __global__ void __launch_bounds__(NTHREADS, 1)
 k_gemm_grad_hidden(const u16* __restrict__ dlog, const u16* __restrict__ wT, int64_t Vp, int64_t H,
                    int64_t N, int64_t g0, int64_t G, int n_mt, int n_nt, u16* __restrict__ grad_hidden) {
@@ -743,7 +761,7 @@ k_gemm_grad_hidden(const u16* __restrict__ dlog, const u16* __restrict__ wT, int
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int wm = wave >> 2, wn = wave & 3;
   Acc acc;
-  gemm_tile(acc, dlog, Vp, lrow0, G, wT, Vp, col0, H, Vp, smem);
+  gemm_tile(acc, dlog, BK, G * BK * 2, lrow0, G, wT, BK, H * BK * 2, col0, H, Vp, smem);
 #pragma unroll
   for (int i = 0; i < NB; ++i)
 #pragma unroll
@@ -758,12 +776,13 @@ k_gemm_grad_hidden(const u16* __restrict__ dlog, const u16* __restrict__ wT, int
     }
 }
 
-// grad_weight FP32 accumulation for one group: gw[v][:] (+)= dlogT [Vp][G] * (h^T [H][G])^T.
+// grad_weight FP32 accumulation for one group: gw[v][:] (+)= dlogT * (h^T)^T over K = G;
+// dlogT is stored as K-slabs [G/64][Vp][64], h^T as [G/64][H][64].
 // The read-modify-write goes two 16-row blocks at a time with all their
 // reads issued before the adds and stores, so 32 reads per thread are in
 // flight together.
 __global__ void __launch_bounds__(NTHREADS, 1)
-k_gemm_grad_weight(const u16* __restrict__ dlogT, const u16* __restrict__ hT, int64_t G, int64_t ld, int64_t H,
+k_gemm_grad_weight(const u16* __restrict__ dlogT, const u16* __restrict__ hT, int64_t G, int64_t H,
                    int64_t V, int64_t Vp, int n_mt, int n_nt, int first, float* __restrict__ gw_f32) {
   __shared__ __attribute__((aligned(16))) char smem_raw[MAINLOOP_LDS];
   LDS_AS char* smem = (LDS_AS char*)smem_raw;
@@ -773,7 +792,7 @@ k_gemm_grad_weight(const u16* __restrict__ dlogT, const u16* __restrict__ hT, in
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int wm = wave >> 2, wn = wave & 3;
   Acc acc;
-  gemm_tile(acc, dlogT, ld, row0, Vp, hT, ld, col0, H, G, smem);
+  gemm_tile(acc, dlogT, BK, Vp * BK * 2, row0, Vp, hT, BK, H * BK * 2, col0, H, G, smem);
 #pragma unroll
   for (int i0 = 0; i0 < NB; i0 += 2) {
     float old[2][4][NBJ];
@@ -887,21 +906,21 @@ hipError_t launch_finalize_loss(const double* chunk_acc, int64_t T, const unsign
 }
 
 hipError_t launch_transpose(const void* in, int64_t ld_in, int64_t r0, int64_t R_valid, int64_t C, void* out,
-                            int64_t ld_out, int64_t R_pad, hipStream_t st) {
+                            int64_t R_pad, hipStream_t st) {
   dim3 grid((unsigned)((C + TT - 1) / TT), (unsigned)((R_pad + TT - 1) / TT));
   hipLaunchKernelGGL(k_transpose, grid, dim3(256), 0, st, (const u16*)in, ld_in, r0, R_valid, C, (u16*)out,
-                     ld_out, R_pad);
+                     R_pad);
   return hipGetLastError();
 }
 
 hipError_t launch_dlogits(const Shapes& s, const int32_t* label32, const float* part_m, const float* lse_ws,
                           const unsigned long long* n_valid, float grad_scale, int is_mean, const float* row_scale,
-                          int64_t g0, int64_t G, void* dlog, int write_dlog, void* dlogT, int64_t ld_t,
-                          float* gb_f32, hipStream_t st) {
+                          int64_t g0, int64_t G, void* dlog, int write_dlog, void* dlogT, float* gb_f32,
+                          hipStream_t st) {
   const int n_mt = (int)(G / DL_ROWS), n_vt = (int)(s.Vp / TILE);
   hipLaunchKernelGGL(k_dlogits_from_p, dim3((unsigned)(n_mt * n_vt)), dim3(256), 0, st, (u16*)dlog, (u16*)dlogT,
                      part_m, label32, lse_ws, n_valid, grad_scale, is_mean, row_scale, s.V, s.Vp, g0, G, write_dlog,
-                     ld_t, gb_f32);
+                     gb_f32);
   return hipGetLastError();
 }
 
@@ -913,11 +932,11 @@ hipError_t launch_grad_hidden(const Shapes& s, const void* dlog, const void* wT,
   return hipGetLastError();
 }
 
-hipError_t launch_grad_weight(const Shapes& s, const void* dlogT, const void* hT, int64_t G, int64_t ld, int first,
+hipError_t launch_grad_weight(const Shapes& s, const void* dlogT, const void* hT, int64_t G, int first,
                               float* gw_f32, hipStream_t st) {
   const int n_mt = (int)(s.Vp / TILE), n_nt = (int)((s.H + TILE - 1) / TILE);
   hipLaunchKernelGGL(k_gemm_grad_weight, dim3((unsigned)(n_mt * n_nt)), dim3(NTHREADS), 0, st,
-                     (const u16*)dlogT, (const u16*)hT, G, ld, s.H, s.V, s.Vp, n_mt, n_nt, first, gw_f32);
+                     (const u16*)dlogT, (const u16*)hT, G, s.H, s.V, s.Vp, n_mt, n_nt, first, gw_f32);
   return hipGetLastError();
 }
 
