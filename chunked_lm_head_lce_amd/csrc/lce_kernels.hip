@@ -87,10 +87,7 @@ __device__ __forceinline__ float sum16(float v) {
 // column tiles, so concurrently running tiles on one XCD share operand panels
 // in that XCD's L2.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ void tile_coords(int n_m, int n_n, int& tm, int& tn) {
-  const int nb = gridDim.x;
-  int t = blockIdx.x;
-  if ((nb & 7) == 0) t = (t & 7) * (nb >> 3) + (t >> 3);
+__device__ __forceinline__ void tile_from_index(int t, int n_m, int n_n, int& tm, int& tn) {
   constexpr int GROUP_M = 4;
   const int per_group = GROUP_M * n_n;
   const int g = t / per_group;
@@ -99,6 +96,27 @@ __device__ __forceinline__ void tile_coords(int n_m, int n_n, int& tm, int& tn) 
   const int in_g = t - g * per_group;
   tm = first_m + in_g % gm;
   tn = in_g / gm;
+}
+// One workgroup per tile (grid = n_m * n_n).
+__device__ __forceinline__ void tile_coords(int n_m, int n_n, int& tm, int& tn) {
+  const int nb = gridDim.x;
+  int t = blockIdx.x;
+  if ((nb & 7) == 0) t = (t & 7) * (nb >> 3) + (t >> 3);
+  tile_from_index(t, n_m, n_n, tm, tn);
+}
+// Persistent walk (grid a multiple of 8, at most one workgroup per CU): XCD
+// x = blockIdx % 8 owns logical tiles [x * per_xcd, (x + 1) * per_xcd), and
+// its gridDim/8 workgroups take them in turn, so the tiles running at once on
+// one XCD are consecutive, as in tile_coords. Returns false once the
+// workgroup's share is done (the same for every wave of the workgroup).
+__device__ __forceinline__ bool walk_tile(int n_m, int n_n, int it, int& tm, int& tn) {
+  const int ntiles = n_m * n_n;
+  const int per_xcd = (ntiles + 7) >> 3;
+  const int k = it * (int)(gridDim.x >> 3) + (int)(blockIdx.x >> 3);
+  const int t = (int)(blockIdx.x & 7) * per_xcd + k;
+  if (k >= per_xcd || t >= ntiles) return false;
+  tile_from_index(t, n_m, n_n, tm, tn);
+  return true;
 }
 
 // ---------------------------------------------------------------------------
@@ -275,10 +293,37 @@ __device__ __forceinline__ void mainloop_stage(Acc& acc, Frags& f0, Frags& f1, i
 // 2^22 elements). smem must hold MAINLOOP_LDS bytes. Every LDS access of the
 // stages (loads and reads) completes before the routine returns, but without
 // a final barrier: a caller that reuses smem must synchronise first.
-__device__ __forceinline__ void gemm_tile(Acc& acc, const u16* __restrict__ X, int64_t ldx, int64_t kx,
-                                          int64_t x_row0, int64_t x_rows, const u16* __restrict__ Y, int64_t ldy,
-                                          int64_t ky, int64_t y_row0, int64_t y_rows, int64_t K,
-                                          LDS_AS char* smem) {
+//
+// In three steps, so that a persistent kernel can issue the next tile's first
+// loads before it runs the current tile's epilogue: tile_setup (addresses
+// only), tile_prologue (stage 0 and the first six loads of stage 1; the rest
+// go out in slots 0..1 of stage 0) and tile_run (the K loop). Between
+// tile_prologue and tile_run the caller may issue any other memory accesses
+// except to the stage buffers: tile_run's first wait (vmcnt <= 6) is then
+// only stricter, since direct loads complete in issue order.
+__device__ __forceinline__ TileLoads tile_setup(const u16* __restrict__ X, int64_t ldx, int64_t kx, int64_t x_row0,
+                                                int64_t x_rows, const u16* __restrict__ Y, int64_t ldy, int64_t ky,
+                                                int64_t y_row0, int64_t y_rows, LDS_AS char* smem) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  TileLoads t;
+  t.ox = stage_offsets(ldx, x_row0, x_rows, wave, lane);
+  t.oy = stage_offsets(ldy, y_row0, y_rows, wave, lane);
+  t.xbase = uniform_ptr(X + x_row0 * ldx);
+  t.ybase = uniform_ptr(Y + y_row0 * ldy);
+  t.kx = kx;
+  t.ky = ky;
+  t.lds_wave = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)smem + (uint32_t)wave * 32 * 128);
+  return t;
+}
+__device__ __forceinline__ void tile_prologue(const TileLoads& t, int nk) {
+#pragma unroll
+  for (int f = 0; f < 2 * FILLS; ++f) stage_load(t, 0, f);
+  if (nk > 1)
+#pragma unroll
+    for (int f = 0; f < 6; ++f) stage_load(t, 1, f);
+}
+__device__ __forceinline__ void tile_run(Acc& acc, const TileLoads& t, int nk, LDS_AS char* smem) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 2, wn = wave & 3;
@@ -288,24 +333,7 @@ __device__ __forceinline__ void gemm_tile(Acc& acc, const u16* __restrict__ X, i
     for (int j = 0; j < NBJ; ++j)
 #pragma unroll
       for (int r = 0; r < 4; ++r) acc.v[i][j][r] = 0.f;
-
-  const int nk = (int)(K / BK);
   const int rA = wm * 128 + (lane & 15), rB = wn * 64 + (lane & 15), q = lane >> 4;
-  TileLoads t;
-  t.ox = stage_offsets(ldx, x_row0, x_rows, wave, lane);
-  t.oy = stage_offsets(ldy, y_row0, y_rows, wave, lane);
-  t.xbase = uniform_ptr(X + x_row0 * ldx);
-  t.ybase = uniform_ptr(Y + y_row0 * ldy);
-  t.kx = kx;
-  t.ky = ky;
-  t.lds_wave = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)smem + (uint32_t)wave * 32 * 128);
-  // Prologue: stage 0 whole, then the first six loads of stage 1 (the rest
-  // go out in slots 0..1 of stage 0); f0 of stage 0 once stage 0 is visible.
-#pragma unroll
-  for (int f = 0; f < 2 * FILLS; ++f) stage_load(t, 0, f);
-  if (nk > 1)
-#pragma unroll
-    for (int f = 0; f < 6; ++f) stage_load(t, 1, f);
   if (nk > 1) __builtin_amdgcn_s_waitcnt(WAIT_VM(6));
   else __builtin_amdgcn_s_waitcnt(WAIT_VM0);
   __syncthreads();
@@ -314,6 +342,15 @@ __device__ __forceinline__ void gemm_tile(Acc& acc, const u16* __restrict__ X, i
   for (int n = 0; n < NB + NBJ; ++n) read_frag(f0, smem, 0, n, rA, rB, q);
   for (int s = 0; s < nk; ++s) mainloop_stage(acc, f0, f1, s, nk, smem, t, rA, rB, q);
   __builtin_amdgcn_s_waitcnt(WAIT_LGKM0);
+}
+__device__ __forceinline__ void gemm_tile(Acc& acc, const u16* __restrict__ X, int64_t ldx, int64_t kx,
+                                          int64_t x_row0, int64_t x_rows, const u16* __restrict__ Y, int64_t ldy,
+                                          int64_t ky, int64_t y_row0, int64_t y_rows, int64_t K,
+                                          LDS_AS char* smem) {
+  const int nk = (int)(K / BK);
+  const TileLoads t = tile_setup(X, ldx, kx, x_row0, x_rows, Y, ldy, ky, y_row0, y_rows, smem);
+  tile_prologue(t, nk);
+  tile_run(acc, t, nk, smem);
 }
 
 // ---------------------------------------------------------------------------
@@ -353,113 +390,141 @@ __global__ void __launch_bounds__(256) k_prepare_labels(const int64_t* __restric
 // Staging tile for bf16 outputs that leave through LDS: 256 rows x 256
 // columns, rows padded to 528 B (16-B aligned) so that the epilogue's 2-byte
 // writes of lanes 0..31 and 32..63 (rows r and r+4) use different banks.
-constexpr int STAGE_LD = TILE + 8;                    // u16 per staged row
-constexpr int STAGE_LDS = TILE * STAGE_LD * 2;        // 135168 B
+// Per-wave staging of one 16-row block of p~ (16 x 64 bf16, rows padded to
+// 144 B: the 16-bit writes of the four 4-row groups of a wave land 16 banks
+// apart), outside the stage buffers so that the next tile's loads can fill
+// those while this tile's epilogue runs.
+constexpr int PST_LD = 72;                     // u16 per staged row
+constexpr int PST_WAVE = 16 * PST_LD;          // u16 per wave
 
-// Forward tile: z = h W^T + b for 256 rows x 256 vocabulary ids, reduced in
+// Forward tiles: z = h W^T + b for 256 rows x 256 vocabulary ids, reduced in
 // the epilogue to each row's (max, sum exp(z - max)) over each wave's
 // 64-column quarter of the tile (part index NQ*tile + quarter). z never
 // leaves registers. With STORE_P (backward row groups) the tile also writes
-// the bf16 unnormalised softmax exp(z - max_quarter) into p [rows][Vp]; the
-// dlogits pass turns it into G once the row's lse is known, so the logits are
-// computed only once per call. Columns past V count as z = -inf (p = 0); a
-// quarter with no column below V stores max = -inf and sum = 0.
+// the bf16 unnormalised softmax exp(z - max_quarter) into p (K-slabs
+// [Vp/64][ld_part][64]); the dlogits pass turns it into G once the row's lse
+// is known, so the logits are computed only once per call. Columns past V
+// count as z = -inf (p = 0); a quarter with no column below V stores
+// max = -inf and sum = 0.
+//
+// Persistent: each workgroup walks its share of the tiles (walk_tile) and
+// issues the next tile's first loads before this tile's epilogue, so their
+// latency is covered by the epilogue's arithmetic and stores. The epilogue
+// keeps out of the stage buffers: partials go straight from registers to
+// global memory, p~ through a per-wave staging block, and the bias is read
+// into registers at the start of the tile.
 template <bool STORE_P>
 __global__ void __launch_bounds__(NTHREADS, 1)
 k_fwd_tile(const u16* __restrict__ hidden, int64_t ldh, const u16* __restrict__ weight, int64_t ldw,
            const u16* __restrict__ bias, int64_t N, int64_t V, int64_t Vp, int64_t H, int64_t g0, int64_t ld_part,
            int n_mt, int n_vt, float* __restrict__ part_m, float* __restrict__ part_s, u16* __restrict__ p_out) {
-  __shared__ __attribute__((aligned(16))) char smem_raw[STORE_P ? STAGE_LDS : MAINLOOP_LDS];
-  __shared__ float s_bias[TILE];
-  __shared__ float s_red_m[NQ][TILE];
-  __shared__ float s_red_s[NQ][TILE];
+  __shared__ __attribute__((aligned(16))) char smem_raw[MAINLOOP_LDS];
+  __shared__ __attribute__((aligned(16))) u16 s_pst[STORE_P ? 8 * PST_WAVE : 8];
   LDS_AS char* smem = (LDS_AS char*)smem_raw;
-  LDS_AS u16* stage = (LDS_AS u16*)smem_raw;
-
-  int tm, tn;
-  tile_coords(n_mt, n_vt, tm, tn);
-  const int64_t lrow0 = (int64_t)tm * TILE;       // row inside the group (or global row)
-  const int64_t row0 = g0 + lrow0;
-  const int64_t col0 = (int64_t)tn * TILE;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int wm = wave >> 2, wn = wave & 3;
-  // bias, with -inf marking columns past V
-  if (tid < TILE) s_bias[tid] = col0 + tid < V ? (bias != nullptr ? bf2f(bias[col0 + tid]) : 0.f) : -INFINITY;
-
-  Acc acc;
-  gemm_tile(acc, hidden, ldh, BK * 2, row0, N, weight, ldw, BK * 2, col0, V, H, smem);
-  __syncthreads();   // s_bias visible; the staging tile overlays the mainloop's LDS
-
-  // Bias pre-scaled by log2(e): exp(z - m) = exp2(acc*L + b*L - m*L) is one
-  // FMA and one exp2 per element. The four rows r of a row block are reduced
-  // together so their DPP steps interleave instead of waiting on each other.
-  float cbl[NBJ];
+  LDS_AS u16* pst = (LDS_AS u16*)s_pst + (STORE_P ? wave * PST_WAVE : 0);
+  const int nk = (int)(H / BK);
+  int it = 0, tm, tn;
+  if (!walk_tile(n_mt, n_vt, it, tm, tn)) return;
+  TileLoads t = tile_setup(hidden, ldh, BK * 2, g0 + (int64_t)tm * TILE, N, weight, ldw, BK * 2,
+                           (int64_t)tn * TILE, V, smem);
+  tile_prologue(t, nk);
+  for (;;) {
+    const int64_t lrow0 = (int64_t)tm * TILE;       // row inside the group (or global row)
+    const int64_t col0 = (int64_t)tn * TILE;
+    const int ptn = tn;
+    // Bias of this lane's four columns, loaded unconditionally (clamped
+    // address, any valid pointer when there is no bias) and first used after
+    // the K loop: a conditional load would make the compiler wait for it on
+    // the spot, and with it for every direct load in flight.
+    const u16* bsrc = bias != nullptr ? bias : hidden;
+    u16 braw[NBJ];
 #pragma unroll
-  for (int j = 0; j < NBJ; ++j) cbl[j] = s_bias[acc_col(wn, j, lane)] * LOG2E;
-#pragma unroll
-  for (int i = 0; i < NB; ++i) {
-    float m[4];                               // row max of z * log2(e)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      m[r] = -INFINITY;
-#pragma unroll
-      for (int j = 0; j < NBJ; ++j) m[r] = fmaxf(m[r], fmaf(acc.v[i][j][r], LOG2E, cbl[j]));
+    for (int j = 0; j < NBJ; ++j) {
+      const int64_t col = col0 + acc_col(wn, j, lane);
+      braw[j] = bsrc[bias != nullptr ? (col < V ? col : V - 1) : 0];
     }
+    Acc acc;
+    tile_run(acc, t, nk, smem);
+    // Bias pre-scaled by log2(e), -inf past V: exp(z - m) = exp2(acc*L + b*L
+    // - m*L) is one FMA and one exp2 per element.
+    float cbl[NBJ];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) m[r] = fmaxf(m[r], dpp<DPP_XOR1>(m[r]));
-#pragma unroll
-    for (int r = 0; r < 4; ++r) m[r] = fmaxf(m[r], dpp<DPP_XOR2>(m[r]));
-#pragma unroll
-    for (int r = 0; r < 4; ++r) m[r] = fmaxf(m[r], dpp<DPP_HALF_MIRROR>(m[r]));
-#pragma unroll
-    for (int r = 0; r < 4; ++r) m[r] = fmaxf(m[r], dpp<DPP_MIRROR>(m[r]));
-    float sm[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int rl = acc_row(wm, i, r, lane);
-      const float ms = m[r] == -INFINITY ? 0.f : m[r];   // all columns past V: every e = 0
-      sm[r] = 0.f;
-#pragma unroll
-      for (int j = 0; j < NBJ; ++j) {
-        const float e = __builtin_amdgcn_exp2f(fmaf(acc.v[i][j][r], LOG2E, cbl[j] - ms));
-        sm[r] += e;
-        if (STORE_P) stage[rl * STAGE_LD + acc_col(wn, j, lane)] = f2bf(e);
-      }
+    for (int j = 0; j < NBJ; ++j) {
+      const int64_t col = col0 + acc_col(wn, j, lane);
+      cbl[j] = col < V ? (bias != nullptr ? bf2f(braw[j]) * LOG2E : 0.f) : -INFINITY;
+      // pinned here: computed later, the wait for braw would also wait for
+      // the next tile's loads
+      asm volatile("" ::"v"(cbl[j]));
     }
+    const bool more = walk_tile(n_mt, n_vt, ++it, tm, tn);
+    bare_barrier();   // every wave is past its last read of the stage buffers
+    if (more) {
+      t = tile_setup(hidden, ldh, BK * 2, g0 + (int64_t)tm * TILE, N, weight, ldw, BK * 2, (int64_t)tn * TILE, V,
+                     smem);
+      tile_prologue(t, nk);
+    }
+    float* pm = part_m + (int64_t)(NQ * ptn + wn) * ld_part + lrow0 + wm * 128 + 4 * (lane >> 4);
+    float* ps = part_s + (int64_t)(NQ * ptn + wn) * ld_part + lrow0 + wm * 128 + 4 * (lane >> 4);
+    u16* pq = STORE_P ? p_out + ((col0 >> 6) + wn) * ld_part * 64 + (lrow0 + wm * 128) * 64 : nullptr;
+    // The four rows r of a row block are reduced together so their DPP
+    // steps interleave instead of waiting on each other.
 #pragma unroll
-    for (int r = 0; r < 4; ++r) sm[r] += dpp<DPP_XOR1>(sm[r]);
-#pragma unroll
-    for (int r = 0; r < 4; ++r) sm[r] += dpp<DPP_XOR2>(sm[r]);
-#pragma unroll
-    for (int r = 0; r < 4; ++r) sm[r] += dpp<DPP_HALF_MIRROR>(sm[r]);
-#pragma unroll
-    for (int r = 0; r < 4; ++r) sm[r] += dpp<DPP_MIRROR>(sm[r]);
-    if ((lane & 15) == 0) {
+    for (int i = 0; i < NB; ++i) {
+      float m[4];                               // row max of z * log2(e)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int rl = acc_row(wm, i, r, lane);
-        s_red_m[wn][rl] = m[r] * LN2;            // back to natural-log units
-        s_red_s[wn][rl] = sm[r];
+        m[r] = -INFINITY;
+#pragma unroll
+        for (int j = 0; j < NBJ; ++j) m[r] = fmaxf(m[r], fmaf(acc.v[i][j][r], LOG2E, cbl[j]));
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) m[r] = fmaxf(m[r], dpp<DPP_XOR1>(m[r]));
+#pragma unroll
+      for (int r = 0; r < 4; ++r) m[r] = fmaxf(m[r], dpp<DPP_XOR2>(m[r]));
+#pragma unroll
+      for (int r = 0; r < 4; ++r) m[r] = fmaxf(m[r], dpp<DPP_HALF_MIRROR>(m[r]));
+#pragma unroll
+      for (int r = 0; r < 4; ++r) m[r] = fmaxf(m[r], dpp<DPP_MIRROR>(m[r]));
+      float sm[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float ms = m[r] == -INFINITY ? 0.f : m[r];   // all columns past V: every e = 0
+        sm[r] = 0.f;
+#pragma unroll
+        for (int j = 0; j < NBJ; ++j) {
+          const float e = __builtin_amdgcn_exp2f(fmaf(acc.v[i][j][r], LOG2E, cbl[j] - ms));
+          sm[r] += e;
+          if (STORE_P) pst[(4 * (lane >> 4) + r) * PST_LD + j * 16 + (lane & 15)] = f2bf(e);
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sm[r] += dpp<DPP_XOR1>(sm[r]);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sm[r] += dpp<DPP_XOR2>(sm[r]);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sm[r] += dpp<DPP_HALF_MIRROR>(sm[r]);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sm[r] += dpp<DPP_MIRROR>(sm[r]);
+      if ((lane & 15) == 0) {   // rows 4*(lane/16) .. +3 of the block, in natural-log units
+        *(f32x4*)(pm + i * 16) = (f32x4){m[0] * LN2, m[1] * LN2, m[2] * LN2, m[3] * LN2};
+        *(f32x4*)(ps + i * 16) = (f32x4){sm[0], sm[1], sm[2], sm[3]};
+      }
+      if (STORE_P) {
+        // The wave reads back its own staged block (LDS serves a wave's
+        // accesses in order); 16 rows x 128 B, 8 lanes per row, streamed out.
+        asm volatile("" ::: "memory");
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+          const int id = k * 64 + lane, rr = id >> 3, ch = id & 7;
+          const u32x4 val = *(const LDS_AS u32x4*)(pst + rr * PST_LD + ch * 8);
+          __builtin_nontemporal_store(val, (u32x4*)(pq + (i * 16 + rr) * 64 + ch * 8));
+        }
+        asm volatile("" ::: "memory");
       }
     }
-  }
-  __syncthreads();
-  for (int idx = tid; idx < NQ * TILE; idx += NTHREADS) {
-    const int h = idx / TILE, row = idx % TILE;
-    part_m[(int64_t)(NQ * tn + h) * ld_part + lrow0 + row] = s_red_m[h][row];
-    part_s[(int64_t)(NQ * tn + h) * ld_part + lrow0 + row] = s_red_s[h][row];
-  }
-  if (STORE_P) {
-    // 256 rows x 32 sixteen-byte chunks; 32 lanes cover one row, 8 lanes
-    // one quarter (128 B of K-slab col0/64 + quarter).
-    u16* pq = p_out + (col0 >> 6) * ld_part * 64;
-#pragma unroll 4
-    for (int it = 0; it < TILE * TILE / 8 / NTHREADS; ++it) {
-      const int id = it * NTHREADS + tid;
-      const int row = id >> 5, ch = id & 31;
-      const u32x4 val = *(const LDS_AS u32x4*)(stage + row * STAGE_LD + ch * 8);
-      __builtin_nontemporal_store(val, (u32x4*)(pq + ((ch >> 3) * ld_part + lrow0 + row) * 64 + (ch & 7) * 8));
-    }
+    if (!more) break;
   }
 }
 
@@ -776,11 +841,53 @@ k_gemm_grad_hidden(const u16* __restrict__ dlog, const u16* __restrict__ wT, int
     }
 }
 
+// gw rows of one tile (+)= the accumulators: base points at column
+// (col0 + wn*64 + lane%16) of row 0; rows past V are skipped when CHECK. The
+// read-modify-write goes two 16-row blocks at a time with all their reads
+// issued before the adds and stores, so 32 reads per lane are in flight.
+template <bool CHECK>
+__device__ __forceinline__ void gw_update(const Acc& acc, float* __restrict__ base, int64_t row0, int64_t H,
+                                          int64_t V, int wm, int lane, int first) {
+  if (first) {
+#pragma unroll
+    for (int i = 0; i < NB; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int64_t v = row0 + acc_row(wm, i, r, lane);
+        if (CHECK && v >= V) continue;
+        float* dst = base + v * H;
+#pragma unroll
+        for (int j = 0; j < NBJ; ++j) dst[j * 16] = acc.v[i][j][r];
+      }
+    return;
+  }
+#pragma unroll
+  for (int i0 = 0; i0 < NB; i0 += 2) {
+    float old[2][4][NBJ];
+#pragma unroll
+    for (int di = 0; di < 2; ++di)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int64_t v = row0 + acc_row(wm, i0 + di, r, lane);
+        const float* src = base + (CHECK && v >= V ? 0 : v) * H;
+#pragma unroll
+        for (int j = 0; j < NBJ; ++j) old[di][r][j] = src[j * 16];
+      }
+#pragma unroll
+    for (int di = 0; di < 2; ++di)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int64_t v = row0 + acc_row(wm, i0 + di, r, lane);
+        if (CHECK && v >= V) continue;
+        float* dst = base + v * H;
+#pragma unroll
+        for (int j = 0; j < NBJ; ++j) dst[j * 16] = old[di][r][j] + acc.v[i0 + di][j][r];
+      }
+  }
+}
+
 // grad_weight FP32 accumulation for one group: gw[v][:] (+)= dlogT * (h^T)^T over K = G;
 // dlogT is stored as K-slabs [G/64][Vp][64], h^T as [G/64][H][64].
-// The read-modify-write goes two 16-row blocks at a time with all their
-// reads issued before the adds and stores, so 32 reads per thread are in
-// flight together.
 __global__ void __launch_bounds__(NTHREADS, 1)
 k_gemm_grad_weight(const u16* __restrict__ dlogT, const u16* __restrict__ hT, int64_t G, int64_t H,
                    int64_t V, int64_t Vp, int n_mt, int n_nt, int first, float* __restrict__ gw_f32) {
@@ -793,31 +900,12 @@ k_gemm_grad_weight(const u16* __restrict__ dlogT, const u16* __restrict__ hT, in
   const int wm = wave >> 2, wn = wave & 3;
   Acc acc;
   gemm_tile(acc, dlogT, BK, Vp * BK * 2, row0, Vp, hT, BK, H * BK * 2, col0, H, G, smem);
-#pragma unroll
-  for (int i0 = 0; i0 < NB; i0 += 2) {
-    float old[2][4][NBJ];
-#pragma unroll
-    for (int di = 0; di < 2; ++di)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int64_t v = row0 + acc_row(wm, i0 + di, r, lane);
-#pragma unroll
-        for (int j = 0; j < NBJ; ++j) {
-          const int64_t col = col0 + acc_col(wn, j, lane);
-          old[di][r][j] = (!first && v < V && col < H) ? gw_f32[v * H + col] : 0.f;
-        }
-      }
-#pragma unroll
-    for (int di = 0; di < 2; ++di)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int64_t v = row0 + acc_row(wm, i0 + di, r, lane);
-#pragma unroll
-        for (int j = 0; j < NBJ; ++j) {
-          const int64_t col = col0 + acc_col(wn, j, lane);
-          if (v < V && col < H) gw_f32[v * H + col] = old[di][r][j] + acc.v[i0 + di][j][r];
-        }
-      }
+  // H % 64 == 0: a wave's 64 columns are all below H or all past it; only
+  // the last vocabulary tile has rows past V.
+  if (col0 + wn * 64 < H) {
+    float* base = gw_f32 + col0 + wn * 64 + (lane & 15);
+    if (row0 + TILE <= V) gw_update<false>(acc, base, row0, H, V, wm, lane, first);
+    else gw_update<true>(acc, base, row0, H, V, wm, lane, first);
   }
 }
 
@@ -865,10 +953,29 @@ hipError_t launch_prepare_labels(const int64_t* labels, int64_t N, int64_t Np, i
   return hipGetLastError();
 }
 
+// Grid of a persistent tile kernel: one workgroup per CU (the kernels' LDS
+// admits no second one), a multiple of 8 so that blockIdx % 8 names the XCD,
+// and no more than the tiles need.
+static int persistent_grid(int64_t ntiles) {
+  static int cu_count[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+  if (cu_count[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 8) n = 8;
+    cu_count[dev] = n;
+  }
+  const int64_t per_xcd = (ntiles + 7) / 8;
+  const int64_t nx = cu_count[dev] / 8 < per_xcd ? cu_count[dev] / 8 : per_xcd;
+  return (int)(8 * nx);
+}
+
 hipError_t launch_fwd_tiles(const Shapes& s, const void* hidden, const void* weight, const void* bias, int64_t g0,
                             int64_t rows, float* part_m, float* part_s, void* p_out, hipStream_t st) {
   const int n_mt = (int)(rows / TILE), n_vt = (int)(s.Vp / TILE);
-  const dim3 grid((unsigned)(n_mt * n_vt)), block(NTHREADS);
+  const int nb = persistent_grid((int64_t)n_mt * n_vt);
+  if (nb == 0) return hipSuccess;
+  const dim3 grid((unsigned)nb), block(NTHREADS);
   if (p_out)
     hipLaunchKernelGGL(k_fwd_tile<true>, grid, block, 0, st, (const u16*)hidden, s.ldh, (const u16*)weight, s.ldw,
                        (const u16*)bias, s.N, s.V, s.Vp, s.H, g0, rows, n_mt, n_vt, part_m, part_s, (u16*)p_out);
