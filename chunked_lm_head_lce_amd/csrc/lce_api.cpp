@@ -24,7 +24,7 @@ struct Layout {
   // forward
   size_t label32 = 0, n_valid = 0, status = 0, zlab = 0, lse = 0, part_m = 0, part_s = 0, chunk_acc = 0;
   // backward
-  size_t wT = 0, hT = 0, dlog = 0, dlogT = 0, gw_f32 = 0, gb_f32 = 0;
+  size_t wT = 0, htail = 0, dlog = 0, gw_f32 = 0, gb_f32 = 0;
   size_t total = 0;
 };
 
@@ -92,11 +92,11 @@ Layout make_layout(const lce_problem* p, int kind) {
   L.chunk_acc = take((size_t)n_chunks(p) * 8);
   if (bwd) {
     const int64_t G = group_rows(p, s);
-    // the four backward operands, each stored as K-slabs [K/64][rows][64]
+    // W^T and the group's p~ / G, both stored as K-slabs [K/64][rows][64];
+    // htail holds the last partial 64 rows of a group (zero past N)
     L.wT = take((size_t)s.H * s.Vp * 2);
-    L.hT = take((size_t)s.H * G * 2);
+    L.htail = take((size_t)64 * s.ldh * 2);
     L.dlog = take((size_t)G * s.Vp * 2);
-    L.dlogT = take((size_t)s.Vp * G * 2);
     L.gb_f32 = take((size_t)s.Vp * 4);
     if (kind == LCE_WS_BACKWARD) L.gw_f32 = take((size_t)s.V * s.H * 4);
   }
@@ -330,12 +330,11 @@ int lce_forward_backward_ex(const lce_problem* p, const void* hidden, const void
     if (st != LCE_OK) return st;
     // Row groups: the logits of a group are computed once; the tiles leave
     // exp(z - max_quarter) in dlog, the group's lse follows, and the dlogits
-    // pass turns dlog into G (and G^T) for the two gradient products.
+    // pass turns dlog into G in place for the two gradient products.
     const int64_t G = group_rows(p, s);
     void* wT = ws + c.L.wT;
-    void* hT = ws + c.L.hT;
+    void* htail = ws + c.L.htail;
     void* dlog = ws + c.L.dlog;
-    void* dlogT = ws + c.L.dlogT;
     const int is_mean = p->reduction == LCE_REDUCTION_MEAN;
     const bool any_grad = need_gh || need_gw || need_gb;
     if (need_gh)
@@ -349,17 +348,14 @@ int lce_forward_backward_ex(const lce_problem* p, const void* hidden, const void
       if (!any_grad) continue;
       LCE_LAUNCH(tr, LCE_K_BWD_DLOGITS, rows_valid, s.V, 0,
                  lce::launch_dlogits(s, c.label32, c.part_m, c.lse_ws, c.n_valid, grad_scale, is_mean, row_scale, g0,
-                                     Gc, dlog, need_gh ? 1 : 0, need_gw ? dlogT : nullptr, need_gb ? gb : nullptr,
-                                     stream));
+                                     Gc, dlog, (need_gh || need_gw) ? 1 : 0, need_gb ? gb : nullptr, stream));
       if (need_gh)
         LCE_LAUNCH(tr, LCE_K_GRAD_HIDDEN, rows_valid, s.H, s.V,
                    lce::launch_grad_hidden(s, dlog, wT, g0, Gc, grad_hidden, stream));
-      if (need_gw) {
-        LCE_LAUNCH(tr, LCE_K_TRANSPOSE, 0, 0, 0,
-                   lce::launch_transpose(hidden, s.ldh, g0, rows_valid, s.H, hT, Gc, stream));
+      if (need_gw)
         LCE_LAUNCH(tr, LCE_K_GRAD_WEIGHT, s.V, s.H, rows_valid,
-                   lce::launch_grad_weight(s, dlogT, hT, Gc, (g0 == 0 && !accumulate) ? 1 : 0, gw, stream));
-      }
+                   lce::launch_grad_weight(s, dlog, Gc, hidden, g0, rows_valid, htail,
+                                           (g0 == 0 && !accumulate) ? 1 : 0, gw, stream));
     }
   }
   if (need_gw && grad_weight)

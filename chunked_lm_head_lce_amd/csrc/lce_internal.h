@@ -40,22 +40,23 @@ hipError_t launch_finalize_loss(const double* chunk_acc, int64_t T, const unsign
 hipError_t launch_transpose(const void* in, int64_t ld_in, int64_t r0, int64_t R_valid, int64_t C, void* out,
                             int64_t R_pad, hipStream_t st);
 // dlogits of one row group from the stored exp(z - max_quarter) in dlog
-// (K-slabs [Vp/64][G][64]): G in place (when write_dlog), G^T into dlogT as
-// K-slabs [G/64][Vp][64] (when non-null), column sums into gb_f32 (when
-// non-null); row i also scaled by row_scale[i] when row_scale is non-null.
+// (K-slabs [Vp/64][G][64]): G in place (when write_dlog), column sums into
+// gb_f32 (when non-null); row i also scaled by row_scale[i] when row_scale
+// is non-null.
 hipError_t launch_dlogits(const Shapes& s, const int32_t* label32, const float* part_m, const float* lse_ws,
                           const unsigned long long* n_valid, float grad_scale, int is_mean, const float* row_scale,
-                          int64_t g0, int64_t G, void* dlog, int write_dlog, void* dlogT, float* gb_f32,
-                          hipStream_t st);
+                          int64_t g0, int64_t G, void* dlog, int write_dlog, float* gb_f32, hipStream_t st);
 // data[k] *= *scale (bf16 or f32 elements).
 hipError_t launch_scale(void* data, bool f32, int64_t n, const float* scale, hipStream_t st);
 // grad_hidden rows [g0, g0 + G) = dlog * wT^T over K = Vp (dlog: K-slabs
 // [Vp/64][G][64], wT: [Vp/64][H][64]).
 hipError_t launch_grad_hidden(const Shapes& s, const void* dlog, const void* wT, int64_t g0, int64_t G,
                               void* grad_hidden, hipStream_t st);
-// gw (+)= dlogT * hT^T over K = G (dlogT: K-slabs [G/64][Vp][64], hT: [G/64][H][64]).
-hipError_t launch_grad_weight(const Shapes& s, const void* dlogT, const void* hT, int64_t G, int first,
-                              float* gw_f32, hipStream_t st);
+// gw (+)= sum over the group's rows i < rows_valid of G[i][v] h[g0 + i][:]
+// (dlog: K-slabs [Vp/64][G][64] holding G; hidden row-major [N][ldh]).
+// htail: 64 * ldh elements of scratch for the group's last partial 64 rows.
+hipError_t launch_grad_weight(const Shapes& s, const void* dlog, int64_t G, const void* hidden, int64_t g0,
+                              int64_t rows_valid, void* htail, int first, float* gw_f32, hipStream_t st);
 hipError_t launch_cast(const float* in, void* out, int64_t n, hipStream_t st);
 
 }  // namespace lce

@@ -196,6 +196,8 @@ struct TileLoads {
   const void* xbase;
   const void* ybase;
   int64_t kx, ky;
+  const void* ytail;     // Y stage s_tail comes from here instead (TAIL loads only)
+  int s_tail;
   StageOffsets ox, oy;
   uint32_t lds_wave;     // LDS byte address of this wave's 32 rows in stage buffer 0
 };
@@ -208,12 +210,17 @@ __device__ __forceinline__ const void* uniform_ptr(const void* p) {
 }
 
 // Issues load f (0..7) of stage s: f < 4 fill X rows, f >= 4 fill Y rows.
+// With TAIL, Y stage t.s_tail is read from t.ytail (same offsets).
+template <bool TAIL>
 __device__ __forceinline__ void stage_load(const TileLoads& t, int s, int f) {
   const uint32_t buf = t.lds_wave + (uint32_t)((s & 1) * STAGE);
-  if (f < FILLS)
+  if (f < FILLS) {
     lds_dma16((const char*)t.xbase + s * t.kx, t.ox.off[f], buf + f * 1024);
-  else
-    lds_dma16((const char*)t.ybase + s * t.ky, t.oy.off[f - FILLS], buf + OPERAND_STAGE + (f - FILLS) * 1024);
+  } else {
+    const char* yb = (const char*)t.ybase + s * t.ky;
+    if (TAIL && s == t.s_tail) yb = (const char*)t.ytail;
+    lds_dma16(yb, t.oy.off[f - FILLS], buf + OPERAND_STAGE + (f - FILLS) * 1024);
+  }
 }
 
 #define FENCE() __builtin_amdgcn_sched_barrier(0)
@@ -230,10 +237,52 @@ struct Frags {
 };
 // Fragment read n (0..11) of sub-step `sub` (0, 1) of the stage in `buf`: B
 // blocks first (every MFMA of the first row block needs all of them), then A.
-__device__ __forceinline__ void read_frag(Frags& f, const LDS_AS char* buf, int sub, int n, int rA, int rB, int q) {
-  if (n < NBJ) f.b[n] = frag(buf + OPERAND_STAGE, rB + n * 16, sub * 4 + q);
-  else f.a[n - NBJ] = frag(buf, rA + (n - NBJ) * 16, sub * 4 + q);
+// FragK: both operands K-contiguous in LDS (the layout above).
+struct FragK {
+  int rA, rB, q;
+  __device__ __forceinline__ FragK(int wave, int lane)
+      : rA((wave >> 2) * 128 + (lane & 15)), rB((wave & 3) * 64 + (lane & 15)), q(lane >> 4) {}
+  __device__ __forceinline__ void read(Frags& f, const LDS_AS char* buf, int sub, int n) const {
+    if (n < NBJ) f.b[n] = frag(buf + OPERAND_STAGE, rB + n * 16, sub * 4 + q);
+    else f.a[n - NBJ] = frag(buf, rA + (n - NBJ) * 16, sub * 4 + q);
+  }
+};
+
+// K-major stage layout, for operands whose rows run along K in memory: tile
+// [64 k][256 m] bf16, 512 B per k row, the 16-byte m-chunk c of row k at
+// chunk slot c ^ (2 tr_swz(k)). Fragments come from ds_read_b64_tr_b16, which
+// within each 16-lane group hands lane i element i % 4 of the 8-byte reads of
+// lanes i/4, i/4 + 4, i/4 + 8 and i/4 + 12. So lane j of group q points at
+// row k0 + j/4, m = m0 + 4 (j % 4): lane i then holds m0 + i for k0 .. k0+3,
+// half of its MFMA operand (k0 = 8q, then 8q + 4). One read of half a wave
+// (two groups) touches rows k0 + 0..3 and k0 + 8..11; tr_swz gives those
+// eight rows eight different 32-byte bank groups.
+constexpr int TR_ROW = 512;
+__device__ __forceinline__ int tr_swz(int k) { return (k & 3) | (((k >> 3) & 1) << 2); }
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+__device__ __forceinline__ bf16x8 frag_tr(const LDS_AS char* p) {
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4*)p);
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4*)(p + 4 * TR_ROW));
+  return __builtin_bit_cast(bf16x8, (s16x8)__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
+// FragT: both operands K-major; per-lane byte offsets of the 12 fragments in
+// a stage (sub-step 0, first half), fixed for the whole K loop.
+struct FragT {
+  uint32_t a[NB], b[NBJ];
+  __device__ __forceinline__ FragT(int wave, int lane) {
+    const int q = lane >> 4, j = lane & 15, t = tr_swz(8 * q + (j >> 2));
+    const uint32_t row = (uint32_t)(8 * q + (j >> 2)) * TR_ROW + 8 * (j & 3);
+#pragma unroll
+    for (int i = 0; i < NB; ++i) a[i] = row + 32 * (((wave >> 2) * NB + i) ^ t);
+#pragma unroll
+    for (int i = 0; i < NBJ; ++i) b[i] = OPERAND_STAGE + row + 32 * (((wave & 3) * NBJ + i) ^ t);
+  }
+  __device__ __forceinline__ void read(Frags& f, const LDS_AS char* buf, int sub, int n) const {
+    if (n < NBJ) f.b[n] = frag_tr(buf + b[n] + sub * 32 * TR_ROW);
+    else f.a[n - NBJ] = frag_tr(buf + a[n - NBJ] + sub * 32 * TR_ROW);
+  }
+};
 
 // Schedule of one 64-deep stage s, in 16 slots of 4 MFMAs (slots 0..7:
 // sub-step 0 from fragment set f0, slots 8..15: sub-step 1 from f1), two
@@ -251,8 +300,9 @@ __device__ __forceinline__ void read_frag(Frags& f, const LDS_AS char* buf, int 
 // slot was slower here.)
 // At entry: f0 holds stage s sub-step 0; loads 0..5 of stage s+1 went out in
 // the previous stage (slots 10..15), loads 6..7 go out in slots 0..1.
+template <bool TAIL, class FS>
 __device__ __forceinline__ void mainloop_stage(Acc& acc, Frags& f0, Frags& f1, int s, int nk, LDS_AS char* smem,
-                                               const TileLoads& t, int rA, int rB, int q) {
+                                               const TileLoads& t, const FS& fs) {
   LDS_AS char* cur = smem + (s & 1) * STAGE;
   LDS_AS char* nxt = smem + ((s + 1) & 1) * STAGE;
 #pragma unroll
@@ -269,19 +319,19 @@ __device__ __forceinline__ void mainloop_stage(Acc& acc, Frags& f0, Frags& f1, i
     acc.v[i][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.a[i], f.b[1], acc.v[i][1], 0, 0, 0);
     FENCE();
     if (slot < 2) {
-      if (s + 1 < nk) stage_load(t, s + 1, 6 + slot);
+      if (s + 1 < nk) stage_load<TAIL>(t, s + 1, 6 + slot);
     } else if (slot >= 10) {
-      if (s + 2 < nk) stage_load(t, s + 2, slot - 10);
+      if (s + 2 < nk) stage_load<TAIL>(t, s + 2, slot - 10);
     }
     // fragment reads: f1 of this stage in slots 0..5, f0 of the next in 10..15
-    if (slot < 6) read_frag(f1, cur, 1, 2 * slot, rA, rB, q);
-    else if (slot >= 10) read_frag(f0, nxt, 0, 2 * (slot - 10), rA, rB, q);
+    if (slot < 6) fs.read(f1, cur, 1, 2 * slot);
+    else if (slot >= 10) fs.read(f0, nxt, 0, 2 * (slot - 10));
     FENCE();
     acc.v[i][2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.a[i], f.b[2], acc.v[i][2], 0, 0, 0);
     acc.v[i][3] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.a[i], f.b[3], acc.v[i][3], 0, 0, 0);
     FENCE();
-    if (slot < 6) read_frag(f1, cur, 1, 2 * slot + 1, rA, rB, q);
-    else if (slot >= 10) read_frag(f0, nxt, 0, 2 * (slot - 10) + 1, rA, rB, q);
+    if (slot < 6) fs.read(f1, cur, 1, 2 * slot + 1);
+    else if (slot >= 10) fs.read(f0, nxt, 0, 2 * (slot - 10) + 1);
   }
   FENCE();
 }
@@ -313,34 +363,37 @@ __device__ __forceinline__ TileLoads tile_setup(const u16* __restrict__ X, int64
   t.ybase = uniform_ptr(Y + y_row0 * ldy);
   t.kx = kx;
   t.ky = ky;
+  t.ytail = nullptr;
+  t.s_tail = -1;
   t.lds_wave = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)smem + (uint32_t)wave * 32 * 128);
   return t;
 }
+template <bool TAIL = false>
 __device__ __forceinline__ void tile_prologue(const TileLoads& t, int nk) {
 #pragma unroll
-  for (int f = 0; f < 2 * FILLS; ++f) stage_load(t, 0, f);
+  for (int f = 0; f < 2 * FILLS; ++f) stage_load<TAIL>(t, 0, f);
   if (nk > 1)
 #pragma unroll
-    for (int f = 0; f < 6; ++f) stage_load(t, 1, f);
+    for (int f = 0; f < 6; ++f) stage_load<TAIL>(t, 1, f);
 }
+template <bool TAIL = false, class FS = FragK>
 __device__ __forceinline__ void tile_run(Acc& acc, const TileLoads& t, int nk, LDS_AS char* smem) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave >> 2, wn = wave & 3;
 #pragma unroll
   for (int i = 0; i < NB; ++i)
 #pragma unroll
     for (int j = 0; j < NBJ; ++j)
 #pragma unroll
       for (int r = 0; r < 4; ++r) acc.v[i][j][r] = 0.f;
-  const int rA = wm * 128 + (lane & 15), rB = wn * 64 + (lane & 15), q = lane >> 4;
+  const FS fs(wave, lane);
   if (nk > 1) __builtin_amdgcn_s_waitcnt(WAIT_VM(6));
   else __builtin_amdgcn_s_waitcnt(WAIT_VM0);
   __syncthreads();
   Frags f0, f1;
 #pragma unroll
-  for (int n = 0; n < NB + NBJ; ++n) read_frag(f0, smem, 0, n, rA, rB, q);
-  for (int s = 0; s < nk; ++s) mainloop_stage(acc, f0, f1, s, nk, smem, t, rA, rB, q);
+  for (int n = 0; n < NB + NBJ; ++n) fs.read(f0, smem, 0, n);
+  for (int s = 0; s < nk; ++s) mainloop_stage<TAIL>(acc, f0, f1, s, nk, smem, t, fs);
   __builtin_amdgcn_s_waitcnt(WAIT_LGKM0);
 }
 __device__ __forceinline__ void gemm_tile(Acc& acc, const u16* __restrict__ X, int64_t ldx, int64_t kx,
@@ -691,26 +744,20 @@ __global__ void __launch_bounds__(256) k_transpose(const u16* __restrict__ in, i
 // stored unnormalised softmax p~ = exp(z - max_q) (bf16, written by the
 // forward tile, max_q over the 64-column quarter q of the tile):
 // G = s valid (p~ exp(max_q - lse) - [j == y]). G
-// overwrites p~ in dlog (K-slabs [Vp/64][G][64]) when `write_dlog`, and goes
-// to dlogT (K-slabs [G/64][Vp][64]) when non-null; its column sums
-// go into the FP32 bias gradient. Each thread owns 8 x 8 blocks: 8 rows of
-// one 16-byte column chunk, all 8 loads issued before any use, transposed in
-// registers and staged through LDS for dlogT. 72 KB of LDS: two blocks per CU.
-// G and G^T are written with non-temporal stores (read once, by the next
-// product kernel), which keep them from evicting operand lines from L2.
+// overwrites p~ in dlog (K-slabs [Vp/64][G][64]) when `write_dlog` (both
+// gradient products read it there); its column sums go into the FP32 bias
+// gradient. Each thread owns 8 x 8 blocks: 8 rows of one 16-byte column
+// chunk, all 8 loads issued before any use. G is written with non-temporal
+// stores (read by the next product kernels, not by this one), which keep it
+// from evicting operand lines from L2.
 constexpr int DL_ROWS = 128;
-__device__ __forceinline__ int tswz(int col) { return (col >> 3) & 15; }
 
-__global__ void __launch_bounds__(256, 2)
-k_dlogits_from_p(u16* __restrict__ dlog, u16* __restrict__ dlogT, const float* __restrict__ part_m,
+__global__ void __launch_bounds__(256)
+k_dlogits_from_p(u16* __restrict__ dlog, const float* __restrict__ part_m,
                  const int32_t* __restrict__ label32, const float* __restrict__ lse_ws,
                  const unsigned long long* __restrict__ n_valid, float grad_scale, int is_mean,
                  const float* __restrict__ row_scale, int64_t V, int64_t Vp, int64_t g0, int64_t G, int write_dlog,
                  float* __restrict__ gb_f32) {
-  // transposed staging [256 cols][128 rows] bf16; the 16-byte row chunk c of
-  // column col is stored at slot c ^ tswz(col): conflict-free for the column
-  // writes (16 lanes, 16 different columns) and for the chunk reads.
-  __shared__ __attribute__((aligned(16))) u16 tst[TILE * DL_ROWS];
   __shared__ float s_f[NQ][DL_ROWS];
   __shared__ int s_lab[DL_ROWS];
   __shared__ float s_hot[DL_ROWS];
@@ -777,16 +824,6 @@ k_dlogits_from_p(u16* __restrict__ dlog, u16* __restrict__ dlogT, const float* _
         __builtin_nontemporal_store(o, (u32x4*)(src + r * 64));
       }
     }
-    if (dlogT) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int col = cb * 8 + e;
-        u32x4 o;
-#pragma unroll
-        for (int w = 0; w < 4; ++w) o[w] = (uint32_t)f2bf(d[2 * w][e]) | ((uint32_t)f2bf(d[2 * w + 1][e]) << 16);
-        *(LDS_AS u32x4*)((LDS_AS u16*)tst + col * DL_ROWS + ((rb ^ tswz(col)) << 3)) = o;
-      }
-    }
   }
   if (gb_f32) {
 #pragma unroll
@@ -798,18 +835,6 @@ k_dlogits_from_p(u16* __restrict__ dlog, u16* __restrict__ dlogT, const float* _
 #pragma unroll
     for (int k = 0; k < 8; ++k) sum += s_gb[k][tid];
     atomicAdd(gb_f32 + col0 + tid, sum);
-  }
-  if (dlogT) {
-    // 256 columns x 16 sixteen-byte row chunks; 16 lanes cover one column,
-    // 8 lanes its 128 B in one K-slab.
-#pragma unroll 4
-    for (int it = 0; it < TILE * DL_ROWS / 8 / 256; ++it) {
-      const int id = it * 256 + tid;
-      const int col = id >> 4, ch = id & 15;
-      const u32x4 v = *(const LDS_AS u32x4*)((LDS_AS u16*)tst + col * DL_ROWS + ((ch ^ tswz(col)) << 3));
-      __builtin_nontemporal_store(
-          v, (u32x4*)(dlogT + (((lrow0 >> 6) + (ch >> 3)) * Vp + col0 + col) * 64 + (ch & 7) * 8));
-    }
   }
 }
 
@@ -886,26 +911,67 @@ __device__ __forceinline__ void gw_update(const Acc& acc, float* __restrict__ ba
   }
 }
 
-// grad_weight FP32 accumulation for one group: gw[v][:] (+)= dlogT * (h^T)^T over K = G;
-// dlogT is stored as K-slabs [G/64][Vp][64], h^T as [G/64][H][64].
+// DMA offsets of the K-major layout: fill b of a wave covers rows
+// k = 8 wave + 2b + lane/32, lane % 32 the 16-byte slot p, which holds m-chunk
+// c = p ^ (2 tr_swz(k)).
+__device__ __forceinline__ void tr_slot(int wave, int lane, int b, int& k, int& c) {
+  k = wave * 8 + 2 * b + (lane >> 5);
+  c = (lane & 31) ^ (2 * tr_swz(k));
+}
+
+// grad_weight FP32 accumulation for one group: gw[v][:] (+)= sum_i G[i][v] h[i][:]
+// over the group's rows, read as they are stored (K-major for this product):
+// G as K-slabs [Vp/64][slab_rows][64], h row-major [.][ldh] from row g0.
+// Stage s_tail (the group's last, partial 64 rows) takes h from htail
+// ([64][ldh], zero past N) so that no row past N is read.
 __global__ void __launch_bounds__(NTHREADS, 1)
-k_gemm_grad_weight(const u16* __restrict__ dlogT, const u16* __restrict__ hT, int64_t G, int64_t H,
-                   int64_t V, int64_t Vp, int n_mt, int n_nt, int first, float* __restrict__ gw_f32) {
+k_gemm_grad_weight(const u16* __restrict__ G, int64_t slab_rows, const u16* __restrict__ hidden, int64_t ldh,
+                   int64_t g0, const u16* __restrict__ htail, int s_tail, int nk, int64_t H, int64_t V,
+                   int n_mt, int n_nt, int first, float* __restrict__ gw_f32) {
   __shared__ __attribute__((aligned(16))) char smem_raw[MAINLOOP_LDS];
   LDS_AS char* smem = (LDS_AS char*)smem_raw;
   int tm, tn;
   tile_coords(n_mt, n_nt, tm, tn);
   const int64_t row0 = (int64_t)tm * TILE, col0 = (int64_t)tn * TILE;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 2, wn = wave & 3;
+  TileLoads t;
+#pragma unroll
+  for (int b = 0; b < FILLS; ++b) {
+    int k, c;
+    tr_slot(wave, lane, b, k, c);
+    t.ox.off[b] = (uint32_t)((((int64_t)(c >> 3) * slab_rows + k) * 64 + (c & 7) * 8) * 2);
+    const int64_t col = col0 + 8 * c <= H - 8 ? 8 * c : H - 8 - col0;   // past H: any column in range
+    t.oy.off[b] = (uint32_t)(((int64_t)k * ldh + col) * 2);
+  }
+  t.xbase = uniform_ptr(G + (row0 >> 6) * slab_rows * 64);
+  t.ybase = uniform_ptr(hidden + g0 * ldh + col0);
+  t.kx = 64 * 64 * 2;
+  t.ky = 64 * ldh * 2;
+  t.ytail = htail != nullptr ? uniform_ptr(htail + col0) : nullptr;
+  t.s_tail = s_tail;
+  t.lds_wave = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)smem + (uint32_t)wave * 32 * 128);
   Acc acc;
-  gemm_tile(acc, dlogT, BK, Vp * BK * 2, row0, Vp, hT, BK, H * BK * 2, col0, H, G, smem);
+  tile_prologue<true>(t, nk);
+  tile_run<true, FragT>(acc, t, nk, smem);
   // H % 64 == 0: a wave's 64 columns are all below H or all past it; only
   // the last vocabulary tile has rows past V.
   if (col0 + wn * 64 < H) {
     float* base = gw_f32 + col0 + wn * 64 + (lane & 15);
     if (row0 + TILE <= V) gw_update<false>(acc, base, row0, H, V, wm, lane, first);
     else gw_update<true>(acc, base, row0, H, V, wm, lane, first);
+  }
+}
+
+// htail [64][ld] = rows r0 .. r0 + 63 of in [.][ld] (first C columns), zero
+// for rows at or past N.
+__global__ void __launch_bounds__(256) k_tail_rows(const u16* __restrict__ in, int64_t ld, int64_t r0, int64_t N,
+                                                    int64_t C, u16* __restrict__ out) {
+  const int64_t n = 64 * C;
+  for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < n; e += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t r = e / C, c = e - r * C;
+    out[r * ld + c] = r0 + r < N ? in[(r0 + r) * ld + c] : (u16)0;
   }
 }
 
@@ -1022,10 +1088,9 @@ hipError_t launch_transpose(const void* in, int64_t ld_in, int64_t r0, int64_t R
 
 hipError_t launch_dlogits(const Shapes& s, const int32_t* label32, const float* part_m, const float* lse_ws,
                           const unsigned long long* n_valid, float grad_scale, int is_mean, const float* row_scale,
-                          int64_t g0, int64_t G, void* dlog, int write_dlog, void* dlogT, float* gb_f32,
-                          hipStream_t st) {
+                          int64_t g0, int64_t G, void* dlog, int write_dlog, float* gb_f32, hipStream_t st) {
   const int n_mt = (int)(G / DL_ROWS), n_vt = (int)(s.Vp / TILE);
-  hipLaunchKernelGGL(k_dlogits_from_p, dim3((unsigned)(n_mt * n_vt)), dim3(256), 0, st, (u16*)dlog, (u16*)dlogT,
+  hipLaunchKernelGGL(k_dlogits_from_p, dim3((unsigned)(n_mt * n_vt)), dim3(256), 0, st, (u16*)dlog,
                      part_m, label32, lse_ws, n_valid, grad_scale, is_mean, row_scale, s.V, s.Vp, g0, G, write_dlog,
                      gb_f32);
   return hipGetLastError();
@@ -1039,11 +1104,22 @@ hipError_t launch_grad_hidden(const Shapes& s, const void* dlog, const void* wT,
   return hipGetLastError();
 }
 
-hipError_t launch_grad_weight(const Shapes& s, const void* dlogT, const void* hT, int64_t G, int first,
-                              float* gw_f32, hipStream_t st) {
+hipError_t launch_grad_weight(const Shapes& s, const void* dlog, int64_t G, const void* hidden, int64_t g0,
+                              int64_t rows_valid, void* htail, int first, float* gw_f32, hipStream_t st) {
   const int n_mt = (int)(s.Vp / TILE), n_nt = (int)((s.H + TILE - 1) / TILE);
-  hipLaunchKernelGGL(k_gemm_grad_weight, dim3((unsigned)(n_mt * n_nt)), dim3(NTHREADS), 0, st,
-                     (const u16*)dlogT, (const u16*)hT, G, s.H, s.V, s.Vp, n_mt, n_nt, first, gw_f32);
+  const int nk = (int)((rows_valid + 63) / 64);
+  int s_tail = -1;
+  if (rows_valid % 64 != 0) {
+    s_tail = (int)(rows_valid / 64);
+    const int64_t n = 64 * s.H;
+    hipLaunchKernelGGL(k_tail_rows, dim3((unsigned)((n + 255) / 256 < 1024 ? (n + 255) / 256 : 1024)), dim3(256), 0,
+                       st, (const u16*)hidden, s.ldh, g0 + 64 * (int64_t)s_tail, s.N, s.H, (u16*)htail);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(k_gemm_grad_weight, dim3((unsigned)(n_mt * n_nt)), dim3(NTHREADS), 0, st, (const u16*)dlog, G,
+                     (const u16*)hidden, s.ldh, g0, s_tail >= 0 ? (const u16*)htail : nullptr, s_tail, nk, s.H, s.V,
+                     n_mt, n_nt, first, gw_f32);
   return hipGetLastError();
 }
 
