@@ -24,7 +24,7 @@ struct Layout {
   // forward
   size_t label32 = 0, n_valid = 0, status = 0, zlab = 0, lse = 0, part_m = 0, part_s = 0, chunk_acc = 0;
   // backward
-  size_t wT = 0, htail = 0, dlog = 0, gw_f32 = 0, gb_f32 = 0;
+  size_t wT = 0, htail = 0, gw_part = 0, dlog = 0, gw_f32 = 0, gb_f32 = 0;
   size_t total = 0;
 };
 
@@ -96,6 +96,7 @@ Layout make_layout(const lce_problem* p, int kind) {
     // htail holds the last partial 64 rows of a group (zero past N)
     L.wT = take((size_t)s.H * s.Vp * 2);
     L.htail = take((size_t)64 * s.ldh * 2);
+    L.gw_part = take((size_t)lce::kMaxGwItems * 256 * 256 * 4);   // split grad_weight tiles
     L.dlog = take((size_t)G * s.Vp * 2);
     L.gb_f32 = take((size_t)s.Vp * 4);
     if (kind == LCE_WS_BACKWARD) L.gw_f32 = take((size_t)s.V * s.H * 4);
@@ -334,6 +335,7 @@ int lce_forward_backward_ex(const lce_problem* p, const void* hidden, const void
     const int64_t G = group_rows(p, s);
     void* wT = ws + c.L.wT;
     void* htail = ws + c.L.htail;
+    float* gw_part = (float*)(ws + c.L.gw_part);
     void* dlog = ws + c.L.dlog;
     const int is_mean = p->reduction == LCE_REDUCTION_MEAN;
     const bool any_grad = need_gh || need_gw || need_gb;
@@ -354,7 +356,7 @@ int lce_forward_backward_ex(const lce_problem* p, const void* hidden, const void
                    lce::launch_grad_hidden(s, dlog, wT, g0, Gc, grad_hidden, stream));
       if (need_gw)
         LCE_LAUNCH(tr, LCE_K_GRAD_WEIGHT, s.V, s.H, rows_valid,
-                   lce::launch_grad_weight(s, dlog, Gc, hidden, g0, rows_valid, htail,
+                   lce::launch_grad_weight(s, dlog, Gc, hidden, g0, rows_valid, htail, gw_part,
                                            (g0 == 0 && !accumulate) ? 1 : 0, gw, stream));
     }
   }

@@ -54,9 +54,18 @@ hipError_t launch_grad_hidden(const Shapes& s, const void* dlog, const void* wT,
                               void* grad_hidden, hipStream_t st);
 // gw (+)= sum over the group's rows i < rows_valid of G[i][v] h[g0 + i][:]
 // (dlog: K-slabs [Vp/64][G][64] holding G; hidden row-major [N][ldh]).
-// htail: 64 * ldh elements of scratch for the group's last partial 64 rows.
+// htail: 64 * ldh elements of scratch for the group's last partial 64 rows;
+// part: kMaxGwItems * 256 * 256 floats of scratch for split tiles.
 hipError_t launch_grad_weight(const Shapes& s, const void* dlog, int64_t G, const void* hidden, int64_t g0,
-                              int64_t rows_valid, void* htail, int first, float* gw_f32, hipStream_t st);
+                              int64_t rows_valid, void* htail, float* part, int first, float* gw_f32,
+                              hipStream_t st);
+// grad_weight's tiles: the first n_full run whole (a multiple of the CU
+// count), the rest are split `split` ways along K (split = 1: none) so that
+// they fill one round; at most kMaxGwItems split pieces.
+constexpr int kMaxGwSplit = 8;
+constexpr int kMaxGwItems = 256;
+void grad_weight_split(int n_tiles, int nk, int cus, int* n_full, int* split);
+int device_cus();
 hipError_t launch_cast(const float* in, void* out, int64_t n, hipStream_t st);
 
 }  // namespace lce

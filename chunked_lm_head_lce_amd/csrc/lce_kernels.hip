@@ -924,14 +924,30 @@ __device__ __forceinline__ void tr_slot(int wave, int lane, int b, int& k, int& 
 // G as K-slabs [Vp/64][slab_rows][64], h row-major [.][ldh] from row g0.
 // Stage s_tail (the group's last, partial 64 rows) takes h from htail
 // ([64][ldh], zero past N) so that no row past N is read.
+//
+// The first n_full tiles (whole rounds of the GPU) are one workgroup each.
+// The n_tiles - n_full left over would run as one thin last round, so each
+// is split over `split` workgroups by K; those write FP32 partial tiles to
+// part ([item][256][256]) and k_gw_reduce adds them in a fixed order.
 __global__ void __launch_bounds__(NTHREADS, 1)
 k_gemm_grad_weight(const u16* __restrict__ G, int64_t slab_rows, const u16* __restrict__ hidden, int64_t ldh,
                    int64_t g0, const u16* __restrict__ htail, int s_tail, int nk, int64_t H, int64_t V,
-                   int n_mt, int n_nt, int first, float* __restrict__ gw_f32) {
+                   int n_mt, int n_nt, int n_full, int split, int first, float* __restrict__ gw_f32,
+                   float* __restrict__ part) {
   __shared__ __attribute__((aligned(16))) char smem_raw[MAINLOOP_LDS];
   LDS_AS char* smem = (LDS_AS char*)smem_raw;
-  int tm, tn;
-  tile_coords(n_mt, n_nt, tm, tn);
+  int tm, tn, s0 = 0, s1 = nk, item = -1;
+  if ((int)blockIdx.x < n_full) {
+    int t = blockIdx.x;
+    if ((n_full & 7) == 0) t = (t & 7) * (n_full >> 3) + (t >> 3);
+    tile_from_index(t, n_mt, n_nt, tm, tn);
+  } else {
+    item = (int)blockIdx.x - n_full;
+    const int sp = item % split;
+    tile_from_index(n_full + item / split, n_mt, n_nt, tm, tn);
+    s0 = (int)((int64_t)nk * sp / split);
+    s1 = (int)((int64_t)nk * (sp + 1) / split);
+  }
   const int64_t row0 = (int64_t)tm * TILE, col0 = (int64_t)tn * TILE;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -945,16 +961,27 @@ k_gemm_grad_weight(const u16* __restrict__ G, int64_t slab_rows, const u16* __re
     const int64_t col = col0 + 8 * c <= H - 8 ? 8 * c : H - 8 - col0;   // past H: any column in range
     t.oy.off[b] = (uint32_t)(((int64_t)k * ldh + col) * 2);
   }
-  t.xbase = uniform_ptr(G + (row0 >> 6) * slab_rows * 64);
-  t.ybase = uniform_ptr(hidden + g0 * ldh + col0);
+  // stages s0 .. s1-1 of the K loop (all of them for a whole tile)
+  t.xbase = uniform_ptr(G + (row0 >> 6) * slab_rows * 64 + (int64_t)s0 * 64 * 64);
+  t.ybase = uniform_ptr(hidden + (g0 + (int64_t)s0 * 64) * ldh + col0);
   t.kx = 64 * 64 * 2;
   t.ky = 64 * ldh * 2;
   t.ytail = htail != nullptr ? uniform_ptr(htail + col0) : nullptr;
-  t.s_tail = s_tail;
+  t.s_tail = s_tail >= s0 && s_tail < s1 ? s_tail - s0 : -1;
   t.lds_wave = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)smem + (uint32_t)wave * 32 * 128);
   Acc acc;
-  tile_prologue<true>(t, nk);
-  tile_run<true, FragT>(acc, t, nk, smem);
+  tile_prologue<true>(t, s1 - s0);
+  tile_run<true, FragT>(acc, t, s1 - s0, smem);
+  if (item >= 0) {   // partial tile of a split item: plain stores, summed by k_gw_reduce
+    float* dst = part + (int64_t)item * TILE * TILE + wn * 64 + (lane & 15);
+#pragma unroll
+    for (int i = 0; i < NB; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int j = 0; j < NBJ; ++j) dst[acc_row(wm, i, r, lane) * TILE + j * 16] = acc.v[i][j][r];
+    return;
+  }
   // H % 64 == 0: a wave's 64 columns are all below H or all past it; only
   // the last vocabulary tile has rows past V.
   if (col0 + wn * 64 < H) {
@@ -962,6 +989,26 @@ k_gemm_grad_weight(const u16* __restrict__ G, int64_t slab_rows, const u16* __re
     if (row0 + TILE <= V) gw_update<false>(acc, base, row0, H, V, wm, lane, first);
     else gw_update<true>(acc, base, row0, H, V, wm, lane, first);
   }
+}
+
+// gw (+)= the sum, in split order, of the partial tiles of the split items:
+// item e = tile n_full + e / split, part index e % split. One workgroup per
+// 256 x 4 strip of one tile (64 threads, one float4 each).
+__global__ void __launch_bounds__(64) k_gw_reduce(const float* __restrict__ part, int n_full, int split, int n_mt,
+                                                  int n_nt, int64_t H, int64_t V, int first,
+                                                  float* __restrict__ gw_f32) {
+  const int tile = blockIdx.y;
+  int tm, tn;
+  tile_from_index(n_full + tile, n_mt, n_nt, tm, tn);
+  const int r = blockIdx.x;                       // row of the tile
+  const int c = threadIdx.x * 4;                  // first of four columns
+  const int64_t v = (int64_t)tm * TILE + r, col = (int64_t)tn * TILE + c;
+  if (v >= V || col >= H) return;                 // H % 64 == 0: all four in or out
+  f32x4 sum = (f32x4){0.f, 0.f, 0.f, 0.f};
+  for (int sp = 0; sp < split; ++sp)
+    sum += *(const f32x4*)(part + ((int64_t)tile * split + sp) * TILE * TILE + r * TILE + c);
+  f32x4* dst = (f32x4*)(gw_f32 + v * H + col);
+  *dst = first ? sum : *dst + sum;
 }
 
 // htail [64][ld] = rows r0 .. r0 + 63 of in [.][ld] (first C columns), zero
@@ -1019,10 +1066,8 @@ hipError_t launch_prepare_labels(const int64_t* labels, int64_t N, int64_t Np, i
   return hipGetLastError();
 }
 
-// Grid of a persistent tile kernel: one workgroup per CU (the kernels' LDS
-// admits no second one), a multiple of 8 so that blockIdx % 8 names the XCD,
-// and no more than the tiles need.
-static int persistent_grid(int64_t ntiles) {
+// Compute units of the current device (cached per device).
+int device_cus() {
   static int cu_count[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
@@ -1031,8 +1076,16 @@ static int persistent_grid(int64_t ntiles) {
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 8) n = 8;
     cu_count[dev] = n;
   }
+  return cu_count[dev];
+}
+
+// Grid of a persistent tile kernel: one workgroup per CU (the kernels' LDS
+// admits no second one), a multiple of 8 so that blockIdx % 8 names the XCD,
+// and no more than the tiles need.
+static int persistent_grid(int64_t ntiles) {
+  const int cus = device_cus();
   const int64_t per_xcd = (ntiles + 7) / 8;
-  const int64_t nx = cu_count[dev] / 8 < per_xcd ? cu_count[dev] / 8 : per_xcd;
+  const int64_t nx = cus / 8 < per_xcd ? cus / 8 : per_xcd;
   return (int)(8 * nx);
 }
 
@@ -1105,7 +1158,8 @@ hipError_t launch_grad_hidden(const Shapes& s, const void* dlog, const void* wT,
 }
 
 hipError_t launch_grad_weight(const Shapes& s, const void* dlog, int64_t G, const void* hidden, int64_t g0,
-                              int64_t rows_valid, void* htail, int first, float* gw_f32, hipStream_t st) {
+                              int64_t rows_valid, void* htail, float* part, int first, float* gw_f32,
+                              hipStream_t st) {
   const int n_mt = (int)(s.Vp / TILE), n_nt = (int)((s.H + TILE - 1) / TILE);
   const int nk = (int)((rows_valid + 63) / 64);
   int s_tail = -1;
@@ -1117,10 +1171,32 @@ hipError_t launch_grad_weight(const Shapes& s, const void* dlog, int64_t G, cons
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(k_gemm_grad_weight, dim3((unsigned)(n_mt * n_nt)), dim3(NTHREADS), 0, st, (const u16*)dlog, G,
-                     (const u16*)hidden, s.ldh, g0, s_tail >= 0 ? (const u16*)htail : nullptr, s_tail, nk, s.H, s.V,
-                     n_mt, n_nt, first, gw_f32);
+  const int n_tiles = n_mt * n_nt;
+  int n_full = n_tiles, split = 1;
+  grad_weight_split(n_tiles, nk, device_cus(), &n_full, &split);
+  hipLaunchKernelGGL(k_gemm_grad_weight, dim3((unsigned)(n_full + (n_tiles - n_full) * split)), dim3(NTHREADS), 0,
+                     st, (const u16*)dlog, G, (const u16*)hidden, s.ldh, g0,
+                     s_tail >= 0 ? (const u16*)htail : nullptr, s_tail, nk, s.H, s.V, n_mt, n_nt, n_full, split,
+                     first, gw_f32, part);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || n_full == n_tiles) return e;
+  hipLaunchKernelGGL(k_gw_reduce, dim3(TILE, (unsigned)(n_tiles - n_full)), dim3(64), 0, st, part, n_full, split,
+                     n_mt, n_nt, s.H, s.V, first, gw_f32);
   return hipGetLastError();
+}
+
+void grad_weight_split(int n_tiles, int nk, int cus, int* n_full, int* split) {
+  const int rem = n_tiles % cus;
+  *n_full = n_tiles;
+  *split = 1;
+  if (rem == 0) return;
+  int sp = cus / rem;
+  if (sp > kMaxGwSplit) sp = kMaxGwSplit;
+  if (sp > nk / 4) sp = nk / 4;
+  if (sp * rem > kMaxGwItems) sp = kMaxGwItems / rem;
+  if (sp < 2) return;
+  *n_full = n_tiles - rem;
+  *split = sp;
 }
 
 hipError_t launch_scale(void* data, bool f32, int64_t n, const float* scale, hipStream_t st) {

@@ -241,3 +241,19 @@ def test_repeatable(cuda):
     assert torch.equal(a.grad_hidden, b.grad_hidden) and torch.equal(a.grad_weight, b.grad_weight)
     assert torch.equal(a.lse, b.lse)
     assert abs(float(a.loss.item()) - float(b.loss.item())) <= 1e-6 * abs(float(a.loss.item()))
+
+
+def test_grad_weight_whole_and_split_tiles(cuda):
+    """274 grad_weight tiles (V = 70000 over 256-row tiles, one column tile):
+    on a GPU with fewer CUs the tiles past the last whole round are split
+    along the rows of the group and summed by a second kernel; 700 rows end
+    in a partial 64-row stage, read from the zero-padded tail copy."""
+    n, h, v = 700, 256, 70000
+    say(f"[gpu] grad_weight whole + split tiles shape={(n, h, v)}")
+    inp = make_case(n, h, v, seed=71, bias_std=0.05, ignore_frac=0.05, weight_std=0.05)
+    hd, wd, bd, yd = to_device(inp, cuda)
+    out = lce.lce_forward_backward(hd, wd, bd, yd, reduction="sum")
+    again = lce.lce_forward_backward(hd, wd, bd, yd, reduction="sum")
+    torch.cuda.synchronize()
+    check_all(out, oracle_of(inp, "sum"), inp, "sum")
+    assert torch.equal(out.grad_weight, again.grad_weight)   # fixed summation order
