@@ -29,6 +29,9 @@ def compile_command(out: str = LIB, extra: list[str] | None = None) -> list[str]
         hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-shared", "-fPIC",
         # packed fp32 instructions are kept out of all device code
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+        # one lane's tile-claiming atomic must not become a wave-wide
+        # reduction that waits for its result where it is issued
+        "-mllvm", "-amdgpu-atomic-optimizer-strategy=None",
         "-I", os.path.join(ROOT, "include"),
         *(extra or []),
         *[os.path.join(CSRC, s) for s in SOURCES],

@@ -22,7 +22,8 @@ size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 struct Layout {
   // forward
-  size_t label32 = 0, n_valid = 0, status = 0, zlab = 0, lse = 0, part_m = 0, part_s = 0, chunk_acc = 0;
+  size_t label32 = 0, n_valid = 0, status = 0, zlab = 0, lse = 0, part_m = 0, part_s = 0, chunk_acc = 0,
+         tile_ctr = 0;
   // backward
   size_t wT = 0, htail = 0, gw_part = 0, dlog = 0, gw_f32 = 0, gb_f32 = 0;
   size_t total = 0;
@@ -90,6 +91,7 @@ Layout make_layout(const lce_problem* p, int kind) {
   L.part_m = take((size_t)4 * n_vt * part_rows * 4);
   L.part_s = take((size_t)4 * n_vt * part_rows * 4);
   L.chunk_acc = take((size_t)n_chunks(p) * 8);
+  L.tile_ctr = take(8 * sizeof(int));   // per-XCD tile counters of the forward tiles
   if (bwd) {
     const int64_t G = group_rows(p, s);
     // W^T and the group's p~ / G, both stored as K-slabs [K/64][rows][64];
@@ -156,6 +158,7 @@ struct Common {
   float* part_s;
   float* zlab;
   double* chunk_acc;
+  int* tile_ctr;
 
   int64_t T;
 };
@@ -192,6 +195,7 @@ int run_prepare(Common& c, const int64_t* labels, int64_t* n_valid_out, int32_t*
   c.status = status_out ? status_out : (int32_t*)(ws + c.L.status);
   c.lse_ws = (float*)(ws + c.L.lse);
   c.chunk_acc = (double*)(ws + c.L.chunk_acc);
+  c.tile_ctr = (int*)(ws + c.L.tile_ctr);
   c.part_m = (float*)(ws + c.L.part_m);
   c.part_s = (float*)(ws + c.L.part_s);
   c.zlab = (float*)(ws + c.L.zlab);
@@ -221,7 +225,7 @@ int run_rows(Common& c, const void* hidden, const void* weight, const void* bias
   const Shapes& s = c.s;
   const int64_t rows_valid = (s.N - g0) < rows ? (s.N - g0) : rows;
   LCE_LAUNCH(tr, LCE_K_FWD_LSE, rows_valid, s.V, s.H,
-             lce::launch_fwd_tiles(s, hidden, weight, bias, g0, rows, c.part_m, c.part_s, p_out, st));
+             lce::launch_fwd_tiles(s, hidden, weight, bias, g0, rows, c.part_m, c.part_s, p_out, c.tile_ctr, st));
   LCE_LAUNCH(tr, LCE_K_FINALIZE_ROWS, 0, 0, 0,
              lce::launch_finalize_rows(s, c.part_m, c.part_s, g0, rows, c.zlab, c.label32, c.status,
                                        c.p->reduction, c.lse_ws, lse_out,

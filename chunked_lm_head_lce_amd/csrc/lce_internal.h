@@ -22,8 +22,10 @@ hipError_t launch_prepare_labels(const int64_t* labels, int64_t N, int64_t Np, i
 // (max, sumexp) partials into part_m/part_s [4 * Vp/256][rows] and, when
 // p_out is non-null, bf16 exp(z - max_quarter) into p_out, stored as K-slabs
 // [Vp/64][rows][64] (element (i, j) at ((j/64) * rows + i) * 64 + j % 64).
+// tile_ctr: 8 ints of scratch (the per-XCD tile counters, zeroed here).
 hipError_t launch_fwd_tiles(const Shapes& s, const void* hidden, const void* weight, const void* bias, int64_t g0,
-                            int64_t rows, float* part_m, float* part_s, void* p_out, hipStream_t st);
+                            int64_t rows, float* part_m, float* part_s, void* p_out, int* tile_ctr,
+                            hipStream_t st);
 // zlab[i] = h_i . W_{y_i} + b_{y_i} for valid rows.
 hipError_t launch_label_logit(const Shapes& s, const void* hidden, const void* weight, const void* bias,
                               const int32_t* label32, float* zlab, hipStream_t st);

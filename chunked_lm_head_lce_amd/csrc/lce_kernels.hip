@@ -104,15 +104,13 @@ __device__ __forceinline__ void tile_coords(int n_m, int n_n, int& tm, int& tn) 
   if ((nb & 7) == 0) t = (t & 7) * (nb >> 3) + (t >> 3);
   tile_from_index(t, n_m, n_n, tm, tn);
 }
-// Persistent walk (grid a multiple of 8, at most one workgroup per CU): XCD
-// x = blockIdx % 8 owns logical tiles [x * per_xcd, (x + 1) * per_xcd), and
-// its gridDim/8 workgroups take them in turn, so the tiles running at once on
-// one XCD are consecutive, as in tile_coords. Returns false once the
-// workgroup's share is done (the same for every wave of the workgroup).
-__device__ __forceinline__ bool walk_tile(int n_m, int n_n, int it, int& tm, int& tn) {
+// Persistent kernels (grid a multiple of 8, at most one workgroup per CU):
+// XCD x = blockIdx % 8 owns logical tiles [x * per_xcd, (x + 1) * per_xcd),
+// taken in order, so the tiles running at once on one XCD are neighbours, as
+// in tile_coords. Tile k of this workgroup's XCD; false past its range.
+__device__ __forceinline__ bool xcd_tile(int n_m, int n_n, int k, int& tm, int& tn) {
   const int ntiles = n_m * n_n;
   const int per_xcd = (ntiles + 7) >> 3;
-  const int k = it * (int)(gridDim.x >> 3) + (int)(blockIdx.x >> 3);
   const int t = (int)(blockIdx.x & 7) * per_xcd + k;
   if (k >= per_xcd || t >= ntiles) return false;
   tile_from_index(t, n_m, n_n, tm, tn);
@@ -460,26 +458,37 @@ constexpr int PST_WAVE = 16 * PST_LD;          // u16 per wave
 // count as z = -inf (p = 0); a quarter with no column below V stores
 // max = -inf and sum = 0.
 //
-// Persistent: each workgroup walks its share of the tiles (walk_tile) and
-// issues the next tile's first loads before this tile's epilogue, so their
-// latency is covered by the epilogue's arithmetic and stores. The epilogue
-// keeps out of the stage buffers: partials go straight from registers to
-// global memory, p~ through a per-wave staging block, and the bias is read
-// into registers at the start of the tile.
+// Persistent: one workgroup per CU takes tiles of its XCD's range
+// (xcd_tile) and issues the next tile's first loads before this tile's
+// epilogue, so their latency is covered by the epilogue's arithmetic and
+// stores. The epilogue keeps out of the stage buffers: partials go straight
+// from registers to global memory, p~ through a per-wave staging block, and
+// the bias is read into registers at the start of the tile.
+//
+// Tiles are handed out in order by a per-XCD counter (tile_ctr[8], zero at
+// launch): a workgroup that runs ahead takes the next unclaimed tile, so the
+// tiles running at once on an XCD stay neighbours and share operand panels
+// in its L2 (a fixed stride per workgroup let them drift apart: 38% more
+// fabric reads). Lane 0 claims the tile after next during each epilogue and
+// passes it through LDS.
 template <bool STORE_P>
 __global__ void __launch_bounds__(NTHREADS, 1)
 k_fwd_tile(const u16* __restrict__ hidden, int64_t ldh, const u16* __restrict__ weight, int64_t ldw,
            const u16* __restrict__ bias, int64_t N, int64_t V, int64_t Vp, int64_t H, int64_t g0, int64_t ld_part,
-           int n_mt, int n_vt, float* __restrict__ part_m, float* __restrict__ part_s, u16* __restrict__ p_out) {
+           int n_mt, int n_vt, float* __restrict__ part_m, float* __restrict__ part_s, u16* __restrict__ p_out,
+           int* __restrict__ tile_ctr) {
   __shared__ __attribute__((aligned(16))) char smem_raw[MAINLOOP_LDS];
   __shared__ __attribute__((aligned(16))) u16 s_pst[STORE_P ? 8 * PST_WAVE : 8];
+  __shared__ int s_next;
   LDS_AS char* smem = (LDS_AS char*)smem_raw;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int wm = wave >> 2, wn = wave & 3;
   LDS_AS u16* pst = (LDS_AS u16*)s_pst + (STORE_P ? wave * PST_WAVE : 0);
   const int nk = (int)(H / BK);
-  int it = 0, tm, tn;
-  if (!walk_tile(n_mt, n_vt, it, tm, tn)) return;
+  const int xcd = (int)(blockIdx.x & 7), per_step = (int)(gridDim.x >> 3);
+  int tm, tn;
+  if (!xcd_tile(n_mt, n_vt, (int)(blockIdx.x >> 3), tm, tn)) return;
+  if (tid == 0) s_next = per_step + atomicAdd(tile_ctr + xcd, 1);
   TileLoads t = tile_setup(hidden, ldh, BK * 2, g0 + (int64_t)tm * TILE, N, weight, ldw, BK * 2,
                            (int64_t)tn * TILE, V, smem);
   tile_prologue(t, nk);
@@ -511,13 +520,19 @@ k_fwd_tile(const u16* __restrict__ hidden, int64_t ldh, const u16* __restrict__ 
       // the next tile's loads
       asm volatile("" ::"v"(cbl[j]));
     }
-    const bool more = walk_tile(n_mt, n_vt, ++it, tm, tn);
-    bare_barrier();   // every wave is past its last read of the stage buffers
+    const int k_next = s_next;   // claimed before this tile's K loop (whose barriers publish it)
+    const bool more = xcd_tile(n_mt, n_vt, k_next, tm, tn);
+    bare_barrier();   // every wave is past its last read of the stage buffers (and of s_next)
     if (more) {
       t = tile_setup(hidden, ldh, BK * 2, g0 + (int64_t)tm * TILE, N, weight, ldw, BK * 2, (int64_t)tn * TILE, V,
                      smem);
       tile_prologue(t, nk);
     }
+    // claim the tile after next now; the result is needed only after the
+    // next K loop, and waiting for it at the end of the epilogue costs
+    // nothing (the next tile's first loads, issued earlier, have landed)
+    int claimed = 0;
+    if (more && tid == 0) claimed = atomicAdd(tile_ctr + xcd, 1);
     float* pm = part_m + (int64_t)(NQ * ptn + wn) * ld_part + lrow0 + wm * 128 + 4 * (lane >> 4);
     float* ps = part_s + (int64_t)(NQ * ptn + wn) * ld_part + lrow0 + wm * 128 + 4 * (lane >> 4);
     u16* pq = STORE_P ? p_out + ((col0 >> 6) + wn) * ld_part * 64 + (lrow0 + wm * 128) * 64 : nullptr;
@@ -577,6 +592,11 @@ k_fwd_tile(const u16* __restrict__ hidden, int64_t ldh, const u16* __restrict__ 
         asm volatile("" ::: "memory");
       }
     }
+    // First use of `claimed`, so the compiler's wait for the atomic lands
+    // here. (The library is built with the atomic optimizer off: its
+    // wave-wide rewrite of a uniform-address atomic reads the result at once.)
+    asm volatile("" ::: "memory");
+    if (more && tid == 0) s_next = per_step + claimed;
     if (!more) break;
   }
 }
@@ -1090,18 +1110,22 @@ static int persistent_grid(int64_t ntiles) {
 }
 
 hipError_t launch_fwd_tiles(const Shapes& s, const void* hidden, const void* weight, const void* bias, int64_t g0,
-                            int64_t rows, float* part_m, float* part_s, void* p_out, hipStream_t st) {
+                            int64_t rows, float* part_m, float* part_s, void* p_out, int* tile_ctr,
+                            hipStream_t st) {
   const int n_mt = (int)(rows / TILE), n_vt = (int)(s.Vp / TILE);
   const int nb = persistent_grid((int64_t)n_mt * n_vt);
   if (nb == 0) return hipSuccess;
+  hipError_t e = launch_zero(tile_ctr, 8 * sizeof(int), st);
+  if (e != hipSuccess) return e;
   const dim3 grid((unsigned)nb), block(NTHREADS);
   if (p_out)
     hipLaunchKernelGGL(k_fwd_tile<true>, grid, block, 0, st, (const u16*)hidden, s.ldh, (const u16*)weight, s.ldw,
-                       (const u16*)bias, s.N, s.V, s.Vp, s.H, g0, rows, n_mt, n_vt, part_m, part_s, (u16*)p_out);
+                       (const u16*)bias, s.N, s.V, s.Vp, s.H, g0, rows, n_mt, n_vt, part_m, part_s, (u16*)p_out,
+                       tile_ctr);
   else
     hipLaunchKernelGGL(k_fwd_tile<false>, grid, block, 0, st, (const u16*)hidden, s.ldh, (const u16*)weight,
                        s.ldw, (const u16*)bias, s.N, s.V, s.Vp, s.H, g0, rows, n_mt, n_vt, part_m, part_s,
-                       (u16*)nullptr);
+                       (u16*)nullptr, tile_ctr);
   return hipGetLastError();
 }
 
