@@ -658,10 +658,26 @@ __global__ void __launch_bounds__(64 * FIN_WAVES) k_finalize_rows(
   const bool live = i < row_end && i < N;
   float M = -INFINITY, S = 0.f;
   if (live) {
+    // four independent running (max, sum) pairs, so that four loads and four
+    // merges are in flight per lane instead of one dependent chain
     const int64_t pi = i - part_row0;
-#pragma unroll 8
-    for (int k = wave; k < n_part; k += FIN_WAVES)
-      merge_ms(M, S, part_m[(int64_t)k * ld_part + pi], part_s[(int64_t)k * ld_part + pi]);
+    float Mc[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY}, Sc[4] = {0.f, 0.f, 0.f, 0.f};
+    int k = wave;
+#pragma unroll 2
+    for (; k + 3 * FIN_WAVES < n_part; k += 4 * FIN_WAVES) {
+      float mk[4], sk[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        mk[u] = part_m[(int64_t)(k + u * FIN_WAVES) * ld_part + pi];
+        sk[u] = part_s[(int64_t)(k + u * FIN_WAVES) * ld_part + pi];
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) merge_ms(Mc[u], Sc[u], mk[u], sk[u]);
+    }
+    for (; k < n_part; k += FIN_WAVES)
+      merge_ms(Mc[0], Sc[0], part_m[(int64_t)k * ld_part + pi], part_s[(int64_t)k * ld_part + pi]);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) merge_ms(M, S, Mc[u], Sc[u]);
   }
   s_m[wave][lane] = M;
   s_s[wave][lane] = S;
