@@ -87,8 +87,8 @@ __device__ __forceinline__ float sum16(float v) {
 // column tiles, so concurrently running tiles on one XCD share operand panels
 // in that XCD's L2.
 // ---------------------------------------------------------------------------
+template <int GROUP_M = 4>
 __device__ __forceinline__ void tile_from_index(int t, int n_m, int n_n, int& tm, int& tn) {
-  constexpr int GROUP_M = 4;
   const int per_group = GROUP_M * n_n;
   const int g = t / per_group;
   const int first_m = g * GROUP_M;
@@ -947,6 +947,11 @@ __device__ __forceinline__ void gw_update(const Acc& acc, float* __restrict__ ba
   }
 }
 
+// grad_weight walks 2 vocabulary tiles across all hidden tiles at a time
+// (a 2 x 16 window per XCD at H = 4096): measured 1% faster than 4 x 8 with
+// its K-major operands (8 x 4: 3% slower, 16 x 2: 12% slower).
+constexpr int GW_GROUP_M = 2;
+
 // DMA offsets of the K-major layout: fill b of a wave covers rows
 // k = 8 wave + 2b + lane/32, lane % 32 the 16-byte slot p, which holds m-chunk
 // c = p ^ (2 tr_swz(k)).
@@ -976,11 +981,11 @@ k_gemm_grad_weight(const u16* __restrict__ G, int64_t slab_rows, const u16* __re
   if ((int)blockIdx.x < n_full) {
     int t = blockIdx.x;
     if ((n_full & 7) == 0) t = (t & 7) * (n_full >> 3) + (t >> 3);
-    tile_from_index(t, n_mt, n_nt, tm, tn);
+    tile_from_index<GW_GROUP_M>(t, n_mt, n_nt, tm, tn);
   } else {
     item = (int)blockIdx.x - n_full;
     const int sp = item % split;
-    tile_from_index(n_full + item / split, n_mt, n_nt, tm, tn);
+    tile_from_index<GW_GROUP_M>(n_full + item / split, n_mt, n_nt, tm, tn);
     s0 = (int)((int64_t)nk * sp / split);
     s1 = (int)((int64_t)nk * (sp + 1) / split);
   }
@@ -1035,7 +1040,7 @@ __global__ void __launch_bounds__(64) k_gw_reduce(const float* __restrict__ part
                                                   float* __restrict__ gw_f32) {
   const int tile = blockIdx.y;
   int tm, tn;
-  tile_from_index(n_full + tile, n_mt, n_nt, tm, tn);
+  tile_from_index<GW_GROUP_M>(n_full + tile, n_mt, n_nt, tm, tn);
   const int r = blockIdx.x;                       // row of the tile
   const int c = threadIdx.x * 4;                  // first of four columns
   const int64_t v = (int64_t)tm * TILE + r, col = (int64_t)tn * TILE + c;
