@@ -474,8 +474,8 @@ constexpr int PST_WAVE = 16 * PST_LD;          // u16 per wave
 template <bool STORE_P>
 __global__ void __launch_bounds__(NTHREADS, 1)
 k_fwd_tile(const u16* __restrict__ hidden, int64_t ldh, const u16* __restrict__ weight, int64_t ldw,
-           const u16* __restrict__ bias, int64_t N, int64_t V, int64_t Vp, int64_t H, int64_t g0, int64_t ld_part,
-           int n_mt, int n_vt, float* __restrict__ part_m, float* __restrict__ part_s, u16* __restrict__ p_out,
+           const u16* __restrict__ bias, int64_t N, int64_t V, int64_t H, int64_t g0, int64_t ld_part, int n_mt,
+           int n_vt, float* __restrict__ part_m, float* __restrict__ part_s, u16* __restrict__ p_out,
            int* __restrict__ tile_ctr) {
   __shared__ __attribute__((aligned(16))) char smem_raw[MAINLOOP_LDS];
   __shared__ __attribute__((aligned(16))) u16 s_pst[STORE_P ? 8 * PST_WAVE : 8];
@@ -792,7 +792,7 @@ __global__ void __launch_bounds__(256)
 k_dlogits_from_p(u16* __restrict__ dlog, const float* __restrict__ part_m,
                  const int32_t* __restrict__ label32, const float* __restrict__ lse_ws,
                  const unsigned long long* __restrict__ n_valid, float grad_scale, int is_mean,
-                 const float* __restrict__ row_scale, int64_t V, int64_t Vp, int64_t g0, int64_t G, int write_dlog,
+                 const float* __restrict__ row_scale, int64_t V, int64_t g0, int64_t G, int write_dlog,
                  float* __restrict__ gb_f32) {
   __shared__ float s_f[NQ][DL_ROWS];
   __shared__ int s_lab[DL_ROWS];
@@ -1141,12 +1141,11 @@ hipError_t launch_fwd_tiles(const Shapes& s, const void* hidden, const void* wei
   const dim3 grid((unsigned)nb), block(NTHREADS);
   if (p_out)
     hipLaunchKernelGGL(k_fwd_tile<true>, grid, block, 0, st, (const u16*)hidden, s.ldh, (const u16*)weight, s.ldw,
-                       (const u16*)bias, s.N, s.V, s.Vp, s.H, g0, rows, n_mt, n_vt, part_m, part_s, (u16*)p_out,
-                       tile_ctr);
+                       (const u16*)bias, s.N, s.V, s.H, g0, rows, n_mt, n_vt, part_m, part_s, (u16*)p_out, tile_ctr);
   else
     hipLaunchKernelGGL(k_fwd_tile<false>, grid, block, 0, st, (const u16*)hidden, s.ldh, (const u16*)weight,
-                       s.ldw, (const u16*)bias, s.N, s.V, s.Vp, s.H, g0, rows, n_mt, n_vt, part_m, part_s,
-                       (u16*)nullptr, tile_ctr);
+                       s.ldw, (const u16*)bias, s.N, s.V, s.H, g0, rows, n_mt, n_vt, part_m, part_s, (u16*)nullptr,
+                       tile_ctr);
   return hipGetLastError();
 }
 
@@ -1189,8 +1188,7 @@ hipError_t launch_dlogits(const Shapes& s, const int32_t* label32, const float* 
                           int64_t g0, int64_t G, void* dlog, int write_dlog, float* gb_f32, hipStream_t st) {
   const int n_mt = (int)(G / DL_ROWS), n_vt = (int)(s.Vp / TILE);
   hipLaunchKernelGGL(k_dlogits_from_p, dim3((unsigned)(n_mt * n_vt)), dim3(256), 0, st, (u16*)dlog,
-                     part_m, label32, lse_ws, n_valid, grad_scale, is_mean, row_scale, s.V, s.Vp, g0, G, write_dlog,
-                     gb_f32);
+                     part_m, label32, lse_ws, n_valid, grad_scale, is_mean, row_scale, s.V, g0, G, write_dlog, gb_f32);
   return hipGetLastError();
 }
 
