@@ -25,7 +25,7 @@ struct Layout {
   size_t label32 = 0, n_valid = 0, status = 0, zlab = 0, lse = 0, part_m = 0, part_s = 0, chunk_acc = 0,
          tile_ctr = 0;
   // backward
-  size_t wT = 0, htail = 0, gw_part = 0, dlog = 0, gw_f32 = 0, gb_f32 = 0;
+  size_t wT = 0, hT = 0, gw_part = 0, dlog = 0, gw_f32 = 0, gb_f32 = 0;
   size_t total = 0;
 };
 
@@ -94,10 +94,10 @@ Layout make_layout(const lce_problem* p, int kind) {
   L.tile_ctr = take(8 * sizeof(int));   // per-XCD tile counters of the forward tiles
   if (bwd) {
     const int64_t G = group_rows(p, s);
-    // W^T and the group's p~ / G, both stored as K-slabs [K/64][rows][64];
-    // htail holds the last partial 64 rows of a group (zero past N)
+    // W^T, the group's h^T and its p~ / G, all stored as K-slabs
+    // [K/64][rows][64]
     L.wT = take((size_t)s.H * s.Vp * 2);
-    L.htail = take((size_t)64 * s.ldh * 2);
+    L.hT = take((size_t)s.H * G * 2);
     L.gw_part = take((size_t)lce::kMaxGwItems * 256 * 256 * 4);   // split grad_weight tiles
     L.dlog = take((size_t)G * s.Vp * 2);
     L.gb_f32 = take((size_t)s.Vp * 4);
@@ -338,7 +338,7 @@ int lce_forward_backward_ex(const lce_problem* p, const void* hidden, const void
     // pass turns dlog into G in place for the two gradient products.
     const int64_t G = group_rows(p, s);
     void* wT = ws + c.L.wT;
-    void* htail = ws + c.L.htail;
+    void* hT = ws + c.L.hT;
     float* gw_part = (float*)(ws + c.L.gw_part);
     void* dlog = ws + c.L.dlog;
     const int is_mean = p->reduction == LCE_REDUCTION_MEAN;
@@ -358,10 +358,13 @@ int lce_forward_backward_ex(const lce_problem* p, const void* hidden, const void
       if (need_gh)
         LCE_LAUNCH(tr, LCE_K_GRAD_HIDDEN, rows_valid, s.H, s.V,
                    lce::launch_grad_hidden(s, dlog, wT, g0, Gc, grad_hidden, stream));
-      if (need_gw)
+      if (need_gw) {
+        LCE_LAUNCH(tr, LCE_K_TRANSPOSE, 0, 0, 0,
+                   lce::launch_transpose(hidden, s.ldh, g0, rows_valid, s.H, hT, Gc, stream));
         LCE_LAUNCH(tr, LCE_K_GRAD_WEIGHT, s.V, s.H, rows_valid,
-                   lce::launch_grad_weight(s, dlog, Gc, hidden, g0, rows_valid, htail, gw_part,
-                                           (g0 == 0 && !accumulate) ? 1 : 0, gw, stream));
+                   lce::launch_grad_weight(s, dlog, Gc, hT, rows_valid, gw_part, (g0 == 0 && !accumulate) ? 1 : 0,
+                                           gw, stream));
+      }
     }
   }
   if (need_gw && grad_weight)

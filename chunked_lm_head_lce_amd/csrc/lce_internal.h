@@ -55,12 +55,11 @@ hipError_t launch_scale(void* data, bool f32, int64_t n, const float* scale, hip
 hipError_t launch_grad_hidden(const Shapes& s, const void* dlog, const void* wT, int64_t g0, int64_t G,
                               void* grad_hidden, hipStream_t st);
 // gw (+)= sum over the group's rows i < rows_valid of G[i][v] h[g0 + i][:]
-// (dlog: K-slabs [Vp/64][G][64] holding G; hidden row-major [N][ldh]).
-// htail: 64 * ldh elements of scratch for the group's last partial 64 rows;
-// part: kMaxGwItems * 256 * 256 floats of scratch for split tiles.
-hipError_t launch_grad_weight(const Shapes& s, const void* dlog, int64_t G, const void* hidden, int64_t g0,
-                              int64_t rows_valid, void* htail, float* part, int first, float* gw_f32,
-                              hipStream_t st);
+// (dlog: K-slabs [Vp/64][G][64] holding G; hT: the group's rows of h as
+// K-slabs [G/64][H][64], zero past N). part: kMaxGwItems * 256 * 256 floats
+// of scratch for split tiles.
+hipError_t launch_grad_weight(const Shapes& s, const void* dlog, int64_t G, const void* hT, int64_t rows_valid,
+                              float* part, int first, float* gw_f32, hipStream_t st);
 // grad_weight's tiles: the first n_full run whole (a multiple of the CU
 // count), the rest are split `split` ways along K (split = 1: none) so that
 // they fill one round; at most kMaxGwItems split pieces.

@@ -194,8 +194,6 @@ struct TileLoads {
   const void* xbase;
   const void* ybase;
   int64_t kx, ky;
-  const void* ytail;     // Y stage s_tail comes from here instead (TAIL loads only)
-  int s_tail;
   StageOffsets ox, oy;
   uint32_t lds_wave;     // LDS byte address of this wave's 32 rows in stage buffer 0
 };
@@ -208,17 +206,12 @@ __device__ __forceinline__ const void* uniform_ptr(const void* p) {
 }
 
 // Issues load f (0..7) of stage s: f < 4 fill X rows, f >= 4 fill Y rows.
-// With TAIL, Y stage t.s_tail is read from t.ytail (same offsets).
-template <bool TAIL>
 __device__ __forceinline__ void stage_load(const TileLoads& t, int s, int f) {
   const uint32_t buf = t.lds_wave + (uint32_t)((s & 1) * STAGE);
-  if (f < FILLS) {
+  if (f < FILLS)
     lds_dma16((const char*)t.xbase + s * t.kx, t.ox.off[f], buf + f * 1024);
-  } else {
-    const char* yb = (const char*)t.ybase + s * t.ky;
-    if (TAIL && s == t.s_tail) yb = (const char*)t.ytail;
-    lds_dma16(yb, t.oy.off[f - FILLS], buf + OPERAND_STAGE + (f - FILLS) * 1024);
-  }
+  else
+    lds_dma16((const char*)t.ybase + s * t.ky, t.oy.off[f - FILLS], buf + OPERAND_STAGE + (f - FILLS) * 1024);
 }
 
 #define FENCE() __builtin_amdgcn_sched_barrier(0)
@@ -266,22 +259,23 @@ __device__ __forceinline__ bf16x8 frag_tr(const LDS_AS char* p) {
   const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4*)(p + 4 * TR_ROW));
   return __builtin_bit_cast(bf16x8, (s16x8)__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
-// FragT: both operands K-major; per-lane byte offsets of the 12 fragments in
-// a stage (sub-step 0, first half), fixed for the whole K loop.
-struct FragT {
+// FragAT: A K-major (transposing reads; per-lane byte offsets of its 8
+// fragments in a stage, sub-step 0, first half, fixed for the whole K loop),
+// B K-contiguous (as FragK). (Raising the wave priority as FragK does
+// measured no faster here.)
+struct FragAT {
   static constexpr bool kPrio = false;
   static constexpr bool kPrioLoads = false;
-  uint32_t a[NB], b[NBJ];
-  __device__ __forceinline__ FragT(int wave, int lane) {
-    const int q = lane >> 4, j = lane & 15, t = tr_swz(8 * q + (j >> 2));
+  uint32_t a[NB];
+  int rB, q;
+  __device__ __forceinline__ FragAT(int wave, int lane) : rB((wave & 3) * 64 + (lane & 15)), q(lane >> 4) {
+    const int j = lane & 15, t = tr_swz(8 * q + (j >> 2));
     const uint32_t row = (uint32_t)(8 * q + (j >> 2)) * TR_ROW + 8 * (j & 3);
 #pragma unroll
     for (int i = 0; i < NB; ++i) a[i] = row + 32 * (((wave >> 2) * NB + i) ^ t);
-#pragma unroll
-    for (int i = 0; i < NBJ; ++i) b[i] = OPERAND_STAGE + row + 32 * (((wave & 3) * NBJ + i) ^ t);
   }
   __device__ __forceinline__ void read(Frags& f, const LDS_AS char* buf, int sub, int n) const {
-    if (n < NBJ) f.b[n] = frag_tr(buf + b[n] + sub * 32 * TR_ROW);
+    if (n < NBJ) f.b[n] = frag(buf + OPERAND_STAGE, rB + n * 16, sub * 4 + q);
     else f.a[n - NBJ] = frag_tr(buf + a[n - NBJ] + sub * 32 * TR_ROW);
   }
 };
@@ -306,7 +300,7 @@ struct FragT {
 // (the forward tiles) with the loads.
 // At entry: f0 holds stage s sub-step 0; loads 0..5 of stage s+1 went out in
 // the previous stage (slots 10..15), loads 6..7 go out in slots 0..1.
-template <bool TAIL, class FS>
+template <class FS>
 __device__ __forceinline__ void mainloop_stage(Acc& acc, Frags& f0, Frags& f1, int s, int nk, LDS_AS char* smem,
                                                const TileLoads& t, const FS& fs) {
   LDS_AS char* cur = smem + (s & 1) * STAGE;
@@ -328,9 +322,9 @@ __device__ __forceinline__ void mainloop_stage(Acc& acc, Frags& f0, Frags& f1, i
     FENCE();
     if (FS::kPrioLoads) __builtin_amdgcn_s_setprio(1);
     if (slot < 2) {
-      if (s + 1 < nk) stage_load<TAIL>(t, s + 1, 6 + slot);
+      if (s + 1 < nk) stage_load(t, s + 1, 6 + slot);
     } else if (slot >= 10) {
-      if (s + 2 < nk) stage_load<TAIL>(t, s + 2, slot - 10);
+      if (s + 2 < nk) stage_load(t, s + 2, slot - 10);
     }
     if (FS::kPrioLoads) __builtin_amdgcn_s_setprio(0);
     // fragment reads: f1 of this stage in slots 0..5, f0 of the next in 10..15
@@ -375,20 +369,17 @@ __device__ __forceinline__ TileLoads tile_setup(const u16* __restrict__ X, int64
   t.ybase = uniform_ptr(Y + y_row0 * ldy);
   t.kx = kx;
   t.ky = ky;
-  t.ytail = nullptr;
-  t.s_tail = -1;
   t.lds_wave = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)smem + (uint32_t)wave * 32 * 128);
   return t;
 }
-template <bool TAIL = false>
 __device__ __forceinline__ void tile_prologue(const TileLoads& t, int nk) {
 #pragma unroll
-  for (int f = 0; f < 2 * FILLS; ++f) stage_load<TAIL>(t, 0, f);
+  for (int f = 0; f < 2 * FILLS; ++f) stage_load(t, 0, f);
   if (nk > 1)
 #pragma unroll
-    for (int f = 0; f < 6; ++f) stage_load<TAIL>(t, 1, f);
+    for (int f = 0; f < 6; ++f) stage_load(t, 1, f);
 }
-template <bool TAIL = false, class FS = FragK>
+template <class FS = FragK>
 __device__ __forceinline__ void tile_run(Acc& acc, const TileLoads& t, int nk, LDS_AS char* smem) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -405,7 +396,7 @@ __device__ __forceinline__ void tile_run(Acc& acc, const TileLoads& t, int nk, L
   Frags f0, f1;
 #pragma unroll
   for (int n = 0; n < NB + NBJ; ++n) fs.read(f0, smem, 0, n);
-  for (int s = 0; s < nk; ++s) mainloop_stage<TAIL>(acc, f0, f1, s, nk, smem, t, fs);
+  for (int s = 0; s < nk; ++s) mainloop_stage(acc, f0, f1, s, nk, smem, t, fs);
   __builtin_amdgcn_s_waitcnt(WAIT_LGKM0);
 }
 __device__ __forceinline__ void gemm_tile(Acc& acc, const u16* __restrict__ X, int64_t ldx, int64_t kx,
@@ -975,19 +966,20 @@ __device__ __forceinline__ void tr_slot(int wave, int lane, int b, int& k, int& 
 }
 
 // grad_weight FP32 accumulation for one group: gw[v][:] (+)= sum_i G[i][v] h[i][:]
-// over the group's rows, read as they are stored (K-major for this product):
-// G as K-slabs [Vp/64][slab_rows][64], h row-major [.][ldh] from row g0.
-// Stage s_tail (the group's last, partial 64 rows) takes h from htail
-// ([64][ldh], zero past N) so that no row past N is read.
+// over the group's rows. G is read as it is stored, K-major for this
+// product (K-slabs [Vp/64][slab_rows][64], transposing LDS reads); h comes as
+// hT, the group's rows transposed into K-slabs [slab_rows/64][H][64] (zero
+// past N), read like the other kernels' operands. (Reading h K-major too
+// saved that transpose but made the loop 1.8% slower: two 8-byte reads per
+// fragment instead of one 16-byte read.)
 //
 // The first n_full tiles (whole rounds of the GPU) are one workgroup each.
 // The n_tiles - n_full left over would run as one thin last round, so each
 // is split over `split` workgroups by K; those write FP32 partial tiles to
 // part ([item][256][256]) and k_gw_reduce adds them in a fixed order.
 __global__ void __launch_bounds__(NTHREADS, 1)
-k_gemm_grad_weight(const u16* __restrict__ G, int64_t slab_rows, const u16* __restrict__ hidden, int64_t ldh,
-                   int64_t g0, const u16* __restrict__ htail, int s_tail, int nk, int64_t H, int64_t V,
-                   int n_mt, int n_nt, int n_full, int split, int first, float* __restrict__ gw_f32,
+k_gemm_grad_weight(const u16* __restrict__ G, int64_t slab_rows, const u16* __restrict__ hT, int nk, int64_t H,
+                   int64_t V, int n_mt, int n_nt, int n_full, int split, int first, float* __restrict__ gw_f32,
                    float* __restrict__ part) {
   __shared__ __attribute__((aligned(16))) char smem_raw[MAINLOOP_LDS];
   LDS_AS char* smem = (LDS_AS char*)smem_raw;
@@ -1013,20 +1005,17 @@ k_gemm_grad_weight(const u16* __restrict__ G, int64_t slab_rows, const u16* __re
     int k, c;
     tr_slot(wave, lane, b, k, c);
     t.ox.off[b] = (uint32_t)((((int64_t)(c >> 3) * slab_rows + k) * 64 + (c & 7) * 8) * 2);
-    const int64_t col = col0 + 8 * c <= H - 8 ? 8 * c : H - 8 - col0;   // past H: any column in range
-    t.oy.off[b] = (uint32_t)(((int64_t)k * ldh + col) * 2);
   }
+  t.oy = stage_offsets(BK, col0, H, wave, lane);
   // stages s0 .. s1-1 of the K loop (all of them for a whole tile)
   t.xbase = uniform_ptr(G + (row0 >> 6) * slab_rows * 64 + (int64_t)s0 * 64 * 64);
-  t.ybase = uniform_ptr(hidden + (g0 + (int64_t)s0 * 64) * ldh + col0);
+  t.ybase = uniform_ptr(hT + ((int64_t)s0 * H + col0) * 64);
   t.kx = 64 * 64 * 2;
-  t.ky = 64 * ldh * 2;
-  t.ytail = htail != nullptr ? uniform_ptr(htail + col0) : nullptr;
-  t.s_tail = s_tail >= s0 && s_tail < s1 ? s_tail - s0 : -1;
+  t.ky = H * BK * 2;
   t.lds_wave = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)smem + (uint32_t)wave * 32 * 128);
   Acc acc;
-  tile_prologue<true>(t, s1 - s0);
-  tile_run<true, FragT>(acc, t, s1 - s0, smem);
+  tile_prologue(t, s1 - s0);
+  tile_run<FragAT>(acc, t, s1 - s0, smem);
   if (item >= 0) {   // partial tile of a split item: plain stores, summed by k_gw_reduce
     float* dst = part + (int64_t)item * TILE * TILE + wn * 64 + (lane & 15);
 #pragma unroll
@@ -1064,17 +1053,6 @@ __global__ void __launch_bounds__(64) k_gw_reduce(const float* __restrict__ part
     sum += *(const f32x4*)(part + ((int64_t)tile * split + sp) * TILE * TILE + r * TILE + c);
   f32x4* dst = (f32x4*)(gw_f32 + v * H + col);
   *dst = first ? sum : *dst + sum;
-}
-
-// htail [64][ld] = rows r0 .. r0 + 63 of in [.][ld] (first C columns), zero
-// for rows at or past N.
-__global__ void __launch_bounds__(256) k_tail_rows(const u16* __restrict__ in, int64_t ld, int64_t r0, int64_t N,
-                                                    int64_t C, u16* __restrict__ out) {
-  const int64_t n = 64 * C;
-  for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < n; e += (int64_t)gridDim.x * blockDim.x) {
-    const int64_t r = e / C, c = e - r * C;
-    out[r * ld + c] = r0 + r < N ? in[(r0 + r) * ld + c] : (u16)0;
-  }
 }
 
 // data[k] *= *scale (the scale read from device memory).
@@ -1214,27 +1192,16 @@ hipError_t launch_grad_hidden(const Shapes& s, const void* dlog, const void* wT,
   return hipGetLastError();
 }
 
-hipError_t launch_grad_weight(const Shapes& s, const void* dlog, int64_t G, const void* hidden, int64_t g0,
-                              int64_t rows_valid, void* htail, float* part, int first, float* gw_f32,
-                              hipStream_t st) {
+hipError_t launch_grad_weight(const Shapes& s, const void* dlog, int64_t G, const void* hT, int64_t rows_valid,
+                              float* part, int first, float* gw_f32, hipStream_t st) {
   const int n_mt = (int)(s.Vp / TILE), n_nt = (int)((s.H + TILE - 1) / TILE);
   const int nk = (int)((rows_valid + 63) / 64);
-  int s_tail = -1;
-  if (rows_valid % 64 != 0) {
-    s_tail = (int)(rows_valid / 64);
-    const int64_t n = 64 * s.H;
-    hipLaunchKernelGGL(k_tail_rows, dim3((unsigned)((n + 255) / 256 < 1024 ? (n + 255) / 256 : 1024)), dim3(256), 0,
-                       st, (const u16*)hidden, s.ldh, g0 + 64 * (int64_t)s_tail, s.N, s.H, (u16*)htail);
-    const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
   const int n_tiles = n_mt * n_nt;
   int n_full = n_tiles, split = 1;
   grad_weight_split(n_tiles, nk, device_cus(), &n_full, &split);
   hipLaunchKernelGGL(k_gemm_grad_weight, dim3((unsigned)(n_full + (n_tiles - n_full) * split)), dim3(NTHREADS), 0,
-                     st, (const u16*)dlog, G, (const u16*)hidden, s.ldh, g0,
-                     s_tail >= 0 ? (const u16*)htail : nullptr, s_tail, nk, s.H, s.V, n_mt, n_nt, n_full, split,
-                     first, gw_f32, part);
+                     st, (const u16*)dlog, G, (const u16*)hT, nk, s.H, s.V, n_mt, n_nt, n_full, split, first, gw_f32,
+                     part);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || n_full == n_tiles) return e;
   hipLaunchKernelGGL(k_gw_reduce, dim3(TILE, (unsigned)(n_tiles - n_full)), dim3(64), 0, st, part, n_full, split,

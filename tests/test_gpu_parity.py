@@ -247,7 +247,7 @@ def test_grad_weight_whole_and_split_tiles(cuda):
     """274 grad_weight tiles (V = 70000 over 256-row tiles, one column tile):
     on a GPU with fewer CUs the tiles past the last whole round are split
     along the rows of the group and summed by a second kernel; 700 rows end
-    in a partial 64-row stage, read from the zero-padded tail copy."""
+    in a partial 64-row stage (zero rows of G and of the transposed h)."""
     n, h, v = 700, 256, 70000
     say(f"[gpu] grad_weight whole + split tiles shape={(n, h, v)}")
     inp = make_case(n, h, v, seed=71, bias_std=0.05, ignore_frac=0.05, weight_std=0.05)
