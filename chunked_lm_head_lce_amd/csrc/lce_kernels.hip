@@ -108,12 +108,14 @@ __device__ __forceinline__ void tile_coords(int n_m, int n_n, int& tm, int& tn) 
 // XCD x = blockIdx % 8 owns logical tiles [x * per_xcd, (x + 1) * per_xcd),
 // taken in order, so the tiles running at once on one XCD are neighbours, as
 // in tile_coords. Tile k of this workgroup's XCD; false past its range.
+// (The forward walks 8 row tiles at a time, an 8 x 4 window: measured
+// ~1% faster than 4 x 8 there.)
 __device__ __forceinline__ bool xcd_tile(int n_m, int n_n, int k, int& tm, int& tn) {
   const int ntiles = n_m * n_n;
   const int per_xcd = (ntiles + 7) >> 3;
   const int t = (int)(blockIdx.x & 7) * per_xcd + k;
   if (k >= per_xcd || t >= ntiles) return false;
-  tile_from_index(t, n_m, n_n, tm, tn);
+  tile_from_index<8>(t, n_m, n_n, tm, tn);
   return true;
 }
 
