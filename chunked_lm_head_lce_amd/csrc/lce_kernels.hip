@@ -9,18 +9,20 @@
 //   grad_bias = sum_i G_i  (FP32 accumulation, one cast at the end).
 //
 // Every contraction runs through one bf16 MFMA tile routine that computes
-//   C[m][n] = sum_k X[m][k] * Y[n][k]        (both operands K-contiguous)
+//   C[m][n] = sum_k X[m][k] * Y[n][k]
 // for a 256 x 256 output tile, so the kernels differ only in their operands
 // and epilogues:
-//   z tile       X = hidden rows,       Y = weight rows,  K = H
+//   z tile       X = hidden rows,  Y = weight rows,  K = H
 //                (per backward row group the epilogue also keeps bf16
 //                exp(z - max), which an element-wise pass turns into G)
-//   grad_hidden  X = dlogits,   Y = W^T,  K = Vp
-//   grad_weight  X = dlogits^T, Y = h^T,  K = G
-// The backward operands are written by this library's own passes, so they
-// are stored as K-slabs: [K/64][rows][64], each 64-deep stage of a 256-row
-// tile one contiguous 32 KB block (row-major operands with row strides of
-// 30-300 KB touch hundreds of DRAM pages per stage; measured 1-3% slower).
+//   grad_hidden  X = G,            Y = W^T,          K = Vp
+//   grad_weight  X = G^T,          Y = h^T,          K = the group's rows
+// Operands are K-contiguous in memory except G in grad_weight, which is read
+// K-major and transposed by the LDS reads (FragAT). The backward operands
+// are written by this library's own passes, so they are stored as K-slabs:
+// [K/64][rows][64], each 64-deep stage of a 256-row tile one contiguous
+// 32 KB block (row-major operands with row strides of 30-300 KB touch
+// hundreds of DRAM pages per stage; measured 1-6% slower).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 #include <math.h>
