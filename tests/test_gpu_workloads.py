@@ -76,6 +76,16 @@ def _check_large(cuda, name, chunk_sweep=None):
         assert torch.equal(o.grad_hidden, out.grad_hidden)
         assert torch.equal(o.grad_weight, out.grad_weight)
 
+    # the forward-only call: every row in one pass, no stored softmax
+    say(f"[gpu] workload {name}: forward only")
+    f = lce.lce_forward(hd, wd, bd, yd, chunk_rows=w.chunk_rows, reduction=w.reduction, want_chunk_loss=True)
+    torch.cuda.synchronize()
+    assert int(f.status.item()) == 0
+    assert int(f.n_valid.item()) == meta["n_valid"]
+    assert_loss_close(float(f.loss.item()), meta["loss_sum"])
+    assert_rows_close(np32(f.lse), lse_ref, "forward-only lse (all rows)")
+    assert abs(float(f.chunk_loss.double().sum()) - meta["loss_sum"]) <= 2e-3 * abs(meta["loss_sum"])
+
     h32, w32, b32 = inp.hidden_f32(), inp.weight_f32(), inp.bias_f32()
     rows = sample_rows(w, inp.labels)
     say(f"[gpu] workload {name}: oracle on {len(rows)} rows")
