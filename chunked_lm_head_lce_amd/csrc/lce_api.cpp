@@ -328,6 +328,8 @@ int lce_forward_backward_ex(const lce_problem* p, const void* hidden, const void
   float* gw = grad_weight_f32 ? grad_weight_f32 : (float*)(ws + c.L.gw_f32);
   float* gb = grad_bias_f32 ? grad_bias_f32 : (float*)(ws + c.L.gb_f32);
   if (need_gb && !accumulate) LCE_LAUNCH(tr, LCE_K_ZERO, 0, 0, 0, lce::launch_zero(gb, s.V * 4, stream));
+  // the last row group's grad_weight writes the bf16 result itself
+  bool gw_cast_done = false;
   if (s.N == 0) {
     if (need_gw && !accumulate) LCE_LAUNCH(tr, LCE_K_ZERO, 0, 0, 0, lce::launch_zero(gw, s.V * s.H * 4, stream));
   } else {
@@ -347,6 +349,7 @@ int lce_forward_backward_ex(const lce_problem* p, const void* hidden, const void
       LCE_LAUNCH(tr, LCE_K_TRANSPOSE, 0, 0, 0,
                  lce::launch_transpose(weight, s.ldw, 0, s.V, s.H, wT, s.Vp, stream));
     for (int64_t g0 = 0; g0 < s.Np; g0 += G) {
+      const bool last = g0 + G >= s.Np;
       const int64_t Gc = (s.Np - g0) < G ? (s.Np - g0) : G;
       const int64_t rows_valid = (s.N - g0) < Gc ? (s.N - g0) : Gc;
       st = run_rows(c, hidden, weight, bias, g0, Gc, any_grad ? dlog : nullptr, loss, lse, stream, tr);
@@ -363,11 +366,14 @@ int lce_forward_backward_ex(const lce_problem* p, const void* hidden, const void
                    lce::launch_transpose(hidden, s.ldh, g0, rows_valid, s.H, hT, Gc, stream));
         LCE_LAUNCH(tr, LCE_K_GRAD_WEIGHT, s.V, s.H, rows_valid,
                    lce::launch_grad_weight(s, dlog, Gc, hT, rows_valid, gw_part, (g0 == 0 && !accumulate) ? 1 : 0,
-                                           gw, stream));
+                                           gw, last ? grad_weight : nullptr,
+                                           (!last || grad_weight == nullptr || grad_weight_f32 != nullptr) ? 1 : 0,
+                                           stream));
+        if (last) gw_cast_done = true;
       }
     }
   }
-  if (need_gw && grad_weight)
+  if (need_gw && grad_weight && !gw_cast_done)
     LCE_LAUNCH(tr, LCE_K_CAST, 0, 0, 0, lce::launch_cast(gw, grad_weight, s.V * s.H, stream));
   if (need_gb && grad_bias) LCE_LAUNCH(tr, LCE_K_CAST, 0, 0, 0, lce::launch_cast(gb, grad_bias, s.V, stream));
   LCE_LAUNCH(tr, LCE_K_FINALIZE_LOSS, 0, 0, 0,

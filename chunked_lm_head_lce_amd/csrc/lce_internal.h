@@ -57,9 +57,11 @@ hipError_t launch_grad_hidden(const Shapes& s, const void* dlog, const void* wT,
 // gw (+)= sum over the group's rows i < rows_valid of G[i][v] h[g0 + i][:]
 // (dlog: K-slabs [Vp/64][G][64] holding G; hT: the group's rows of h as
 // K-slabs [G/64][H][64], zero past N). part: kMaxGwItems * 256 * 256 floats
-// of scratch for split tiles.
+// of scratch for split tiles. first: store instead of add. gw_bf16 (nullable):
+// also write each final sum rounded to bf16 (the last row group); keep32 = 0:
+// do not write the FP32 sums back.
 hipError_t launch_grad_weight(const Shapes& s, const void* dlog, int64_t G, const void* hT, int64_t rows_valid,
-                              float* part, int first, float* gw_f32, hipStream_t st);
+                              float* part, int first, float* gw_f32, void* gw_bf16, int keep32, hipStream_t st);
 // grad_weight's tiles: the first n_full run whole (a multiple of the CU
 // count), the rest are split `split` ways along K (split = 1: none) so that
 // they fill one round; at most kMaxGwItems split pieces.

@@ -916,9 +916,17 @@ k_gemm_grad_hidden(const u16* __restrict__ dlog, const u16* __restrict__ wT, int
 // (col0 + wn*64 + lane%16) of row 0; rows past V are skipped when CHECK. The
 // read-modify-write goes two 16-row blocks at a time with all their reads
 // issued before the adds and stores, so 32 reads per lane are in flight.
+// For the last row group, base16 (the same column of the bf16 output, or
+// null) also receives each final sum rounded to bf16, and keep32 = 0 skips
+// writing the FP32 sum back (the accumulator is then only workspace).
 template <bool CHECK>
-__device__ __forceinline__ void gw_update(const Acc& acc, float* __restrict__ base, int64_t row0, int64_t H,
-                                          int64_t V, int wm, int lane, int first) {
+__device__ __forceinline__ void gw_update(const Acc& acc, float* __restrict__ base, u16* __restrict__ base16,
+                                          int keep32, int64_t row0, int64_t H, int64_t V, int wm, int lane,
+                                          int first) {
+  auto put = [&](int64_t v, int j, float x) {
+    if (keep32) base[v * H + j * 16] = x;
+    if (base16) base16[v * H + j * 16] = f2bf(x);
+  };
   if (first) {
 #pragma unroll
     for (int i = 0; i < NB; ++i)
@@ -926,9 +934,8 @@ __device__ __forceinline__ void gw_update(const Acc& acc, float* __restrict__ ba
       for (int r = 0; r < 4; ++r) {
         const int64_t v = row0 + acc_row(wm, i, r, lane);
         if (CHECK && v >= V) continue;
-        float* dst = base + v * H;
 #pragma unroll
-        for (int j = 0; j < NBJ; ++j) dst[j * 16] = acc.v[i][j][r];
+        for (int j = 0; j < NBJ; ++j) put(v, j, acc.v[i][j][r]);
       }
     return;
   }
@@ -950,9 +957,8 @@ __device__ __forceinline__ void gw_update(const Acc& acc, float* __restrict__ ba
       for (int r = 0; r < 4; ++r) {
         const int64_t v = row0 + acc_row(wm, i0 + di, r, lane);
         if (CHECK && v >= V) continue;
-        float* dst = base + v * H;
 #pragma unroll
-        for (int j = 0; j < NBJ; ++j) dst[j * 16] = old[di][r][j] + acc.v[i0 + di][j][r];
+        for (int j = 0; j < NBJ; ++j) put(v, j, old[di][r][j] + acc.v[i0 + di][j][r]);
       }
   }
 }
@@ -985,7 +991,7 @@ __device__ __forceinline__ void tr_slot(int wave, int lane, int b, int& k, int& 
 __global__ void __launch_bounds__(NTHREADS, 1)
 k_gemm_grad_weight(const u16* __restrict__ G, int64_t slab_rows, const u16* __restrict__ hT, int nk, int64_t H,
                    int64_t V, int n_mt, int n_nt, int n_full, int split, int first, float* __restrict__ gw_f32,
-                   float* __restrict__ part) {
+                   float* __restrict__ part, u16* __restrict__ gw_bf16, int keep32) {
   __shared__ __attribute__((aligned(16))) char smem_raw[MAINLOOP_LDS];
   LDS_AS char* smem = (LDS_AS char*)smem_raw;
   int tm, tn, s0 = 0, s1 = nk, item = -1;
@@ -1035,8 +1041,9 @@ k_gemm_grad_weight(const u16* __restrict__ G, int64_t slab_rows, const u16* __re
   // the last vocabulary tile has rows past V.
   if (col0 + wn * 64 < H) {
     float* base = gw_f32 + col0 + wn * 64 + (lane & 15);
-    if (row0 + TILE <= V) gw_update<false>(acc, base, row0, H, V, wm, lane, first);
-    else gw_update<true>(acc, base, row0, H, V, wm, lane, first);
+    u16* base16 = gw_bf16 ? gw_bf16 + col0 + wn * 64 + (lane & 15) : nullptr;
+    if (row0 + TILE <= V) gw_update<false>(acc, base, base16, keep32, row0, H, V, wm, lane, first);
+    else gw_update<true>(acc, base, base16, keep32, row0, H, V, wm, lane, first);
   }
 }
 
@@ -1045,7 +1052,8 @@ k_gemm_grad_weight(const u16* __restrict__ G, int64_t slab_rows, const u16* __re
 // 256 x 4 strip of one tile (64 threads, one float4 each).
 __global__ void __launch_bounds__(64) k_gw_reduce(const float* __restrict__ part, int n_full, int split, int n_mt,
                                                   int n_nt, int64_t H, int64_t V, int first,
-                                                  float* __restrict__ gw_f32) {
+                                                  float* __restrict__ gw_f32, u16* __restrict__ gw_bf16,
+                                                  int keep32) {
   const int tile = blockIdx.y;
   int tm, tn;
   tile_from_index<GW_GROUP_M>(n_full + tile, n_mt, n_nt, tm, tn);
@@ -1057,7 +1065,13 @@ __global__ void __launch_bounds__(64) k_gw_reduce(const float* __restrict__ part
   for (int sp = 0; sp < split; ++sp)
     sum += *(const f32x4*)(part + ((int64_t)tile * split + sp) * TILE * TILE + r * TILE + c);
   f32x4* dst = (f32x4*)(gw_f32 + v * H + col);
-  *dst = first ? sum : *dst + sum;
+  const f32x4 out = first ? sum : *dst + sum;
+  if (keep32) *dst = out;
+  if (gw_bf16) {
+    u16* d16 = gw_bf16 + v * H + col;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) d16[e] = f2bf(out[e]);
+  }
 }
 
 // data[k] *= *scale (the scale read from device memory).
@@ -1198,7 +1212,7 @@ hipError_t launch_grad_hidden(const Shapes& s, const void* dlog, const void* wT,
 }
 
 hipError_t launch_grad_weight(const Shapes& s, const void* dlog, int64_t G, const void* hT, int64_t rows_valid,
-                              float* part, int first, float* gw_f32, hipStream_t st) {
+                              float* part, int first, float* gw_f32, void* gw_bf16, int keep32, hipStream_t st) {
   const int n_mt = (int)(s.Vp / TILE), n_nt = (int)((s.H + TILE - 1) / TILE);
   const int nk = (int)((rows_valid + 63) / 64);
   const int n_tiles = n_mt * n_nt;
@@ -1206,11 +1220,11 @@ hipError_t launch_grad_weight(const Shapes& s, const void* dlog, int64_t G, cons
   grad_weight_split(n_tiles, nk, device_cus(), &n_full, &split);
   hipLaunchKernelGGL(k_gemm_grad_weight, dim3((unsigned)(n_full + (n_tiles - n_full) * split)), dim3(NTHREADS), 0,
                      st, (const u16*)dlog, G, (const u16*)hT, nk, s.H, s.V, n_mt, n_nt, n_full, split, first, gw_f32,
-                     part);
+                     part, (u16*)gw_bf16, keep32);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || n_full == n_tiles) return e;
   hipLaunchKernelGGL(k_gw_reduce, dim3(TILE, (unsigned)(n_tiles - n_full)), dim3(64), 0, st, part, n_full, split,
-                     n_mt, n_nt, s.H, s.V, first, gw_f32);
+                     n_mt, n_nt, s.H, s.V, first, gw_f32, (u16*)gw_bf16, keep32);
   return hipGetLastError();
 }
 
