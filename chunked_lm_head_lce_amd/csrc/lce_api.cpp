@@ -25,7 +25,7 @@ struct Layout {
   size_t label32 = 0, n_valid = 0, status = 0, zlab = 0, lse = 0, part_m = 0, part_s = 0, chunk_acc = 0,
          tile_ctr = 0;
   // backward
-  size_t wT = 0, hT = 0, gw_part = 0, dlog = 0, gw_f32 = 0, gb_f32 = 0;
+  size_t wT = 0, hT = 0, gw_part = 0, dlog = 0, gw_f32 = 0, gb_f32 = 0, rref = 0, rowc = 0, ovf = 0;
   size_t total = 0;
 };
 
@@ -101,6 +101,9 @@ Layout make_layout(const lce_problem* p, int kind) {
     L.gw_part = take((size_t)lce::kMaxGwItems * 256 * 256 * 4);   // split grad_weight tiles
     L.dlog = take((size_t)G * s.Vp * 2);
     L.gb_f32 = take((size_t)s.Vp * 4);
+    L.rref = take((size_t)G * 4);   // the group's row references of the stored softmax numerators
+    L.rowc = take((size_t)G * 4);   // the group's dlogits row scales
+    L.ovf = take(4);                // set by the forward tiles when a row needs the retry
     if (kind == LCE_WS_BACKWARD) L.gw_f32 = take((size_t)s.V * s.H * 4);
   }
   L.total = off;
@@ -221,11 +224,13 @@ int run_label_logits(Common& c, const void* hidden, const void* weight, const vo
 // then per-row lse / NLL / chunk sums. With p_out the tiles also leave
 // exp(z - max_quarter) behind for the gradient of the same rows.
 int run_rows(Common& c, const void* hidden, const void* weight, const void* bias, int64_t g0, int64_t rows,
-             void* p_out, float* loss, float* lse_out, hipStream_t st, Tracer& tr) {
+             void* p_out, float* loss, float* lse_out, hipStream_t st, Tracer& tr, const float* rref = nullptr,
+             int* ovf = nullptr) {
   const Shapes& s = c.s;
   const int64_t rows_valid = (s.N - g0) < rows ? (s.N - g0) : rows;
   LCE_LAUNCH(tr, LCE_K_FWD_LSE, rows_valid, s.V, s.H,
-             lce::launch_fwd_tiles(s, hidden, weight, bias, g0, rows, c.part_m, c.part_s, p_out, c.tile_ctr, st));
+             lce::launch_fwd_tiles(s, hidden, weight, bias, g0, rows, c.part_m, c.part_s, p_out, c.tile_ctr, rref,
+                                   ovf, nullptr, st));
   LCE_LAUNCH(tr, LCE_K_FINALIZE_ROWS, 0, 0, 0,
              lce::launch_finalize_rows(s, c.part_m, c.part_s, g0, rows, c.zlab, c.label32, c.status,
                                        c.p->reduction, c.lse_ws, lse_out,
@@ -237,7 +242,7 @@ int run_rows(Common& c, const void* hidden, const void* weight, const void* bias
 
 extern "C" {
 
-int lce_abi_version(void) { return 102; }
+int lce_abi_version(void) { return 103; }
 
 const char* lce_status_string(int status) {
   switch (status) {
@@ -335,35 +340,60 @@ int lce_forward_backward_ex(const lce_problem* p, const void* hidden, const void
   } else {
     st = run_label_logits(c, hidden, weight, bias, stream, tr);
     if (st != LCE_OK) return st;
-    // Row groups: the logits of a group are computed once; the tiles leave
-    // exp(z - max_quarter) in dlog, the group's lse follows, and the dlogits
-    // pass turns dlog into G in place for the two gradient products.
+    // Row groups: the logits of a group are computed once. The tiles leave
+    // exp(z - r_i) in dlog, r_i the row's label logit; once the group's lse
+    // is known, k_rowscale patches the label entries and forms the row
+    // scales c_i with G = diag(c) p~'. If a row's maximum is too far above
+    // its label logit (overflow flag), the flag-gated retry launches
+    // recompute the group's p~ against r_i = lse_i; they do nothing
+    // otherwise.
     const int64_t G = group_rows(p, s);
     void* wT = ws + c.L.wT;
     void* hT = ws + c.L.hT;
     float* gw_part = (float*)(ws + c.L.gw_part);
     void* dlog = ws + c.L.dlog;
+    float* rref = (float*)(ws + c.L.rref);
+    float* rowc = (float*)(ws + c.L.rowc);
+    int* ovf = (int*)(ws + c.L.ovf);
     const int is_mean = p->reduction == LCE_REDUCTION_MEAN;
     const bool any_grad = need_gh || need_gw || need_gb;
     if (need_gh)
       LCE_LAUNCH(tr, LCE_K_TRANSPOSE, 0, 0, 0,
-                 lce::launch_transpose(weight, s.ldw, 0, s.V, s.H, wT, s.Vp, stream));
+                 lce::launch_transpose(weight, s.ldw, 0, s.V, s.H, wT, s.Vp, nullptr, stream));
     for (int64_t g0 = 0; g0 < s.Np; g0 += G) {
       const bool last = g0 + G >= s.Np;
       const int64_t Gc = (s.Np - g0) < G ? (s.Np - g0) : G;
       const int64_t rows_valid = (s.N - g0) < Gc ? (s.N - g0) : Gc;
-      st = run_rows(c, hidden, weight, bias, g0, Gc, any_grad ? dlog : nullptr, loss, lse, stream, tr);
+      if (!any_grad) {
+        st = run_rows(c, hidden, weight, bias, g0, Gc, nullptr, loss, lse, stream, tr);
+        if (st != LCE_OK) return st;
+        continue;
+      }
+      LCE_LAUNCH(tr, LCE_K_ROW_REF, 0, 0, 0,
+                 lce::launch_prep_ref(c.label32, c.zlab, g0, Gc, rref, nullptr, stream));
+      LCE_LAUNCH(tr, LCE_K_ZERO, 0, 0, 0, lce::launch_zero(ovf, 4, stream));
+      st = run_rows(c, hidden, weight, bias, g0, Gc, dlog, loss, lse, stream, tr, rref, ovf);
       if (st != LCE_OK) return st;
-      if (!any_grad) continue;
       LCE_LAUNCH(tr, LCE_K_BWD_DLOGITS, rows_valid, s.V, 0,
-                 lce::launch_dlogits(s, c.label32, c.part_m, c.lse_ws, c.n_valid, grad_scale, is_mean, row_scale, g0,
-                                     Gc, dlog, (need_gh || need_gw) ? 1 : 0, need_gb ? gb : nullptr, stream));
+                 lce::launch_rowscale(c.label32, c.zlab, c.lse_ws, rref, row_scale, c.n_valid, grad_scale, is_mean,
+                                      g0, Gc, dlog, rowc, ovf, 0, need_gb ? gb : nullptr, stream));
+      // retry, only when the overflow flag is set
+      LCE_LAUNCH(tr, LCE_K_ROW_REF, 0, 0, 0,
+                 lce::launch_prep_ref(c.label32, c.lse_ws, g0, Gc, rref, ovf, stream));
+      LCE_LAUNCH(tr, LCE_K_FWD_RETRY, 0, 0, 0,
+                 lce::launch_fwd_tiles(s, hidden, weight, bias, g0, Gc, c.part_m, c.part_s, dlog, c.tile_ctr, rref,
+                                       nullptr, ovf, stream));
+      LCE_LAUNCH(tr, LCE_K_BWD_DLOGITS, rows_valid, s.V, 0,
+                 lce::launch_rowscale(c.label32, c.zlab, c.lse_ws, rref, row_scale, c.n_valid, grad_scale, is_mean,
+                                      g0, Gc, dlog, rowc, ovf, 1, need_gb ? gb : nullptr, stream));
+      if (need_gb)
+        LCE_LAUNCH(tr, LCE_K_BIAS_SUMS, rows_valid, s.V, 0, lce::launch_bias_sums(s, dlog, rowc, Gc, gb, stream));
       if (need_gh)
         LCE_LAUNCH(tr, LCE_K_GRAD_HIDDEN, rows_valid, s.H, s.V,
-                   lce::launch_grad_hidden(s, dlog, wT, g0, Gc, grad_hidden, stream));
+                   lce::launch_grad_hidden(s, dlog, wT, g0, Gc, rowc, grad_hidden, stream));
       if (need_gw) {
         LCE_LAUNCH(tr, LCE_K_TRANSPOSE, 0, 0, 0,
-                   lce::launch_transpose(hidden, s.ldh, g0, rows_valid, s.H, hT, Gc, stream));
+                   lce::launch_transpose(hidden, s.ldh, g0, rows_valid, s.H, hT, Gc, rowc, stream));
         LCE_LAUNCH(tr, LCE_K_GRAD_WEIGHT, s.V, s.H, rows_valid,
                    lce::launch_grad_weight(s, dlog, Gc, hT, rows_valid, gw_part, (g0 == 0 && !accumulate) ? 1 : 0,
                                            gw, last ? grad_weight : nullptr,

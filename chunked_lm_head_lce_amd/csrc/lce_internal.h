@@ -23,9 +23,13 @@ hipError_t launch_prepare_labels(const int64_t* labels, int64_t N, int64_t Np, i
 // p_out is non-null, bf16 exp(z - max_quarter) into p_out, stored as K-slabs
 // [Vp/64][rows][64] (element (i, j) at ((j/64) * rows + i) * 64 + j % 64).
 // tile_ctr: 8 ints of scratch (the per-XCD tile counters, zeroed here).
+// With p_out and rref non-null the stored values are exp(z - rref[i]) for
+// rows with a finite rref (capped at e^60; a larger gap sets *ovf = 1) and
+// exp(z - max_quarter) for NaN entries. only_if (nullable): run only if
+// *only_if != 0.
 hipError_t launch_fwd_tiles(const Shapes& s, const void* hidden, const void* weight, const void* bias, int64_t g0,
                             int64_t rows, float* part_m, float* part_s, void* p_out, int* tile_ctr,
-                            hipStream_t st);
+                            const float* rref, int* ovf, const int* only_if, hipStream_t st);
 // zlab[i] = h_i . W_{y_i} + b_{y_i} for valid rows.
 hipError_t launch_label_logit(const Shapes& s, const void* hidden, const void* weight, const void* bias,
                               const int32_t* label32, float* zlab, hipStream_t st);
@@ -38,22 +42,31 @@ hipError_t launch_finalize_loss(const double* chunk_acc, int64_t T, const unsign
                                 hipStream_t st);
 // out = rows [r0, r0 + R_valid) of in [.][ld_in] (first C columns), transposed
 // and stored as K-slabs [R_pad/64][C][64]: element (c, r) at
-// ((r/64) * C + c) * 64 + r % 64; rows R_valid..R_pad-1 are zero.
+// ((r/64) * C + c) * 64 + r % 64; rows R_valid..R_pad-1 are zero. With rowc
+// non-null, row r is scaled by rowc[r] (rounded to bf16).
 hipError_t launch_transpose(const void* in, int64_t ld_in, int64_t r0, int64_t R_valid, int64_t C, void* out,
-                            int64_t R_pad, hipStream_t st);
-// dlogits of one row group from the stored exp(z - max_quarter) in dlog
-// (K-slabs [Vp/64][G][64]): G in place (when write_dlog), column sums into
-// gb_f32 (when non-null); row i also scaled by row_scale[i] when row_scale
-// is non-null.
-hipError_t launch_dlogits(const Shapes& s, const int32_t* label32, const float* part_m, const float* lse_ws,
-                          const unsigned long long* n_valid, float grad_scale, int is_mean, const float* row_scale,
-                          int64_t g0, int64_t G, void* dlog, int write_dlog, float* gb_f32, hipStream_t st);
+                            int64_t R_pad, const float* rowc, hipStream_t st);
+// Row references of one group for the stored softmax numerators: rref[i] =
+// src[g0 + i] for valid rows, NaN otherwise; only_if as above.
+hipError_t launch_prep_ref(const int32_t* label32, const float* src, int64_t g0, int64_t G, float* rref,
+                           const int* only_if, hipStream_t st);
+// Row scales rowc[i] = s row_scale_i valid_i exp(rref_i - lse_i) and the label
+// entry of each valid row of dlog (K-slabs [Vp/64][G][64]) set to
+// exp(z_y - rref_i) - exp(lse_i - rref_i). Runs when (*ovf != 0) == retry.
+// gb_f32 (nullable) receives rowc[i] times the bf16 rounding of that entry.
+hipError_t launch_rowscale(const int32_t* label32, const float* zlab, const float* lse_ws, const float* rref,
+                           const float* row_scale, const unsigned long long* n_valid, float grad_scale, int is_mean,
+                           int64_t g0, int64_t G, void* dlog, float* rowc, const int* ovf, int retry,
+                           float* gb_f32, hipStream_t st);
+// gb_f32[v] += sum_i rowc[i] dlog[i][v] over the group's G rows.
+hipError_t launch_bias_sums(const Shapes& s, const void* dlog, const float* rowc, int64_t G, float* gb_f32,
+                            hipStream_t st);
 // data[k] *= *scale (bf16 or f32 elements).
 hipError_t launch_scale(void* data, bool f32, int64_t n, const float* scale, hipStream_t st);
-// grad_hidden rows [g0, g0 + G) = dlog * wT^T over K = Vp (dlog: K-slabs
-// [Vp/64][G][64], wT: [Vp/64][H][64]).
+// grad_hidden rows [g0, g0 + G): row i = rowc[i] (dlog wT^T)_i over K = Vp
+// (dlog: K-slabs [Vp/64][G][64], wT: [Vp/64][H][64]).
 hipError_t launch_grad_hidden(const Shapes& s, const void* dlog, const void* wT, int64_t g0, int64_t G,
-                              void* grad_hidden, hipStream_t st);
+                              const float* rowc, void* grad_hidden, hipStream_t st);
 // gw (+)= sum over the group's rows i < rows_valid of G[i][v] h[g0 + i][:]
 // (dlog: K-slabs [Vp/64][G][64] holding G; hT: the group's rows of h as
 // K-slabs [G/64][H][64], zero past N). part: kMaxGwItems * 256 * 256 floats

@@ -49,6 +49,7 @@ constexpr int STAGE = 2 * OPERAND_STAGE;           // 64 KB: both operands
 constexpr int MAINLOOP_LDS = 2 * STAGE;            // 128 KB: double buffered
 constexpr float LOG2E = 1.4426950408889634f;       // log2(e): exp(x) = 2^(x log2 e)
 constexpr float LN2 = 0.6931471805599453f;         // ln(2) = 1 / log2(e)
+constexpr float REF_CAP2 = 60.f * LOG2E;           // largest exponent (base 2) of a stored p~: e^60
 // s_waitcnt immediates (gfx9 encoding: vmcnt [3:0]+[15:14], expcnt [6:4],
 // lgkmcnt [11:8]); the other counters are left at their maximum (no wait).
 constexpr int WAIT_LGKM0 = 0xC07F;   // lgkmcnt(0)
@@ -485,10 +486,13 @@ __global__ void __launch_bounds__(NTHREADS, 1)
 k_fwd_tile(const u16* __restrict__ hidden, int64_t ldh, const u16* __restrict__ weight, int64_t ldw,
            const u16* __restrict__ bias, int64_t N, int64_t V, int64_t H, int64_t g0, int64_t ld_part, int n_mt,
            int n_vt, float* __restrict__ part_m, float* __restrict__ part_s, u16* __restrict__ p_out,
-           int* __restrict__ tile_ctr) {
+           int* __restrict__ tile_ctr, const float* __restrict__ rref, int* __restrict__ ovf,
+           const int* __restrict__ only_if) {
   __shared__ __attribute__((aligned(16))) char smem_raw[MAINLOOP_LDS];
   __shared__ __attribute__((aligned(16))) u16 s_pst[STORE_P ? 8 * PST_WAVE : 8];
+  __shared__ __attribute__((aligned(16))) float s_ref[STORE_P ? 2 * TILE : 4];   // per-row references, two tiles
   __shared__ int s_next;
+  if (only_if != nullptr && *only_if == 0) return;   // a retry launch with nothing to retry
   LDS_AS char* smem = (LDS_AS char*)smem_raw;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int wm = wave >> 2, wn = wave & 3;
@@ -498,6 +502,12 @@ k_fwd_tile(const u16* __restrict__ hidden, int64_t ldh, const u16* __restrict__ 
   int tm, tn;
   if (!xcd_tile(n_mt, n_vt, (int)(blockIdx.x >> 3), tm, tn)) return;
   if (tid == 0) s_next = per_step + atomicAdd(tile_ctr + xcd, 1);
+  // The tile's 256 row references go to LDS ahead of its stage loads (one
+  // direct load by wave 0; the K loop's first wait and barrier cover it).
+  const bool use_ref = STORE_P && rref != nullptr;
+  int par = 0;
+  const uint32_t ref_lds = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(LDS_AS char*)s_ref);
+  if (use_ref && wave == 0) lds_dma16(uniform_ptr(rref + (int64_t)tm * TILE), (uint32_t)lane * 16, ref_lds);
   TileLoads t = tile_setup(hidden, ldh, BK * 2, g0 + (int64_t)tm * TILE, N, weight, ldw, BK * 2,
                            (int64_t)tn * TILE, V, smem);
   tile_prologue(t, nk);
@@ -533,6 +543,8 @@ k_fwd_tile(const u16* __restrict__ hidden, int64_t ldh, const u16* __restrict__ 
     const bool more = xcd_tile(n_mt, n_vt, k_next, tm, tn);
     bare_barrier();   // every wave is past its last read of the stage buffers (and of s_next)
     if (more) {
+      if (use_ref && wave == 0)
+        lds_dma16(uniform_ptr(rref + (int64_t)tm * TILE), (uint32_t)lane * 16, ref_lds + (uint32_t)((par ^ 1) * TILE * 4));
       t = tile_setup(hidden, ldh, BK * 2, g0 + (int64_t)tm * TILE, N, weight, ldw, BK * 2, (int64_t)tn * TILE, V,
                      smem);
       tile_prologue(t, nk);
@@ -568,12 +580,25 @@ k_fwd_tile(const u16* __restrict__ hidden, int64_t ldh, const u16* __restrict__ 
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const float ms = m[r] == -INFINITY ? 0.f : m[r];   // all columns past V: every e = 0
+        // Stored p~ = exp(z - ref): ref is the row's reference (its label
+        // logit) when it has one, else the quarter maximum. fr = exp(m - ref),
+        // capped at e^60; a valid row whose maximum lies more than 60 above
+        // its reference raises the overflow flag (the group is redone).
+        float fr = 1.f;
+        if (use_ref) {
+          const float rr = ((const LDS_AS float*)s_ref)[par * TILE + wm * 128 + i * 16 + 4 * (lane >> 4) + r];
+          if (!__builtin_isnan(rr)) {
+            const float d = ms - rr * LOG2E;
+            if (m[r] != -INFINITY && d > REF_CAP2 && ovf != nullptr) *ovf = 1;   // rare: the group is redone
+            fr = __builtin_amdgcn_exp2f(fminf(d, REF_CAP2));
+          }
+        }
         sm[r] = 0.f;
 #pragma unroll
         for (int j = 0; j < NBJ; ++j) {
           const float e = __builtin_amdgcn_exp2f(fmaf(acc.v[i][j][r], LOG2E, cbl[j] - ms));
           sm[r] += e;
-          if (STORE_P) pst[(4 * (lane >> 4) + r) * PST_LD + j * 16 + (lane & 15)] = f2bf(e);
+          if (STORE_P) pst[(4 * (lane >> 4) + r) * PST_LD + j * 16 + (lane & 15)] = f2bf(e * fr);
         }
       }
 #pragma unroll
@@ -606,6 +631,7 @@ k_fwd_tile(const u16* __restrict__ hidden, int64_t ldh, const u16* __restrict__ 
     // wave-wide rewrite of a uniform-address atomic reads the result at once.)
     asm volatile("" ::: "memory");
     if (more && tid == 0) s_next = per_step + claimed;
+    par ^= 1;
     if (!more) break;
   }
 }
@@ -746,7 +772,7 @@ __global__ void __launch_bounds__(256) k_finalize_loss(const double* __restrict_
 constexpr int TT = 128;
 __global__ void __launch_bounds__(256) k_transpose(const u16* __restrict__ in, int64_t ld_in, int64_t r0,
                                                    int64_t R_valid, int64_t C, u16* __restrict__ out,
-                                                   int64_t R_pad) {
+                                                   int64_t R_pad, const float* __restrict__ rowc) {
   __shared__ __attribute__((aligned(16))) u16 t[TT * TT];
   const int64_t cb = (int64_t)blockIdx.x * TT, rb = (int64_t)blockIdx.y * TT;
   const int tid = threadIdx.x;
@@ -757,6 +783,18 @@ __global__ void __launch_bounds__(256) k_transpose(const u16* __restrict__ in, i
   for (int r = 0; r < 8; ++r) {
     const int64_t row = rb + rk * 8 + r;
     v[r] = (row < R_valid && c0 < C) ? *(const u32x4*)(in + (r0 + row) * ld_in + c0) : (u32x4){0, 0, 0, 0};
+  }
+  if (rowc != nullptr) {     // out rows scaled by rowc[row] (bf16, round to nearest even)
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      const int64_t row = rb + rk * 8 + r;
+      const float c = row < R_valid ? rowc[row] : 0.f;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const uint32_t x = v[r][w];
+        v[r][w] = (uint32_t)f2bf(c * bf2f((u16)(x & 0xFFFF))) | ((uint32_t)f2bf(c * bf2f((u16)(x >> 16))) << 16);
+      }
+    }
   }
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
@@ -785,110 +823,118 @@ __global__ void __launch_bounds__(256) k_transpose(const u16* __restrict__ in, i
   }
 }
 
-// dlogits for one 128-row x 256-column block of a row group, from the
-// stored unnormalised softmax p~ = exp(z - max_q) (bf16, written by the
-// forward tile, max_q over the 64-column quarter q of the tile):
-// G = s valid (p~ exp(max_q - lse) - [j == y]). G
-// overwrites p~ in dlog (K-slabs [Vp/64][G][64]) when `write_dlog` (both
-// gradient products read it there); its column sums go into the FP32 bias
-// gradient. Each thread owns 8 x 8 blocks: 8 rows of one 16-byte column
-// chunk, all 8 loads issued before any use. p~ is read and G written with
-// non-temporal accesses (p~ is read once; G is read by the next product
-// kernels, not by this one), which keep them from evicting other lines from
-// L2 (the streaming loads measured 4.8% faster).
-constexpr int DL_ROWS = 128;
+// ---------------------------------------------------------------------------
+// dlogits of a row group without a pass over it. The forward tiles store
+// p~_ij = exp(z_ij - r_i) against one reference per row, r_i = z_{i,y_i} (the
+// label logit), so that
+//   G_ij = s valid_i (exp(z_ij - lse_i) - 1[j = y_i]) = c_i p~'_ij,
+//   c_i = s valid_i exp(r_i - lse_i),   p~'_ij = p~_ij - 1[j = y_i] exp(lse_i - r_i).
+// Only the label entry of each row changes (k_rowscale patches it, from the
+// FP32 label logit and lse: exp(z_y - r) - exp(lse - r), no cancellation
+// through bf16); c_i becomes a row scale of grad_hidden's output and of h^T
+// in grad_weight, and grad_bias is a c-weighted column sum of p~'
+// (k_bias_sums). A valid row whose maximum lies more than 60 above its label
+// logit would leave the range of the stored values: the forward tiles then
+// set the overflow flag, and the group's p~ is recomputed against r_i =
+// lse_i (k_prep_ref, k_fwd_tile and k_rowscale in their retry mode: every
+// stored value is then at most 1).
+// ---------------------------------------------------------------------------
+// rref[i] = src[g0 + i] for valid rows (the label logit, or lse in the retry),
+// NaN for ignored rows and rows past N (their tiles keep the quarter maximum).
+// With only_if non-null the kernel does nothing unless *only_if != 0.
+__global__ void __launch_bounds__(256) k_prep_ref(const int32_t* __restrict__ label32, const float* __restrict__ src,
+                                                  int64_t g0, int64_t G, float* __restrict__ rref,
+                                                  const int* __restrict__ only_if) {
+  if (only_if != nullptr && *only_if == 0) return;
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= G) return;
+  rref[i] = label32[g0 + i] >= 0 ? src[g0 + i] : NAN;
+}
 
-__global__ void __launch_bounds__(256)
-k_dlogits_from_p(u16* __restrict__ dlog, const float* __restrict__ part_m,
-                 const int32_t* __restrict__ label32, const float* __restrict__ lse_ws,
-                 const unsigned long long* __restrict__ n_valid, float grad_scale, int is_mean,
-                 const float* __restrict__ row_scale, int64_t V, int64_t g0, int64_t G, int write_dlog,
-                 float* __restrict__ gb_f32) {
-  __shared__ float s_f[NQ][DL_ROWS];
-  __shared__ int s_lab[DL_ROWS];
-  __shared__ float s_hot[DL_ROWS];
-  __shared__ float s_gb[8][TILE];
-  const int n_mt = (int)(G / DL_ROWS);
-  const int tm = blockIdx.x % n_mt, tn = blockIdx.x / n_mt;
-  const int64_t lrow0 = (int64_t)tm * DL_ROWS, col0 = (int64_t)tn * TILE;
-  const int tid = threadIdx.x;
+// Row scales c_i of one group and the label entries of p~' (see above).
+// retry = 0 runs unless the overflow flag is set, retry = 1 only if it is.
+__global__ void __launch_bounds__(256) k_rowscale(const int32_t* __restrict__ label32, const float* __restrict__ zlab,
+                                                  const float* __restrict__ lse_ws, const float* __restrict__ rref,
+                                                  const float* __restrict__ row_scale,
+                                                  const unsigned long long* __restrict__ n_valid, float grad_scale,
+                                                  int is_mean, int64_t g0, int64_t G, u16* __restrict__ dlog,
+                                                  float* __restrict__ rowc, const int* __restrict__ ovf, int retry,
+                                                  float* __restrict__ gb_f32) {
+  if ((*ovf != 0) != (retry != 0)) return;
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= G) return;
+  const int64_t row = g0 + i;
+  const int lab = label32[row];
+  if (lab < 0) {                       // ignored rows and rows past N
+    rowc[i] = 0.f;
+    return;
+  }
   float scale = grad_scale;
   if (is_mean) {
     const unsigned long long nv = *n_valid;
     scale = grad_scale / (float)(nv > 0 ? nv : 1ull);
   }
-  if (tid < DL_ROWS) {
-    const int64_t row = g0 + lrow0 + tid;
-    const int lab = label32[row];
-    const float lse = lse_ws[row];
-    const bool valid = lab >= 0;                 // false for rows past N
-    const float rs = valid ? scale * (row_scale != nullptr ? row_scale[row] : 1.f) : 0.f;
-#pragma unroll
-    for (int h = 0; h < NQ; ++h) {
-      const float mh = part_m[(int64_t)(NQ * tn + h) * G + lrow0 + tid];
-      s_f[h][tid] = (valid && mh != -INFINITY) ? rs * exp_fast(mh - lse) : 0.f;
-    }
-    const int64_t lc = valid ? (int64_t)lab - col0 : -1;
-    s_lab[tid] = (lc >= 0 && lc < TILE) ? (int)lc : -1;
-    s_hot[tid] = rs;
-  }
+  const float r = rref[i], lse = lse_ws[row];
+  const float c = scale * (row_scale != nullptr ? row_scale[row] : 1.f) * expf(r - lse);
+  const float pl = expf(zlab[row] - r) - expf(lse - r);
+  const u16 pb = f2bf(pl);
+  rowc[i] = c;
+  dlog[((int64_t)(lab >> 6) * G + i) * 64 + (lab & 63)] = pb;
+  // grad_bias sums the stored (bf16) entries; the label entry's rounding is
+  // added back here, so that its term is exact to FP32
+  if (gb_f32 != nullptr) atomicAdd(gb_f32 + lab, c * (pl - bf2f(pb)));
+}
+
+// grad_bias += sum_i c_i p~'[i][v] over one group: one workgroup per 64-id
+// K-slab and 1024 rows (a contiguous 128 KB block of the slab), 8 ids x 32
+// rows per thread, then 32 partial sums per id added through LDS.
+constexpr int BS_ROWS = 1024;
+__global__ void __launch_bounds__(256) k_bias_sums(const u16* __restrict__ dlog, const float* __restrict__ rowc,
+                                                   int64_t G, int64_t V, float* __restrict__ gb_f32) {
+  __shared__ float s_c[BS_ROWS];
+  __shared__ float s_sum[32][64];
+  const int tid = threadIdx.x;
+  const int64_t slab = blockIdx.x, r0 = (int64_t)blockIdx.y * BS_ROWS;
+  for (int k = tid; k < BS_ROWS; k += 256) s_c[k] = r0 + k < G ? rowc[r0 + k] : 0.f;
   __syncthreads();
-  const int cb = tid & 31;                 // column chunk (8 columns), fixed per thread
-  const int qtr = cb >> 3;                 // 64-column quarter of the chunk
-  float colsum[8];
+  const int ch = tid & 7, rg = tid >> 3;       // 8 ids, one of 32 row lanes
+  const u16* base = dlog + (slab * G + r0) * 64 + ch * 8;
+  float acc[8];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) colsum[e] = 0.f;
+  for (int e = 0; e < 8; ++e) acc[e] = 0.f;
 #pragma unroll 1
-  for (int it = 0; it < DL_ROWS / 64; ++it) {
-    const int rb = it * 8 + (tid >> 5);    // row block (8 rows)
-    u16* src = dlog + (((col0 >> 6) + qtr) * G + lrow0 + rb * 8) * 64 + (cb & 7) * 8;
-    u32x4 pv[8];
+  for (int k = 0; k < BS_ROWS / 32; k += 8) {
+    u32x4 v[8];
 #pragma unroll
-    for (int r = 0; r < 8; ++r) pv[r] = __builtin_nontemporal_load((const u32x4*)(src + r * 64));   // read once
-    float d[8][8];                         // [row][col]
-#pragma unroll
-    for (int r = 0; r < 8; ++r) {
-      const int rl = rb * 8 + r;
-      const float f = s_f[qtr][rl];
-      const int lc = s_lab[rl];
-      const float hot = s_hot[rl];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const uint32_t w = pv[r][e >> 1];
-        const float pe = bf2f((u16)((e & 1) ? (w >> 16) : (w & 0xFFFF)));
-        const float g = f * pe - ((lc == cb * 8 + e) ? hot : 0.f);
-        d[r][e] = g;
-        colsum[e] += g;
-      }
+    for (int u = 0; u < 8; ++u) {
+      const int64_t row = rg + 32 * (k + u);
+      v[u] = r0 + row < G ? __builtin_nontemporal_load((const u32x4*)(base + row * 64)) : (u32x4){0, 0, 0, 0};
     }
-    if (write_dlog) {
 #pragma unroll
-      for (int r = 0; r < 8; ++r) {
-        u32x4 o;
+    for (int u = 0; u < 8; ++u) {
+      const float c = s_c[rg + 32 * (k + u)];
 #pragma unroll
-        for (int w = 0; w < 4; ++w) o[w] = (uint32_t)f2bf(d[r][2 * w]) | ((uint32_t)f2bf(d[r][2 * w + 1]) << 16);
-        __builtin_nontemporal_store(o, (u32x4*)(src + r * 64));
-      }
+      for (int e = 0; e < 8; ++e) acc[e] = fmaf(c, bf2f((u16)((e & 1) ? (v[u][e >> 1] >> 16) : (v[u][e >> 1] & 0xFFFF))), acc[e]);
     }
   }
-  if (gb_f32) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) s_gb[tid >> 5][cb * 8 + e] = colsum[e];
-  }
+  for (int e = 0; e < 8; ++e) s_sum[rg][ch * 8 + e] = acc[e];
   __syncthreads();
-  if (gb_f32 && col0 + tid < V) {
+  if (tid < 64) {
     float sum = 0.f;
-#pragma unroll
-    for (int k = 0; k < 8; ++k) sum += s_gb[k][tid];
-    atomicAdd(gb_f32 + col0 + tid, sum);
+#pragma unroll 8
+    for (int k = 0; k < 32; ++k) sum += s_sum[k][tid];
+    const int64_t col = slab * 64 + tid;
+    if (col < V) atomicAdd(gb_f32 + col, sum);
   }
 }
 
-// grad_hidden rows of one group: C = dlog * (W^T)^T over K = Vp, cast to bf16;
-// dlog is stored as K-slabs [Vp/64][G][64], W^T as [Vp/64][H][64].
+// grad_hidden rows of one group: row i = c_i (p~' W)_i over K = Vp, cast to
+// bf16; p~' is stored as K-slabs [Vp/64][G][64], W^T as [Vp/64][H][64].
 __global__ void __launch_bounds__(NTHREADS, 1)
 k_gemm_grad_hidden(const u16* __restrict__ dlog, const u16* __restrict__ wT, int64_t Vp, int64_t H,
-                   int64_t N, int64_t g0, int64_t G, int n_mt, int n_nt, u16* __restrict__ grad_hidden) {
+                   int64_t N, int64_t g0, int64_t G, int n_mt, int n_nt, const float* __restrict__ rowc,
+                   u16* __restrict__ grad_hidden) {
   __shared__ __attribute__((aligned(16))) char smem_raw[MAINLOOP_LDS];
   LDS_AS char* smem = (LDS_AS char*)smem_raw;
   int tm, tn;
@@ -904,10 +950,11 @@ k_gemm_grad_hidden(const u16* __restrict__ dlog, const u16* __restrict__ wT, int
     for (int r = 0; r < 4; ++r) {
       const int64_t row = g0 + lrow0 + acc_row(wm, i, r, lane);
       if (row >= N) continue;
+      const float c = rowc[lrow0 + acc_row(wm, i, r, lane)];
 #pragma unroll
       for (int j = 0; j < NBJ; ++j) {
         const int64_t col = col0 + acc_col(wn, j, lane);
-        if (col < H) grad_hidden[row * H + col] = f2bf(acc.v[i][j][r]);
+        if (col < H) grad_hidden[row * H + col] = f2bf(c * acc.v[i][j][r]);
       }
     }
 }
@@ -1143,7 +1190,7 @@ static int persistent_grid(int64_t ntiles) {
 
 hipError_t launch_fwd_tiles(const Shapes& s, const void* hidden, const void* weight, const void* bias, int64_t g0,
                             int64_t rows, float* part_m, float* part_s, void* p_out, int* tile_ctr,
-                            hipStream_t st) {
+                            const float* rref, int* ovf, const int* only_if, hipStream_t st) {
   const int n_mt = (int)(rows / TILE), n_vt = (int)(s.Vp / TILE);
   const int nb = persistent_grid((int64_t)n_mt * n_vt);
   if (nb == 0) return hipSuccess;
@@ -1152,11 +1199,12 @@ hipError_t launch_fwd_tiles(const Shapes& s, const void* hidden, const void* wei
   const dim3 grid((unsigned)nb), block(NTHREADS);
   if (p_out)
     hipLaunchKernelGGL(k_fwd_tile<true>, grid, block, 0, st, (const u16*)hidden, s.ldh, (const u16*)weight, s.ldw,
-                       (const u16*)bias, s.N, s.V, s.H, g0, rows, n_mt, n_vt, part_m, part_s, (u16*)p_out, tile_ctr);
+                       (const u16*)bias, s.N, s.V, s.H, g0, rows, n_mt, n_vt, part_m, part_s, (u16*)p_out, tile_ctr,
+                       rref, ovf, only_if);
   else
     hipLaunchKernelGGL(k_fwd_tile<false>, grid, block, 0, st, (const u16*)hidden, s.ldh, (const u16*)weight,
                        s.ldw, (const u16*)bias, s.N, s.V, s.H, g0, rows, n_mt, n_vt, part_m, part_s, (u16*)nullptr,
-                       tile_ctr);
+                       tile_ctr, (const float*)nullptr, (int*)nullptr, only_if);
   return hipGetLastError();
 }
 
@@ -1187,27 +1235,41 @@ hipError_t launch_finalize_loss(const double* chunk_acc, int64_t T, const unsign
 }
 
 hipError_t launch_transpose(const void* in, int64_t ld_in, int64_t r0, int64_t R_valid, int64_t C, void* out,
-                            int64_t R_pad, hipStream_t st) {
+                            int64_t R_pad, const float* rowc, hipStream_t st) {
   dim3 grid((unsigned)((C + TT - 1) / TT), (unsigned)((R_pad + TT - 1) / TT));
   hipLaunchKernelGGL(k_transpose, grid, dim3(256), 0, st, (const u16*)in, ld_in, r0, R_valid, C, (u16*)out,
-                     R_pad);
+                     R_pad, rowc);
   return hipGetLastError();
 }
 
-hipError_t launch_dlogits(const Shapes& s, const int32_t* label32, const float* part_m, const float* lse_ws,
-                          const unsigned long long* n_valid, float grad_scale, int is_mean, const float* row_scale,
-                          int64_t g0, int64_t G, void* dlog, int write_dlog, float* gb_f32, hipStream_t st) {
-  const int n_mt = (int)(G / DL_ROWS), n_vt = (int)(s.Vp / TILE);
-  hipLaunchKernelGGL(k_dlogits_from_p, dim3((unsigned)(n_mt * n_vt)), dim3(256), 0, st, (u16*)dlog,
-                     part_m, label32, lse_ws, n_valid, grad_scale, is_mean, row_scale, s.V, g0, G, write_dlog, gb_f32);
+hipError_t launch_prep_ref(const int32_t* label32, const float* src, int64_t g0, int64_t G, float* rref,
+                           const int* only_if, hipStream_t st) {
+  hipLaunchKernelGGL(k_prep_ref, dim3((unsigned)((G + 255) / 256)), dim3(256), 0, st, label32, src, g0, G, rref,
+                     only_if);
+  return hipGetLastError();
+}
+
+hipError_t launch_rowscale(const int32_t* label32, const float* zlab, const float* lse_ws, const float* rref,
+                           const float* row_scale, const unsigned long long* n_valid, float grad_scale, int is_mean,
+                           int64_t g0, int64_t G, void* dlog, float* rowc, const int* ovf, int retry,
+                           float* gb_f32, hipStream_t st) {
+  hipLaunchKernelGGL(k_rowscale, dim3((unsigned)((G + 255) / 256)), dim3(256), 0, st, label32, zlab, lse_ws, rref,
+                     row_scale, n_valid, grad_scale, is_mean, g0, G, (u16*)dlog, rowc, ovf, retry, gb_f32);
+  return hipGetLastError();
+}
+
+hipError_t launch_bias_sums(const Shapes& s, const void* dlog, const float* rowc, int64_t G, float* gb_f32,
+                            hipStream_t st) {
+  const dim3 grid((unsigned)(s.Vp / 64), (unsigned)((G + BS_ROWS - 1) / BS_ROWS));
+  hipLaunchKernelGGL(k_bias_sums, grid, dim3(256), 0, st, (const u16*)dlog, rowc, G, s.V, gb_f32);
   return hipGetLastError();
 }
 
 hipError_t launch_grad_hidden(const Shapes& s, const void* dlog, const void* wT, int64_t g0, int64_t G,
-                              void* grad_hidden, hipStream_t st) {
+                              const float* rowc, void* grad_hidden, hipStream_t st) {
   const int n_mt = (int)(G / TILE), n_nt = (int)((s.H + TILE - 1) / TILE);
   hipLaunchKernelGGL(k_gemm_grad_hidden, dim3((unsigned)(n_mt * n_nt)), dim3(NTHREADS), 0, st,
-                     (const u16*)dlog, (const u16*)wT, s.Vp, s.H, s.N, g0, G, n_mt, n_nt, (u16*)grad_hidden);
+                     (const u16*)dlog, (const u16*)wT, s.Vp, s.H, s.N, g0, G, n_mt, n_nt, rowc, (u16*)grad_hidden);
   return hipGetLastError();
 }
 

@@ -130,14 +130,20 @@ int lce_forward_backward(const lce_problem* p, const void* hidden, const void* w
  * used; `count` returns the number of pairs recorded. Results are otherwise
  * identical to the untraced call.
  * LCE_K_FWD_LSE is the logits-tile kernel with the log-sum-exp epilogue (in
- * lce_forward_backward it also stores each row group's exp(z - max) tiles);
- * LCE_K_BWD_DLOGITS turns those stored tiles into the bf16 dlogits of the
- * group (an element-wise pass, no product); LCE_K_LABEL_LOGIT gathers each
- * valid row's label logit h_i . W_{y_i} + b_{y_i}. */
+ * lce_forward_backward it also stores each row group's softmax numerators
+ * exp(z - r_i), r_i the row's label logit); LCE_K_BWD_DLOGITS forms the
+ * group's dlogits from them (per-row scales and one patched entry per row;
+ * no pass over the stored tiles); LCE_K_LABEL_LOGIT gathers each valid
+ * row's label logit h_i . W_{y_i} + b_{y_i}; LCE_K_ROW_REF prepares a
+ * group's row references; LCE_K_FWD_RETRY recomputes a group's stored
+ * numerators against r_i = lse_i when a row's maximum lies more than 60
+ * above its label logit (otherwise it returns at once); LCE_K_BIAS_SUMS
+ * adds the group's grad_bias column sums. */
 typedef enum {
   LCE_K_ZERO = 0, LCE_K_PREPARE_LABELS = 1, LCE_K_FWD_LSE = 2, LCE_K_FINALIZE_ROWS = 3,
   LCE_K_FINALIZE_LOSS = 4, LCE_K_TRANSPOSE = 5, LCE_K_BWD_DLOGITS = 6, LCE_K_GRAD_HIDDEN = 7,
-  LCE_K_GRAD_WEIGHT = 8, LCE_K_CAST = 9, LCE_K_LABEL_LOGIT = 10, LCE_K_COUNT = 11
+  LCE_K_GRAD_WEIGHT = 8, LCE_K_CAST = 9, LCE_K_LABEL_LOGIT = 10, LCE_K_ROW_REF = 11, LCE_K_FWD_RETRY = 12,
+  LCE_K_BIAS_SUMS = 13, LCE_K_COUNT = 14
 } lce_kernel_kind;
 
 typedef struct {

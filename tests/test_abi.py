@@ -48,7 +48,7 @@ def test_exports_every_declared_function(lib):
 
 
 def test_version_and_strings(lib):
-    assert lib.lce_abi_version() == 102
+    assert lib.lce_abi_version() == 103
     for code in range(6):
         assert _lib.status_string(code) != "unknown status"
     assert _lib.status_string(99) == "unknown status"

@@ -109,6 +109,34 @@ def test_row_groups_match(cuda):
         check_all(out, ref, inp, "sum")
 
 
+@pytest.mark.parametrize("g", [256, 0])
+def test_far_label_logit_retry(cuda, g):
+    """Rows whose largest logit lies far above their label logit (over 60):
+    the stored softmax numerators would leave their range, so the group is
+    recomputed against the row's lse. The results must not notice."""
+    import dataclasses
+    from lce_inputs import bf16_bits
+    inp = make_case(700, 128, 1500, seed=23, bias_std=0.05, ignore_frac=0.1)
+    h = inp.hidden_f32().copy()
+    w = inp.weight_f32().copy()
+    y = inp.labels.copy()
+    # rows 5 and 600 (different row groups at 256 rows per group): logit of
+    # id 7 is 128 * 1.0 = 128, label id 9 has logit 0
+    for r in (5, 600):
+        h[r, :] = 1.0
+        y[r] = 9
+    w[7, :] = 1.0
+    w[9, :] = 0.0
+    inp = dataclasses.replace(inp, hidden_bits=bf16_bits(h), weight_bits=bf16_bits(w), labels=y)
+    hd, wd, bd, yd = to_device(inp, cuda)
+    say(f"[gpu] far label logit, rows_in_flight={g}")
+    out = lce.lce_forward_backward(hd, wd, bd, yd, rows_in_flight=g)
+    torch.cuda.synchronize()
+    ref = oracle_of(inp)
+    assert ref.row_loss[5] > 100 and ref.row_loss[600] > 100
+    check_all(out, ref, inp, "sum")
+
+
 def test_strided_hidden_and_weight(cuda):
     inp = make_case(300, 128, 700, seed=13, bias_std=0.05)
     hd, wd, bd, yd = to_device(inp, cuda)

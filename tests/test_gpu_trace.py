@@ -65,9 +65,12 @@ def test_traced_forward_backward_matches_untraced(cuda):
         assert int(a.n_valid.item()) == int(b.n_valid.item())
         names = [_lib.KERNEL_KINDS[kinds[i]] for i in range(t.count)]
         groups = 3
-        # one forward tile launch, dlogits pass, grad_hidden and grad_weight launch per row group
-        for k in ("fwd_lse", "bwd_dlogits", "grad_hidden", "grad_weight", "finalize_rows"):
-            assert names.count(k) == groups, (k, names)
+        # per row group: the forward tiles, their retry (a no-op here), the
+        # row scales (and their retry), both row-reference steps, the bias
+        # sums and the two gradient products
+        for k, per_group in (("fwd_lse", 1), ("fwd_retry", 1), ("bwd_dlogits", 2), ("row_ref", 2),
+                             ("bias_sums", 1), ("grad_hidden", 1), ("grad_weight", 1), ("finalize_rows", 1)):
+            assert names.count(k) == per_group * groups, (k, names)
         assert names.count("label_logit") == 1 and names.count("finalize_loss") == 1
         # product dims: grad_hidden rows x H x V, grad_weight V x H x the group's valid rows
         valid_rows = [g, g, n - 2 * g]
