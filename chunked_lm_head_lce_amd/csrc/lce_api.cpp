@@ -221,8 +221,8 @@ int run_label_logits(Common& c, const void* hidden, const void* weight, const vo
 }
 
 // Logits tiles with the online log-sum-exp epilogue for rows [g0, g0+rows),
-// then per-row lse / NLL / chunk sums. With p_out the tiles also leave
-// exp(z - max_quarter) behind for the gradient of the same rows.
+// then per-row lse / NLL / chunk sums. With p_out the tiles also leave the
+// softmax numerators exp(z - rref_i) behind for the gradient of the same rows.
 int run_rows(Common& c, const void* hidden, const void* weight, const void* bias, int64_t g0, int64_t rows,
              void* p_out, float* loss, float* lse_out, hipStream_t st, Tracer& tr, const float* rref = nullptr,
              int* ovf = nullptr) {

@@ -20,7 +20,7 @@ hipError_t launch_prepare_labels(const int64_t* labels, int64_t N, int64_t Np, i
                                  hipStream_t st);
 // Forward tiles for rows [g0, g0 + rows) (rows a multiple of 256): quarter-tile
 // (max, sumexp) partials into part_m/part_s [4 * Vp/256][rows] and, when
-// p_out is non-null, bf16 exp(z - max_quarter) into p_out, stored as K-slabs
+// p_out is non-null, bf16 softmax numerators into p_out, stored as K-slabs
 // [Vp/64][rows][64] (element (i, j) at ((j/64) * rows + i) * 64 + j % 64).
 // tile_ctr: 8 ints of scratch (the per-XCD tile counters, zeroed here).
 // With p_out and rref non-null the stored values are exp(z - rref[i]) for

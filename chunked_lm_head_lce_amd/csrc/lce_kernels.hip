@@ -14,10 +14,11 @@
 // and epilogues:
 //   z tile       X = hidden rows,  Y = weight rows,  K = H
 //                (per backward row group the epilogue also keeps bf16
-//                exp(z - max), which an element-wise pass turns into G)
-//   grad_hidden  X = G,            Y = W^T,          K = Vp
-//   grad_weight  X = G^T,          Y = h^T,          K = the group's rows
-// Operands are K-contiguous in memory except G in grad_weight, which is read
+//                p~ = exp(z - r_i), r_i the row's label logit; with one
+//                patched entry per row and a row scale c, G = diag(c) p~')
+//   grad_hidden  X = p~',          Y = W^T,          K = Vp   (rows scaled by c)
+//   grad_weight  X = p~'^T,        Y = (c h)^T,      K = the group's rows
+// Operands are K-contiguous in memory except p~' in grad_weight, which is read
 // K-major and transposed by the LDS reads (FragAT). The backward operands
 // are written by this library's own passes, so they are stored as K-slabs:
 // [K/64][rows][64], each 64-deep stage of a 256-row tile one contiguous
@@ -462,11 +463,12 @@ constexpr int PST_WAVE = 16 * PST_LD;          // u16 per wave
 // the epilogue to each row's (max, sum exp(z - max)) over each wave's
 // 64-column quarter of the tile (part index NQ*tile + quarter). z never
 // leaves registers. With STORE_P (backward row groups) the tile also writes
-// the bf16 unnormalised softmax exp(z - max_quarter) into p (K-slabs
-// [Vp/64][ld_part][64]); the dlogits pass turns it into G once the row's lse
-// is known, so the logits are computed only once per call. Columns past V
-// count as z = -inf (p = 0); a quarter with no column below V stores
-// max = -inf and sum = 0.
+// the bf16 unnormalised softmax exp(z - r_i) into p (K-slabs
+// [Vp/64][ld_part][64]), r_i the row's reference from rref (its label logit,
+// or its lse in the retry; see k_rowscale), or the quarter maximum where
+// rref is NaN (ignored rows, rows past N); the logits are computed only once
+// per call. Columns past V count as z = -inf (p = 0); a quarter with no
+// column below V stores max = -inf and sum = 0.
 //
 // Persistent: one workgroup per CU takes tiles of its XCD's range
 // (xcd_tile) and issues the next tile's first loads before this tile's
