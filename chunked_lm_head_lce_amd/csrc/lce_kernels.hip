@@ -459,6 +459,15 @@ __global__ void __launch_bounds__(256) k_prepare_labels(const int64_t* __restric
 constexpr int PST_LD = 72;                     // u16 per staged row
 constexpr int PST_WAVE = 16 * PST_LD;          // u16 per wave
 
+// 16 x the lane index, computed where it is used: kept live across the K
+// loop it would be spilled, and its reload waits for every store in flight.
+__device__ __forceinline__ uint32_t lane_x16() {
+  uint32_t v;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0\n\tv_lshlrev_b32 %0, 4, %0"
+               : "=v"(v));
+  return v;
+}
+
 // Forward tiles: z = h W^T + b for 256 rows x 256 vocabulary ids, reduced in
 // the epilogue to each row's (max, sum exp(z - max)) over each wave's
 // 64-column quarter of the tile (part index NQ*tile + quarter). z never
@@ -509,7 +518,7 @@ k_fwd_tile(const u16* __restrict__ hidden, int64_t ldh, const u16* __restrict__ 
   const bool use_ref = STORE_P && rref != nullptr;
   int par = 0;
   const uint32_t ref_lds = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(LDS_AS char*)s_ref);
-  if (use_ref && wave == 0) lds_dma16(uniform_ptr(rref + (int64_t)tm * TILE), (uint32_t)lane * 16, ref_lds);
+  if (use_ref && wave == 0) lds_dma16(uniform_ptr(rref + (int64_t)tm * TILE), lane_x16(), ref_lds);
   TileLoads t = tile_setup(hidden, ldh, BK * 2, g0 + (int64_t)tm * TILE, N, weight, ldw, BK * 2,
                            (int64_t)tn * TILE, V, smem);
   tile_prologue(t, nk);
@@ -546,7 +555,7 @@ k_fwd_tile(const u16* __restrict__ hidden, int64_t ldh, const u16* __restrict__ 
     bare_barrier();   // every wave is past its last read of the stage buffers (and of s_next)
     if (more) {
       if (use_ref && wave == 0)
-        lds_dma16(uniform_ptr(rref + (int64_t)tm * TILE), (uint32_t)lane * 16, ref_lds + (uint32_t)((par ^ 1) * TILE * 4));
+        lds_dma16(uniform_ptr(rref + (int64_t)tm * TILE), lane_x16(), ref_lds + (uint32_t)((par ^ 1) * TILE * 4));
       t = tile_setup(hidden, ldh, BK * 2, g0 + (int64_t)tm * TILE, N, weight, ldw, BK * 2, (int64_t)tn * TILE, V,
                      smem);
       tile_prologue(t, nk);
