@@ -109,8 +109,8 @@ def test_row_groups_match(cuda):
         check_all(out, ref, inp, "sum")
 
 
-@pytest.mark.parametrize("g", [256, 0])
-def test_far_label_logit_retry(cuda, g):
+@pytest.mark.parametrize("g,reduction", [(256, "sum"), (0, "sum"), (256, "mean")])
+def test_far_label_logit_retry(cuda, g, reduction):
     """Rows whose largest logit lies far above their label logit (over 60):
     the stored softmax numerators would leave their range, so the group is
     recomputed against the row's lse. The results must not notice."""
@@ -129,12 +129,14 @@ def test_far_label_logit_retry(cuda, g):
     w[9, :] = 0.0
     inp = dataclasses.replace(inp, hidden_bits=bf16_bits(h), weight_bits=bf16_bits(w), labels=y)
     hd, wd, bd, yd = to_device(inp, cuda)
-    say(f"[gpu] far label logit, rows_in_flight={g}")
-    out = lce.lce_forward_backward(hd, wd, bd, yd, rows_in_flight=g)
+    say(f"[gpu] far label logit, rows_in_flight={g}, {reduction}")
+    out = lce.lce_forward_backward(hd, wd, bd, yd, rows_in_flight=g, reduction=reduction)
     torch.cuda.synchronize()
-    ref = oracle_of(inp)
+    ref = oracle_of(inp, reduction=reduction)
+    # without the retry these rows' stored values would be capped at e^60
+    # and their gradients off by a factor of about e^-68
     assert ref.row_loss[5] > 100 and ref.row_loss[600] > 100
-    check_all(out, ref, inp, "sum")
+    check_all(out, ref, inp, reduction)
 
 
 def test_strided_hidden_and_weight(cuda):
