@@ -254,6 +254,40 @@ def rows_reference(hidden, weight, bias, labels, rows, *, n_valid: int,
     return lse, row_loss, g @ w64
 
 
+def label_logits_rows(hidden, weight, bias, labels, rows) -> np.ndarray:
+    """z_{i, y_i} = h_i . W_{y_i} + b_{y_i} (float64) for the given rows, whose
+    labels must be valid: the same entry of z = h W^T + b as ``_label_logits``
+    picks from materialised logits, without forming the other V - 1."""
+    rows = np.asarray(rows)
+    lab = np.asarray(labels, dtype=np.int64)[rows]
+    h64 = np.asarray(hidden[rows], dtype=np.float64)
+    w64 = np.asarray(weight[lab], dtype=np.float64)
+    zy = np.einsum("ij,ij->i", h64, w64)
+    if bias is not None:
+        zy = zy + np.asarray(bias, dtype=np.float64)[lab]
+    return zy
+
+
+def loss_sum_from_lse(hidden, weight, bias, labels, lse_all, *, ignore_index: int = IGNORE_INDEX,
+                      block_rows: int = 8192) -> tuple[float, int]:
+    """(sum_i l_i, n_valid) from every row's lse (``lse_rows_blocked``): l_i =
+    valid_i (lse_i - z_{i, y_i}), the per-token cross-entropy of the pages
+    summed over all rows (LlamaFactory section 4, ``reduction="none"`` then a
+    sum). Used for the full-size workloads, where [N, V] does not fit; the
+    label logits are gathered one block of rows at a time (host memory only).
+    ``hidden`` and ``weight`` may be any objects whose row indexing returns
+    float arrays and that have a ``shape``."""
+    labels = np.asarray(labels, dtype=np.int64)
+    valid = valid_rows(labels, np.shape(weight)[0], ignore_index)
+    rows = np.flatnonzero(valid)
+    lse_all = np.asarray(lse_all, dtype=np.float64)
+    row_loss = np.zeros(labels.shape[0])
+    for s in range(0, rows.shape[0], block_rows):
+        r = rows[s:s + block_rows]
+        row_loss[r] = lse_all[r] - label_logits_rows(hidden, weight, bias, labels, r)
+    return float(np.sum(row_loss)), int(valid.sum())
+
+
 def cols_reference(hidden, weight, bias, labels, lse_all, cols, *, n_valid: int,
                    ignore_index: int = IGNORE_INDEX, reduction: str = "sum",
                    grad_scale=1.0, block_rows: int = 8192):

@@ -169,6 +169,69 @@ def test_chunk_size_invariance(reduction):
         assert math.fsum(ch.chunk_loss) == pytest.approx(math.fsum(full.row_loss), rel=1e-12)
 
 
+@pytest.mark.parametrize("n", [37, 64, 1])
+def test_chunk_sums_match_the_chunk_loop(n):
+    """forward()'s per-chunk sums (chunk k = rows [k c, min((k+1) c, N)), the
+    last one ragged) against the pages' chunk loop, which forms each chunk's
+    loss from that chunk's own logits (LlamaFactory section 4), element by
+    element; and against the closed form for W = 0, b = 0, where every valid
+    row's loss is ln V, so chunk k sums to ln V times its valid rows."""
+    v = 19
+    h, w, b, y = _case(n, 7, v, seed=20 + n, bias=True, ignore_frac=0.3)
+    for c in sorted({1, 3, 7, n, 1000}):
+        fw = O.forward(h, w, b, y, chunk_rows=c)
+        ch = O.chunked_forward_backward(h, w, b, y, c)
+        assert len(fw.chunk_loss) == len(ch.chunk_loss) == -(-n // c)
+        np.testing.assert_allclose(fw.chunk_loss, ch.chunk_loss, rtol=1e-12, atol=1e-13)
+        z = O.forward(h, np.zeros_like(w), np.zeros(v), y, chunk_rows=c)
+        valid = (y != IGNORE_INDEX).astype(np.float64)
+        expect = [valid[s:s + c].sum() * math.log(v) for s in range(0, n, c)]
+        np.testing.assert_allclose(z.chunk_loss, expect, rtol=1e-13, atol=1e-13)
+
+
+def test_make_golden_matches_forward():
+    """The stored-value script's arithmetic (row-blocked lse, label-logit
+    gather, loss sum) on a small workload with a bias, against the oracle's
+    materialised-logits forward pass."""
+    from oracle import make_golden
+    inp = make_case(700, 24, 300, seed=7, bias_std=0.5, labels="zipf", ignore_frac=0.1, weight_std=0.3)
+    lse, meta = make_golden.compute(inp)
+    ref = O.forward(inp.hidden_f32(), inp.weight_f32(), inp.bias_f32(), inp.labels, reduction="sum")
+    np.testing.assert_allclose(lse, ref.lse, rtol=1e-13)
+    assert meta["n_valid"] == ref.n_valid == 700 - 70
+    assert meta["loss_sum"] == pytest.approx(ref.loss, rel=1e-12)
+    assert meta["inputs_sha256"] == inp.digest()
+
+
+class _Bf16Rows:
+    """Rows of a bf16 bit-pattern matrix, converted to float32 only when indexed."""
+
+    def __init__(self, bits):
+        self.bits = bits
+        self.shape = bits.shape
+
+    def __getitem__(self, idx):
+        from lce_inputs import bits_to_f32
+        return bits_to_f32(self.bits[idx])
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("name", ["qwen3_4b_32k", "qwen3_8b_1m_shard", "qwen3_4b_160k"])
+def test_stored_golden_values_follow_from_the_oracle(name):
+    """The stored full-size loss sums are the oracle's: recomputed here from
+    the stored lse with the pinned label-logit gather (the lse pass itself is
+    pinned by test_make_golden_matches_forward on a small case and re-checked
+    on a row subset by the GPU tests)."""
+    meta = json.load(open(os.path.join(GOLDEN, f"{name}.json")))
+    lse = np.load(os.path.join(GOLDEN, f"lse_{name}.npy"))
+    inp = make_inputs(WORKLOADS[name])
+    assert inp.digest() == meta["inputs_sha256"]
+    loss_sum, n_valid = O.loss_sum_from_lse(_Bf16Rows(inp.hidden_bits), _Bf16Rows(inp.weight_bits),
+                                            inp.bias_f32(), inp.labels, lse)
+    assert n_valid == meta["n_valid"]
+    assert loss_sum == pytest.approx(meta["loss_sum"], rel=1e-12)
+
+
 def test_ignored_rows_contribute_nothing():
     n, hd, v = 30, 5, 12
     h, w, b, y = _case(n, hd, v, seed=4, bias=True, ignore_frac=0.3)
@@ -334,6 +397,43 @@ def test_planted_mistakes_are_caught(monkeypatch, name):
     except AssertionError:
         caught = True
     assert caught, f"planted mistake {name} was not caught"
+
+
+def _drop_last_chunk(row_loss, chunk_rows):
+    n = row_loss.shape[0]
+    return np.array([row_loss[s:s + chunk_rows].sum() for s in range(0, n - chunk_rows + 1, chunk_rows)])
+
+
+def _shifted_chunks(row_loss, chunk_rows):
+    n = row_loss.shape[0]
+    return np.array([row_loss[s + 1:s + chunk_rows + 1].sum() for s in range(0, n, chunk_rows)])
+
+
+@pytest.mark.parametrize("mistake", ["drop_last_chunk", "shifted_chunks", "golden_drops_bias",
+                                     "golden_wrong_label"])
+def test_planted_mistakes_in_chunk_and_stored_sums(monkeypatch, mistake):
+    """A dropped ragged chunk, chunk boundaries off by one row, and a stored
+    loss sum without the bias or with the wrong label column must each fail a
+    pin."""
+    if mistake == "drop_last_chunk":
+        monkeypatch.setattr(O, "chunk_sums", _drop_last_chunk)
+        pin = lambda: test_chunk_sums_match_the_chunk_loop(37)   # noqa: E731
+    elif mistake == "shifted_chunks":
+        monkeypatch.setattr(O, "chunk_sums", _shifted_chunks)
+        pin = lambda: test_chunk_sums_match_the_chunk_loop(37)   # noqa: E731
+    elif mistake == "golden_drops_bias":
+        orig = O.label_logits_rows
+        monkeypatch.setattr(O, "label_logits_rows", lambda h, w, b, y, r: orig(h, w, None, y, r))
+        pin = test_make_golden_matches_forward
+    else:
+        orig = O.label_logits_rows
+        monkeypatch.setattr(O, "label_logits_rows",
+                            lambda h, w, b, y, r: orig(h, w, b, np.where(np.asarray(y) >= 0,
+                                                                         (np.asarray(y) + 1) % np.shape(w)[0],
+                                                                         y), r))
+        pin = test_make_golden_matches_forward
+    with pytest.raises(AssertionError):
+        pin()
 
 
 def test_bf16_rounding_paths_agree():
