@@ -62,7 +62,8 @@ def _ptr(t: torch.Tensor | None) -> int | None:
     return None if t is None else t.data_ptr()
 
 
-def _problem(hidden, weight, labels, ignore_index, chunk_rows, reduction, rows_in_flight) -> LceProblem:
+def _problem(hidden, weight, labels, ignore_index, chunk_rows, reduction, rows_in_flight,
+             bias=None) -> LceProblem:
     if reduction not in _lib.LCE_REDUCTION:
         raise ValueError(f"reduction must be one of {sorted(_lib.LCE_REDUCTION)}, got {reduction!r}")
     if hidden.dim() != 2 or weight.dim() != 2 or labels.dim() != 1:
@@ -76,9 +77,18 @@ def _problem(hidden, weight, labels, ignore_index, chunk_rows, reduction, rows_i
         raise ValueError("hidden and weight must be bfloat16")
     if labels.dtype != torch.int64:
         raise ValueError("labels must be int64")
+    if not labels.is_contiguous():
+        raise ValueError("labels must be contiguous")
     for name, t in (("hidden", hidden), ("weight", weight)):
         if t.numel() > 0 and t.stride(1) != 1:
             raise ValueError(f"{name} rows must be contiguous")
+    if bias is not None:
+        if bias.dtype != torch.bfloat16 or bias.dim() != 1 or bias.shape[0] != v or not bias.is_contiguous():
+            raise ValueError(f"bias must be a contiguous bfloat16 [V={v}] tensor, got {bias.dtype} "
+                             f"{tuple(bias.shape)}")
+    for name, t in (("weight", weight), ("labels", labels), ("bias", bias)):
+        if t is not None and t.device != hidden.device:
+            raise ValueError(f"{name} is on {t.device}, hidden on {hidden.device}")
     if chunk_rows is None:
         chunk_rows = max(n, 1)
     if chunk_rows <= 0:
@@ -99,6 +109,38 @@ def _raise(code: int, where: str):
     if code == _lib.LCE_ERR_INVALID_ARG:
         raise ValueError(f"{where}: {_lib.status_string(code)}")
     raise LceError(code, where)
+
+
+def _check_out(out: "LceOutput", n: int, h: int, v: int, reduction: str, chunk_rows: int, dev) -> None:
+    """Caller-given output buffers: shape, dtype, device and contiguity as the
+    library writes them (it takes raw pointers and trusts these)."""
+    t_chunks = -(-n // chunk_rows) if n else 0
+    want = {
+        "loss": ((n,) if reduction == "none" else (), torch.float32),
+        "lse": ((n,), torch.float32),
+        "chunk_loss": ((t_chunks,), torch.float32),
+        "n_valid": ((), torch.int64),
+        "status": ((), torch.int32),
+        "grad_hidden": ((n, h), torch.bfloat16),
+        "grad_weight": ((v, h), torch.bfloat16),
+        "grad_bias": ((v,), torch.bfloat16),
+        "grad_weight_f32": ((v, h), torch.float32),
+        "grad_bias_f32": ((v,), torch.float32),
+    }
+    for name, (shape, dtype) in want.items():
+        t = getattr(out, name)
+        if t is None:
+            if name in ("loss", "n_valid", "status"):
+                raise ValueError(f"out.{name} is required")
+            continue
+        if tuple(t.shape) != shape or t.dtype != dtype or not t.is_contiguous() or t.device != dev:
+            raise ValueError(f"out.{name} must be a contiguous {dtype} tensor of shape {shape} on {dev}, got "
+                             f"{t.dtype} {tuple(t.shape)} on {t.device}")
+
+
+def _check_workspace(ws, dev) -> None:
+    if ws is not None and (ws.dtype != torch.uint8 or not ws.is_contiguous() or ws.device != dev):
+        raise ValueError(f"workspace must be a contiguous uint8 tensor on {dev}")
 
 
 def lce_workspace_bytes(hidden, weight, labels, *, backward: bool, external_f32: bool = False,
@@ -135,11 +177,14 @@ def lce_forward(hidden: torch.Tensor, weight: torch.Tensor, bias: torch.Tensor |
     """Loss (+ per-row lse, per-chunk sums, valid count) without the [N,V] logits."""
     lib = _lib.load()
     _device_checks(hidden, weight, bias, labels)
-    p = _problem(hidden, weight, labels, ignore_index, chunk_rows, reduction, None)
+    p = _problem(hidden, weight, labels, ignore_index, chunk_rows, reduction, None, bias)
     dev = hidden.device
     if out is None:
         out = LceOutput(*_common_outputs(hidden.shape[0], reduction, p.chunk_rows, want_lse, want_chunk_loss, dev))
+    else:
+        _check_out(out, hidden.shape[0], hidden.shape[1], weight.shape[0], reduction, p.chunk_rows, dev)
     nbytes = int(lib.lce_workspace_bytes(ctypes.byref(p), _lib.LCE_WS_FORWARD))
+    _check_workspace(workspace, dev)
     if workspace is None or workspace.numel() < nbytes:
         workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
     out.workspace_bytes = nbytes
@@ -176,10 +221,18 @@ def lce_forward_backward(hidden: torch.Tensor, weight: torch.Tensor, bias: torch
         want_grad_bias = bias is not None
     if want_grad_bias and bias is None:
         raise ValueError("grad_bias requested without a bias")
-    p = _problem(hidden, weight, labels, ignore_index, chunk_rows, reduction, rows_in_flight)
+    p = _problem(hidden, weight, labels, ignore_index, chunk_rows, reduction, rows_in_flight, bias)
     dev = hidden.device
     n, h = hidden.shape
     v = weight.shape[0]
+    if out is not None:
+        _check_out(out, n, h, v, reduction, p.chunk_rows, dev)
+        if out.grad_bias is not None or out.grad_bias_f32 is not None:
+            if bias is None:
+                raise ValueError("out holds grad_bias buffers but there is no bias")
+        if accumulate and ((out.grad_weight is not None and out.grad_weight_f32 is None) or
+                           (out.grad_bias is not None and out.grad_bias_f32 is None)):
+            raise ValueError("accumulate=True needs out.grad_weight_f32 / out.grad_bias_f32")
     if out is None:
         out = LceOutput(*_common_outputs(n, reduction, p.chunk_rows, want_lse, want_chunk_loss, dev))
         if want_grad_hidden:
@@ -196,6 +249,7 @@ def lce_forward_backward(hidden: torch.Tensor, weight: torch.Tensor, bias: torch
     external = out.grad_weight_f32 is not None or out.grad_weight is None
     kind = _lib.LCE_WS_BACKWARD_EXTERNAL_F32 if external else _lib.LCE_WS_BACKWARD
     nbytes = int(lib.lce_workspace_bytes(ctypes.byref(p), kind))
+    _check_workspace(workspace, dev)
     if workspace is None or workspace.numel() < nbytes:
         workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
     out.workspace_bytes = nbytes

@@ -22,10 +22,10 @@ size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 struct Layout {
   // forward
-  size_t label32 = 0, n_valid = 0, status = 0, zlab = 0, lse = 0, part_m = 0, part_s = 0, chunk_acc = 0,
+  size_t label32 = 0, n_valid = 0, status = 0, zy2 = 0, lse = 0, part_m = 0, part_s = 0, chunk_acc = 0,
          tile_ctr = 0;
   // backward
-  size_t wT = 0, hT = 0, gw_part = 0, dlog = 0, gw_f32 = 0, gb_f32 = 0, rref = 0, rowc = 0, ovf = 0;
+  size_t zlab = 0, wT = 0, hT = 0, gw_part = 0, dlog = 0, gw_f32 = 0, gb_f32 = 0, rref = 0, rowc = 0, ovf = 0;
   size_t total = 0;
 };
 
@@ -61,15 +61,42 @@ Shapes shapes_of(const lce_problem* p) {
   return s;
 }
 
+// Rows of one backward row group. A caller's rows_in_flight is taken as
+// given (clamped, rounded up to whole tiles). The default is 16384 rows but
+// at most a quarter of the rows (whole tiles, at least one): the group's bf16
+// softmax numerators then take at most half the bytes of bf16 [N, V] logits,
+// at any N (one tile of 256 rows when N <= 256, the size of one of the pages'
+// 256-row chunks).
 int64_t group_rows(const lce_problem* p, const Shapes& s) {
-  int64_t g = p->rows_in_flight > 0 ? p->rows_in_flight : kDefaultRowsInFlight;
-  g = round_up(g < kMaxRowsInFlight ? g : kMaxRowsInFlight, kTile);
+  int64_t g;
+  if (p->rows_in_flight > 0) {
+    g = round_up(p->rows_in_flight < kMaxRowsInFlight ? p->rows_in_flight : kMaxRowsInFlight, kTile);
+  } else {
+    const int64_t quarter = s.Np / 4 / kTile * kTile;
+    g = quarter < kTile ? kTile : quarter;
+    if (g > kDefaultRowsInFlight) g = kDefaultRowsInFlight;
+  }
   return g < s.Np ? g : s.Np;
+}
+
+// FP32 partial tiles for grad_weight's split last round: each split item is
+// one 256 x 256 tile; a tile is split at most min(kMaxGwSplit, G / 256) ways
+// (at least 4 K stages of 64 rows per piece), so nothing is reserved when no
+// split can happen.
+int64_t gw_part_items(const Shapes& s, int64_t G) {
+  int64_t split_max = G / kTile;
+  if (split_max > lce::kMaxGwSplit) split_max = lce::kMaxGwSplit;
+  if (split_max < 2) return 0;
+  const int64_t n_tiles = (s.Vp / kTile) * ((s.H + kTile - 1) / kTile);
+  const int64_t items = n_tiles * split_max;
+  return items < lce::kMaxGwItems ? items : lce::kMaxGwItems;
 }
 
 int64_t n_chunks(const lce_problem* p) { return (p->n_rows + p->chunk_rows - 1) / p->chunk_rows; }
 
-Layout make_layout(const lce_problem* p, int kind) {
+// fwd_group (forward only): rows whose (max, sum-exp) partials are held at
+// once; 0 = all rows (one pass over every row).
+Layout make_layout(const lce_problem* p, int kind, int64_t fwd_group = 0) {
   const Shapes s = shapes_of(p);
   Layout L;
   size_t off = 0;
@@ -82,23 +109,24 @@ Layout make_layout(const lce_problem* p, int kind) {
   L.label32 = take((size_t)s.Np * 4);
   L.n_valid = take(8);
   L.status = take(4);
-  L.zlab = take((size_t)s.Np * 4);
+  L.zy2 = take((size_t)s.Np * 4);    // label logits from the forward tiles (base 2)
   L.lse = take((size_t)s.Np * 4);
   // (max, sumexp) partials per 64-column quarter tile: for every row in the
   // forward, for one row group at a time in the backward.
   const bool bwd = kind == LCE_WS_BACKWARD || kind == LCE_WS_BACKWARD_EXTERNAL_F32;
-  const int64_t part_rows = bwd ? group_rows(p, s) : s.Np;
+  const int64_t part_rows = bwd ? group_rows(p, s) : (fwd_group > 0 && fwd_group < s.Np ? fwd_group : s.Np);
   L.part_m = take((size_t)4 * n_vt * part_rows * 4);
   L.part_s = take((size_t)4 * n_vt * part_rows * 4);
   L.chunk_acc = take((size_t)n_chunks(p) * 8);
   L.tile_ctr = take(8 * sizeof(int));   // per-XCD tile counters of the forward tiles
   if (bwd) {
     const int64_t G = group_rows(p, s);
+    L.zlab = take((size_t)s.Np * 4);   // label logits by a gather: the row references
     // W^T, the group's h^T and its p~ / G, all stored as K-slabs
     // [K/64][rows][64]
     L.wT = take((size_t)s.H * s.Vp * 2);
     L.hT = take((size_t)s.H * G * 2);
-    L.gw_part = take((size_t)lce::kMaxGwItems * 256 * 256 * 4);   // split grad_weight tiles
+    L.gw_part = take((size_t)gw_part_items(s, G) * 256 * 256 * 4);   // split grad_weight tiles
     L.dlog = take((size_t)G * s.Vp * 2);
     L.gb_f32 = take((size_t)s.Vp * 4);
     L.rref = take((size_t)G * 4);   // the group's row references of the stored softmax numerators
@@ -160,6 +188,7 @@ struct Common {
   float* part_m;
   float* part_s;
   float* zlab;
+  float* zy2;
   double* chunk_acc;
   int* tile_ctr;
 
@@ -168,7 +197,7 @@ struct Common {
 
 int check_common(const lce_problem* p, const void* hidden, const void* weight, const void* bias,
                  const int64_t* labels, const float* loss, void* workspace, size_t workspace_bytes, int kind,
-                 Common& c) {
+                 Common& c, int64_t fwd_group = 0) {
   int st = validate_problem(p);
   if (st != LCE_OK) return st;
   if (loss == nullptr) return LCE_ERR_INVALID_ARG;
@@ -178,7 +207,7 @@ int check_common(const lce_problem* p, const void* hidden, const void* weight, c
     return LCE_ERR_UNSUPPORTED;
   c.p = p;
   c.s = shapes_of(p);
-  c.L = make_layout(p, kind);
+  c.L = make_layout(p, kind, fwd_group);
   if (c.L.total > 0 && (workspace == nullptr || workspace_bytes < c.L.total)) return LCE_ERR_WORKSPACE;
   if (!aligned(workspace, 16)) return LCE_ERR_WORKSPACE;
   c.ws = (char*)workspace;
@@ -202,6 +231,7 @@ int run_prepare(Common& c, const int64_t* labels, int64_t* n_valid_out, int32_t*
   c.part_m = (float*)(ws + c.L.part_m);
   c.part_s = (float*)(ws + c.L.part_s);
   c.zlab = (float*)(ws + c.L.zlab);
+  c.zy2 = (float*)(ws + c.L.zy2);
   LCE_LAUNCH(tr, LCE_K_ZERO, 0, 0, 0, lce::launch_zero(c.n_valid, 8, st));
   LCE_LAUNCH(tr, LCE_K_ZERO, 0, 0, 0, lce::launch_zero(c.status, 4, st));
   LCE_LAUNCH(tr, LCE_K_ZERO, 0, 0, 0, lce::launch_zero(c.chunk_acc, c.T * 8, st));
@@ -212,7 +242,8 @@ int run_prepare(Common& c, const int64_t* labels, int64_t* n_valid_out, int32_t*
   return LCE_OK;
 }
 
-// Label logits of every valid row (the gather half of the NLL).
+// Label logits of every valid row by a gather: the backward's per-row
+// references (the loss takes its label logits from the forward tiles).
 int run_label_logits(Common& c, const void* hidden, const void* weight, const void* bias, hipStream_t st,
                      Tracer& tr) {
   LCE_LAUNCH(tr, LCE_K_LABEL_LOGIT, 0, 0, 0,
@@ -230,9 +261,9 @@ int run_rows(Common& c, const void* hidden, const void* weight, const void* bias
   const int64_t rows_valid = (s.N - g0) < rows ? (s.N - g0) : rows;
   LCE_LAUNCH(tr, LCE_K_FWD_LSE, rows_valid, s.V, s.H,
              lce::launch_fwd_tiles(s, hidden, weight, bias, g0, rows, c.part_m, c.part_s, p_out, c.tile_ctr, rref,
-                                   ovf, nullptr, st));
+                                   ovf, nullptr, c.label32, c.zy2, st));
   LCE_LAUNCH(tr, LCE_K_FINALIZE_ROWS, 0, 0, 0,
-             lce::launch_finalize_rows(s, c.part_m, c.part_s, g0, rows, c.zlab, c.label32, c.status,
+             lce::launch_finalize_rows(s, c.part_m, c.part_s, g0, rows, c.zy2, c.label32, c.status,
                                        c.p->reduction, c.lse_ws, lse_out,
                                        c.p->reduction == LCE_REDUCTION_NONE ? loss : nullptr, c.chunk_acc, st));
   return LCE_OK;
@@ -266,8 +297,26 @@ int lce_forward_traced(const lce_problem* p, const void* hidden, const void* wei
                        const int64_t* labels, float* loss, float* lse, float* chunk_loss, int64_t* n_valid,
                        int32_t* status, void* workspace, size_t workspace_bytes, hipStream_t stream,
                        lce_trace* trace) {
+  return lce::forward_grouped(p, hidden, weight, bias, labels, loss, lse, chunk_loss, n_valid, status, workspace,
+                              workspace_bytes, 0, stream, trace);
+}
+
+}  // extern "C"
+
+namespace lce {
+
+size_t forward_workspace_bytes(const lce_problem* p, int64_t group) {
+  if (validate_problem(p) != LCE_OK) return 0;
+  return make_layout(p, LCE_WS_FORWARD, group).total;
+}
+
+int forward_grouped(const lce_problem* p, const void* hidden, const void* weight, const void* bias,
+                    const int64_t* labels, float* loss, float* lse, float* chunk_loss, int64_t* n_valid,
+                    int32_t* status, void* workspace, size_t workspace_bytes, int64_t group, hipStream_t stream,
+                    lce_trace* trace) {
   Common c;
-  int st = check_common(p, hidden, weight, bias, labels, loss, workspace, workspace_bytes, LCE_WS_FORWARD, c);
+  int st = check_common(p, hidden, weight, bias, labels, loss, workspace, workspace_bytes, LCE_WS_FORWARD, c,
+                        group);
   if (st != LCE_OK) return st;
   Tracer tr;
   tr.t = trace;
@@ -275,10 +324,10 @@ int lce_forward_traced(const lce_problem* p, const void* hidden, const void* wei
   if (trace) trace->count = 0;
   st = run_prepare(c, labels, n_valid, status, stream, tr);
   if (st != LCE_OK) return st;
-  if (c.s.N > 0) {
-    st = run_label_logits(c, hidden, weight, bias, stream, tr);
-    if (st != LCE_OK) return st;
-    st = run_rows(c, hidden, weight, bias, 0, c.s.Np, nullptr, loss, lse, stream, tr);
+  const int64_t step = group > 0 && group < c.s.Np ? group : c.s.Np;
+  for (int64_t g0 = 0; g0 < c.s.N; g0 += step) {
+    st = run_rows(c, hidden, weight, bias, g0, (c.s.Np - g0) < step ? (c.s.Np - g0) : step, nullptr, loss, lse,
+                  stream, tr);
     if (st != LCE_OK) return st;
   }
   LCE_LAUNCH(tr, LCE_K_FINALIZE_LOSS, 0, 0, 0,
@@ -286,6 +335,10 @@ int lce_forward_traced(const lce_problem* p, const void* hidden, const void* wei
                                        stream));
   return LCE_OK;
 }
+
+}  // namespace lce
+
+extern "C" {
 
 int lce_forward(const lce_problem* p, const void* hidden, const void* weight, const void* bias,
                 const int64_t* labels, float* loss, float* lse, float* chunk_loss, int64_t* n_valid,
@@ -338,8 +391,6 @@ int lce_forward_backward_ex(const lce_problem* p, const void* hidden, const void
   if (s.N == 0) {
     if (need_gw && !accumulate) LCE_LAUNCH(tr, LCE_K_ZERO, 0, 0, 0, lce::launch_zero(gw, s.V * s.H * 4, stream));
   } else {
-    st = run_label_logits(c, hidden, weight, bias, stream, tr);
-    if (st != LCE_OK) return st;
     // Row groups: the logits of a group are computed once. The tiles leave
     // exp(z - r_i) in dlog, r_i the row's label logit; once the group's lse
     // is known, k_rowscale patches the label entries and forms the row
@@ -357,6 +408,10 @@ int lce_forward_backward_ex(const lce_problem* p, const void* hidden, const void
     int* ovf = (int*)(ws + c.L.ovf);
     const int is_mean = p->reduction == LCE_REDUCTION_MEAN;
     const bool any_grad = need_gh || need_gw || need_gb;
+    if (any_grad) {
+      st = run_label_logits(c, hidden, weight, bias, stream, tr);
+      if (st != LCE_OK) return st;
+    }
     if (need_gh)
       LCE_LAUNCH(tr, LCE_K_TRANSPOSE, 0, 0, 0,
                  lce::launch_transpose(weight, s.ldw, 0, s.V, s.H, wT, s.Vp, nullptr, stream));
@@ -375,16 +430,16 @@ int lce_forward_backward_ex(const lce_problem* p, const void* hidden, const void
       st = run_rows(c, hidden, weight, bias, g0, Gc, dlog, loss, lse, stream, tr, rref, ovf);
       if (st != LCE_OK) return st;
       LCE_LAUNCH(tr, LCE_K_BWD_DLOGITS, rows_valid, s.V, 0,
-                 lce::launch_rowscale(c.label32, c.zlab, c.lse_ws, rref, row_scale, c.n_valid, grad_scale, is_mean,
+                 lce::launch_rowscale(c.label32, c.zy2, c.lse_ws, rref, row_scale, c.n_valid, grad_scale, is_mean,
                                       g0, Gc, dlog, rowc, ovf, 0, need_gb ? gb : nullptr, stream));
       // retry, only when the overflow flag is set
       LCE_LAUNCH(tr, LCE_K_ROW_REF, 0, 0, 0,
                  lce::launch_prep_ref(c.label32, c.lse_ws, g0, Gc, rref, ovf, stream));
       LCE_LAUNCH(tr, LCE_K_FWD_RETRY, 0, 0, 0,
                  lce::launch_fwd_tiles(s, hidden, weight, bias, g0, Gc, c.part_m, c.part_s, dlog, c.tile_ctr, rref,
-                                       nullptr, ovf, stream));
+                                       nullptr, ovf, c.label32, c.zy2, stream));
       LCE_LAUNCH(tr, LCE_K_BWD_DLOGITS, rows_valid, s.V, 0,
-                 lce::launch_rowscale(c.label32, c.zlab, c.lse_ws, rref, row_scale, c.n_valid, grad_scale, is_mean,
+                 lce::launch_rowscale(c.label32, c.zy2, c.lse_ws, rref, row_scale, c.n_valid, grad_scale, is_mean,
                                       g0, Gc, dlog, rowc, ovf, 1, need_gb ? gb : nullptr, stream));
       if (need_gb)
         LCE_LAUNCH(tr, LCE_K_BIAS_SUMS, rows_valid, s.V, 0, lce::launch_bias_sums(s, dlog, rowc, Gc, gb, stream));
@@ -395,7 +450,8 @@ int lce_forward_backward_ex(const lce_problem* p, const void* hidden, const void
         LCE_LAUNCH(tr, LCE_K_TRANSPOSE, 0, 0, 0,
                    lce::launch_transpose(hidden, s.ldh, g0, rows_valid, s.H, hT, Gc, rowc, stream));
         LCE_LAUNCH(tr, LCE_K_GRAD_WEIGHT, s.V, s.H, rows_valid,
-                   lce::launch_grad_weight(s, dlog, Gc, hT, rows_valid, gw_part, (g0 == 0 && !accumulate) ? 1 : 0,
+                   lce::launch_grad_weight(s, dlog, Gc, hT, rows_valid, gw_part, gw_part_items(s, G),
+                                           (g0 == 0 && !accumulate) ? 1 : 0,
                                            gw, last ? grad_weight : nullptr,
                                            (!last || grad_weight == nullptr || grad_weight_f32 != nullptr) ? 1 : 0,
                                            stream));

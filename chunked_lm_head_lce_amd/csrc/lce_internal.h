@@ -4,7 +4,18 @@
 #include <hip/hip_runtime_api.h>
 #include <stdint.h>
 
+#include "../../include/lce.h"
+
 namespace lce {
+
+// lce_forward_traced with the (max, sum-exp) partials held for `group` rows
+// at a time (a multiple of 256; 0 = all rows at once), and the workspace it
+// needs (0 when *p is invalid).
+size_t forward_workspace_bytes(const lce_problem* p, int64_t group);
+int forward_grouped(const lce_problem* p, const void* hidden, const void* weight, const void* bias,
+                    const int64_t* labels, float* loss, float* lse, float* chunk_loss, int64_t* n_valid,
+                    int32_t* status, void* workspace, size_t workspace_bytes, int64_t group, hipStream_t stream,
+                    lce_trace* trace);
 
 struct Shapes {
   int64_t N, Np;     // rows, rows rounded up to a multiple of 256
@@ -26,15 +37,21 @@ hipError_t launch_prepare_labels(const int64_t* labels, int64_t N, int64_t Np, i
 // With p_out and rref non-null the stored values are exp(z - rref[i]) for
 // rows with a finite rref (capped at e^60; a larger gap sets *ovf = 1) and
 // exp(z - max_quarter) for NaN entries. only_if (nullable): run only if
-// *only_if != 0.
+// *only_if != 0. Partials are base 2: (max t, sum 2^(t - max t)), t =
+// z log2(e). label32 [Np] (-1: no label): for each row with a label the
+// tile holding that column writes its t to zy2[row] (zy2 [Np], global rows).
 hipError_t launch_fwd_tiles(const Shapes& s, const void* hidden, const void* weight, const void* bias, int64_t g0,
                             int64_t rows, float* part_m, float* part_s, void* p_out, int* tile_ctr,
-                            const float* rref, int* ovf, const int* only_if, hipStream_t st);
-// zlab[i] = h_i . W_{y_i} + b_{y_i} for valid rows.
+                            const float* rref, int* ovf, const int* only_if, const int32_t* label32, float* zy2,
+                            hipStream_t st);
+// zlab[i] = h_i . W_{y_i} + b_{y_i} for valid rows (FP32 dot product: the
+// backward's per-row references, needed before the row's tiles run).
 hipError_t launch_label_logit(const Shapes& s, const void* hidden, const void* weight, const void* bias,
                               const int32_t* label32, float* zlab, hipStream_t st);
+// lse and l_i of rows [g0, g0 + rows) from the base-2 partials and the label
+// values zy2 written by the forward tiles.
 hipError_t launch_finalize_rows(const Shapes& s, const float* part_m, const float* part_s, int64_t g0,
-                                int64_t rows, const float* zlab, const int32_t* label32, const int32_t* status,
+                                int64_t rows, const float* zy2, const int32_t* label32, const int32_t* status,
                                 int reduction, float* lse_ws, float* lse_out, float* rowloss_out,
                                 double* chunk_acc, hipStream_t st);
 hipError_t launch_finalize_loss(const double* chunk_acc, int64_t T, const unsigned long long* n_valid,
@@ -52,9 +69,10 @@ hipError_t launch_prep_ref(const int32_t* label32, const float* src, int64_t g0,
                            const int* only_if, hipStream_t st);
 // Row scales rowc[i] = s row_scale_i valid_i exp(rref_i - lse_i) and the label
 // entry of each valid row of dlog (K-slabs [Vp/64][G][64]) set to
-// exp(z_y - rref_i) - exp(lse_i - rref_i). Runs when (*ovf != 0) == retry.
-// gb_f32 (nullable) receives rowc[i] times the bf16 rounding of that entry.
-hipError_t launch_rowscale(const int32_t* label32, const float* zlab, const float* lse_ws, const float* rref,
+// exp(z_y - rref_i) - exp(lse_i - rref_i), z_y = zy2 ln 2. Runs when
+// (*ovf != 0) == retry. gb_f32 (nullable) receives rowc[i] times the bf16
+// rounding of that entry.
+hipError_t launch_rowscale(const int32_t* label32, const float* zy2, const float* lse_ws, const float* rref,
                            const float* row_scale, const unsigned long long* n_valid, float grad_scale, int is_mean,
                            int64_t g0, int64_t G, void* dlog, float* rowc, const int* ovf, int retry,
                            float* gb_f32, hipStream_t st);
@@ -69,18 +87,19 @@ hipError_t launch_grad_hidden(const Shapes& s, const void* dlog, const void* wT,
                               const float* rowc, void* grad_hidden, hipStream_t st);
 // gw (+)= sum over the group's rows i < rows_valid of G[i][v] h[g0 + i][:]
 // (dlog: K-slabs [Vp/64][G][64] holding G; hT: the group's rows of h as
-// K-slabs [G/64][H][64], zero past N). part: kMaxGwItems * 256 * 256 floats
-// of scratch for split tiles. first: store instead of add. gw_bf16 (nullable):
-// also write each final sum rounded to bf16 (the last row group); keep32 = 0:
-// do not write the FP32 sums back.
+// K-slabs [G/64][H][64], zero past N). part: part_items * 256 * 256 floats
+// of scratch for split tiles (no more pieces are made). first: store instead
+// of add. gw_bf16 (nullable): also write each final sum rounded to bf16 (the
+// last row group); keep32 = 0: do not write the FP32 sums back.
 hipError_t launch_grad_weight(const Shapes& s, const void* dlog, int64_t G, const void* hT, int64_t rows_valid,
-                              float* part, int first, float* gw_f32, void* gw_bf16, int keep32, hipStream_t st);
+                              float* part, int64_t part_items, int first, float* gw_f32, void* gw_bf16, int keep32,
+                              hipStream_t st);
 // grad_weight's tiles: the first n_full run whole (a multiple of the CU
 // count), the rest are split `split` ways along K (split = 1: none) so that
-// they fill one round; at most kMaxGwItems split pieces.
+// they fill one round; at most min(max_items, kMaxGwItems) split pieces.
 constexpr int kMaxGwSplit = 8;
 constexpr int kMaxGwItems = 256;
-void grad_weight_split(int n_tiles, int nk, int cus, int* n_full, int* split);
+void grad_weight_split(int n_tiles, int nk, int cus, int max_items, int* n_full, int* split);
 int device_cus();
 hipError_t launch_cast(const float* in, void* out, int64_t n, hipStream_t st);
 

@@ -31,6 +31,7 @@
 #include "lce_internal.h"
 
 #define LDS_AS __attribute__((address_space(3)))
+#define GLOBAL_AS __attribute__((address_space(1)))
 
 namespace lce {
 
@@ -62,7 +63,6 @@ __device__ __forceinline__ u16 f2bf(float x) {
   __bf16 b = (__bf16)x;                    // v_cvt_pk_bf16_f32: round to nearest even
   return __builtin_bit_cast(u16, b);
 }
-__device__ __forceinline__ float exp_fast(float x) { return __builtin_amdgcn_exp2f(x * LOG2E); }
 
 // Reductions across the 16 lanes that hold one accumulator row, with DPP
 // lane permutations (plain VALU operations, no LDS round trip): swap lanes
@@ -470,8 +470,12 @@ __device__ __forceinline__ uint32_t lane_x16() {
 
 // Forward tiles: z = h W^T + b for 256 rows x 256 vocabulary ids, reduced in
 // the epilogue to each row's (max, sum exp(z - max)) over each wave's
-// 64-column quarter of the tile (part index NQ*tile + quarter). z never
-// leaves registers. With STORE_P (backward row groups) the tile also writes
+// 64-column quarter of the tile (part index NQ*tile + quarter), in base-2
+// units: t = z log2(e), partials (max t, sum 2^(t - max t)). The tile that
+// holds a row's label column also stores that t (zy2, rows of label32 >= 0),
+// so the loss l = ln2 ((M - t_y) + log2 S) comes from the same accumulators
+// as the lse and is never negative (M >= t_y, S >= 1). z never leaves
+// registers. With STORE_P (backward row groups) the tile also writes
 // the bf16 unnormalised softmax exp(z - r_i) into p (K-slabs
 // [Vp/64][ld_part][64]), r_i the row's reference from rref (its label logit,
 // or its lse in the retry; see k_rowscale), or the quarter maximum where
@@ -498,10 +502,11 @@ k_fwd_tile(const u16* __restrict__ hidden, int64_t ldh, const u16* __restrict__ 
            const u16* __restrict__ bias, int64_t N, int64_t V, int64_t H, int64_t g0, int64_t ld_part, int n_mt,
            int n_vt, float* __restrict__ part_m, float* __restrict__ part_s, u16* __restrict__ p_out,
            int* __restrict__ tile_ctr, const float* __restrict__ rref, int* __restrict__ ovf,
-           const int* __restrict__ only_if) {
+           const int* __restrict__ only_if, const int32_t* __restrict__ label32, float* __restrict__ zy2) {
   __shared__ __attribute__((aligned(16))) char smem_raw[MAINLOOP_LDS];
   __shared__ __attribute__((aligned(16))) u16 s_pst[STORE_P ? 8 * PST_WAVE : 8];
   __shared__ __attribute__((aligned(16))) float s_ref[STORE_P ? 2 * TILE : 4];   // per-row references, two tiles
+  __shared__ __attribute__((aligned(16))) int s_lab[2 * TILE];                    // per-row labels, two tiles
   __shared__ int s_next;
   if (only_if != nullptr && *only_if == 0) return;   // a retry launch with nothing to retry
   LDS_AS char* smem = (LDS_AS char*)smem_raw;
@@ -518,7 +523,9 @@ k_fwd_tile(const u16* __restrict__ hidden, int64_t ldh, const u16* __restrict__ 
   const bool use_ref = STORE_P && rref != nullptr;
   int par = 0;
   const uint32_t ref_lds = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(LDS_AS char*)s_ref);
+  const uint32_t lab_lds = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(LDS_AS char*)s_lab);
   if (use_ref && wave == 0) lds_dma16(uniform_ptr(rref + (int64_t)tm * TILE), lane_x16(), ref_lds);
+  if (wave == 1) lds_dma16(uniform_ptr(label32 + g0 + (int64_t)tm * TILE), lane_x16(), lab_lds);
   TileLoads t = tile_setup(hidden, ldh, BK * 2, g0 + (int64_t)tm * TILE, N, weight, ldw, BK * 2,
                            (int64_t)tn * TILE, V, smem);
   tile_prologue(t, nk);
@@ -530,12 +537,14 @@ k_fwd_tile(const u16* __restrict__ hidden, int64_t ldh, const u16* __restrict__ 
     // address, any valid pointer when there is no bias) and first used after
     // the K loop: a conditional load would make the compiler wait for it on
     // the spot, and with it for every direct load in flight.
-    const u16* bsrc = bias != nullptr ? bias : hidden;
+    // (32-bit column offsets from a scalar base: V < 2^22.)
+    const GLOBAL_AS u16* bsrc = (const GLOBAL_AS u16*)uniform_ptr(bias != nullptr ? bias : hidden);
+    const int vmax = (int)V - 1;
     u16 braw[NBJ];
 #pragma unroll
     for (int j = 0; j < NBJ; ++j) {
-      const int64_t col = col0 + acc_col(wn, j, lane);
-      braw[j] = bsrc[bias != nullptr ? (col < V ? col : V - 1) : 0];
+      const int col = (int)col0 + acc_col(wn, j, lane);
+      braw[j] = bsrc[bias != nullptr ? (col < vmax ? col : vmax) : 0];
     }
     Acc acc;
     tile_run(acc, t, nk, smem);
@@ -544,8 +553,8 @@ k_fwd_tile(const u16* __restrict__ hidden, int64_t ldh, const u16* __restrict__ 
     float cbl[NBJ];
 #pragma unroll
     for (int j = 0; j < NBJ; ++j) {
-      const int64_t col = col0 + acc_col(wn, j, lane);
-      cbl[j] = col < V ? (bias != nullptr ? bf2f(braw[j]) * LOG2E : 0.f) : -INFINITY;
+      const int col = (int)col0 + acc_col(wn, j, lane);
+      cbl[j] = col <= vmax ? (bias != nullptr ? bf2f(braw[j]) * LOG2E : 0.f) : -INFINITY;
       // pinned here: computed later, the wait for braw would also wait for
       // the next tile's loads
       asm volatile("" ::"v"(cbl[j]));
@@ -556,6 +565,8 @@ k_fwd_tile(const u16* __restrict__ hidden, int64_t ldh, const u16* __restrict__ 
     if (more) {
       if (use_ref && wave == 0)
         lds_dma16(uniform_ptr(rref + (int64_t)tm * TILE), lane_x16(), ref_lds + (uint32_t)((par ^ 1) * TILE * 4));
+      if (wave == 1)
+        lds_dma16(uniform_ptr(label32 + g0 + (int64_t)tm * TILE), lane_x16(), lab_lds + (uint32_t)((par ^ 1) * TILE * 4));
       t = tile_setup(hidden, ldh, BK * 2, g0 + (int64_t)tm * TILE, N, weight, ldw, BK * 2, (int64_t)tn * TILE, V,
                      smem);
       tile_prologue(t, nk);
@@ -568,16 +579,50 @@ k_fwd_tile(const u16* __restrict__ hidden, int64_t ldh, const u16* __restrict__ 
     float* pm = part_m + (int64_t)(NQ * ptn + wn) * ld_part + lrow0 + wm * 128 + 4 * (lane >> 4);
     float* ps = part_s + (int64_t)(NQ * ptn + wn) * ld_part + lrow0 + wm * 128 + 4 * (lane >> 4);
     u16* pq = STORE_P ? p_out + ((col0 >> 6) + wn) * ld_part * 64 + (lrow0 + wm * 128) * 64 : nullptr;
+    // Label logits from these accumulators: a row's label column falls in
+    // this wave's 64 columns for a few of its 128 rows at most, found with
+    // two ballots (bit k: row wm*128 + k, then + 64); only a 16-row block
+    // with such a row reads its labels and stores t_y = z_{i,y_i} log2(e),
+    // the same value that enters the row's maximum and sum below.
+    const LDS_AS int* labs = (const LDS_AS int*)s_lab + par * TILE + wm * 128;
+    const int cw = (int)col0 + wn * 64;
+    uint64_t hit_lo, hit_hi;
+    {
+      const LDS_AS int* lp = (const LDS_AS int*)((const LDS_AS char*)labs + (lane_x16() >> 2));
+      hit_lo = __ballot((unsigned)(lp[0] - cw) < 64u);
+      hit_hi = __ballot((unsigned)(lp[64] - cw) < 64u);
+    }
     // The four rows r of a row block are reduced together so their DPP
     // steps interleave instead of waiting on each other.
 #pragma unroll
     for (int i = 0; i < NB; ++i) {
+      // t = z log2(e) in place, formed once: the label capture, the maximum
+      // and the sum all use these values, so the maximum's own term below is
+      // 2^0 = 1 exactly.
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int j = 0; j < NBJ; ++j) acc.v[i][j][r] = fmaf(acc.v[i][j][r], LOG2E, cbl[j]);
+      if (((i < 4 ? hit_lo : hit_hi) >> ((i & 3) * 16)) & 0xFFFFull) {   // rare, wave-uniform
+        const uint32_t l16 = lane_x16();
+        // rows wm*128 + i*16 + 4*(lane/16) + r of this tile, r = 0..3
+        const uint32_t rb = (uint32_t)(i * 16) + ((l16 >> 8) << 2);
+        GLOBAL_AS float* zrow = (GLOBAL_AS float*)uniform_ptr(zy2 + g0 + lrow0 + wm * 128);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int d = labs[rb + r] - cw;
+          if ((unsigned)d < 64u && (uint32_t)(d & 15) == ((l16 >> 4) & 15)) {
+            const int jj = d >> 4;
+            zrow[rb + r] = jj == 0 ? acc.v[i][0][r] : jj == 1 ? acc.v[i][1][r] : jj == 2 ? acc.v[i][2][r] : acc.v[i][3][r];
+          }
+        }
+      }
       float m[4];                               // row max of z * log2(e)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         m[r] = -INFINITY;
 #pragma unroll
-        for (int j = 0; j < NBJ; ++j) m[r] = fmaxf(m[r], fmaf(acc.v[i][j][r], LOG2E, cbl[j]));
+        for (int j = 0; j < NBJ; ++j) m[r] = fmaxf(m[r], acc.v[i][j][r]);
       }
 #pragma unroll
       for (int r = 0; r < 4; ++r) m[r] = fmaxf(m[r], dpp<DPP_XOR1>(m[r]));
@@ -607,7 +652,7 @@ k_fwd_tile(const u16* __restrict__ hidden, int64_t ldh, const u16* __restrict__ 
         sm[r] = 0.f;
 #pragma unroll
         for (int j = 0; j < NBJ; ++j) {
-          const float e = __builtin_amdgcn_exp2f(fmaf(acc.v[i][j][r], LOG2E, cbl[j] - ms));
+          const float e = __builtin_amdgcn_exp2f(acc.v[i][j][r] - ms);
           sm[r] += e;
           if (STORE_P) pst[(4 * (lane >> 4) + r) * PST_LD + j * 16 + (lane & 15)] = f2bf(e * fr);
         }
@@ -620,8 +665,8 @@ k_fwd_tile(const u16* __restrict__ hidden, int64_t ldh, const u16* __restrict__ 
       for (int r = 0; r < 4; ++r) sm[r] += dpp<DPP_HALF_MIRROR>(sm[r]);
 #pragma unroll
       for (int r = 0; r < 4; ++r) sm[r] += dpp<DPP_MIRROR>(sm[r]);
-      if ((lane & 15) == 0) {   // rows 4*(lane/16) .. +3 of the block, in natural-log units
-        *(f32x4*)(pm + i * 16) = (f32x4){m[0] * LN2, m[1] * LN2, m[2] * LN2, m[3] * LN2};
+      if ((lane & 15) == 0) {   // rows 4*(lane/16) .. +3 of the block, in base-2 units
+        *(f32x4*)(pm + i * 16) = (f32x4){m[0], m[1], m[2], m[3]};
         *(f32x4*)(ps + i * 16) = (f32x4){sm[0], sm[1], sm[2], sm[3]};
       }
       if (STORE_P) {
@@ -676,25 +721,26 @@ __global__ void __launch_bounds__(256) k_label_logit(const u16* __restrict__ hid
   if (lane == 0) zlab[row] = acc + (bias != nullptr ? bf2f(bias[lab]) : 0.f);
 }
 
-// Per row i in [row_begin, row_end): merge the quarter-tile (max, sumexp)
-// partials into lse, form l_i, write lse (and l_i for reduction NONE), and
-// add l_i into its chunk's float64 sum. Partials of row i sit at
+// Per row i in [row_begin, row_end): merge the quarter-tile base-2 (max,
+// sumexp) partials into lse, form l_i from the row's label t_y (zy2), write
+// lse (and l_i for reduction NONE), and add l_i into its chunk's float64 sum. Partials of row i sit at
 // part[k * ld_part + (i - part_row0)], k < n_part. Rows in [N, row_end) only
 // get lse_ws = 0. A block takes 64 rows; its 16 waves each merge every 16th
 // partial of those rows (256-byte coalesced reads), then combine in LDS.
 constexpr int FIN_ROWS = 64;
 constexpr int FIN_WAVES = 16;
 
+// (M, S) <- the merge of two base-2 partials (max t, sum 2^(t - max t)).
 __device__ __forceinline__ void merge_ms(float& M, float& S, float mk, float sk) {
   if (mk == -INFINITY) return;
   const float mn = fmaxf(M, mk);
-  S = S * exp_fast(M - mn) + sk * exp_fast(mk - mn);
+  S = S * __builtin_amdgcn_exp2f(M - mn) + sk * __builtin_amdgcn_exp2f(mk - mn);
   M = mn;
 }
 
 __global__ void __launch_bounds__(64 * FIN_WAVES) k_finalize_rows(
     const float* __restrict__ part_m, const float* __restrict__ part_s, int64_t ld_part, int64_t part_row0,
-    int n_part, const float* __restrict__ zlab, const int32_t* __restrict__ label32, int64_t N,
+    int n_part, const float* __restrict__ zy2, const int32_t* __restrict__ label32, int64_t N,
     int64_t row_begin, int64_t row_end, int64_t chunk_rows, const int32_t* __restrict__ status, int reduction,
     float* __restrict__ lse_ws, float* __restrict__ lse_out, float* __restrict__ rowloss_out,
     double* __restrict__ chunk_acc) {
@@ -734,9 +780,12 @@ __global__ void __launch_bounds__(64 * FIN_WAVES) k_finalize_rows(
     return;
   }
   for (int w = 1; w < FIN_WAVES; ++w) merge_ms(M, S, s_m[w][lane], s_s[w][lane]);
-  const float lse = M + logf(S);
+  // S >= 1: the partial holding the maximum M has its own maximum term
+  // 2^(M - M) = 1, and every other term is >= 0 (the clamp is a guard).
+  const float L = fmaxf(__log2f(S), 0.f);
+  const float lse = LN2 * (M + L);
   const int lab = label32[i];
-  const float l = lab >= 0 ? lse - zlab[i] : 0.f;
+  const float l = lab >= 0 ? LN2 * ((M - zy2[i]) + L) : 0.f;   // M >= t_y: never negative
   lse_ws[i] = lse;
   if (lse_out) lse_out[i] = lse;
   if (reduction == 0 && rowloss_out) rowloss_out[i] = (*status != 0) ? NAN : l;
@@ -864,7 +913,7 @@ __global__ void __launch_bounds__(256) k_prep_ref(const int32_t* __restrict__ la
 
 // Row scales c_i of one group and the label entries of p~' (see above).
 // retry = 0 runs unless the overflow flag is set, retry = 1 only if it is.
-__global__ void __launch_bounds__(256) k_rowscale(const int32_t* __restrict__ label32, const float* __restrict__ zlab,
+__global__ void __launch_bounds__(256) k_rowscale(const int32_t* __restrict__ label32, const float* __restrict__ zy2,
                                                   const float* __restrict__ lse_ws, const float* __restrict__ rref,
                                                   const float* __restrict__ row_scale,
                                                   const unsigned long long* __restrict__ n_valid, float grad_scale,
@@ -887,7 +936,7 @@ __global__ void __launch_bounds__(256) k_rowscale(const int32_t* __restrict__ la
   }
   const float r = rref[i], lse = lse_ws[row];
   const float c = scale * (row_scale != nullptr ? row_scale[row] : 1.f) * expf(r - lse);
-  const float pl = expf(zlab[row] - r) - expf(lse - r);
+  const float pl = expf(zy2[row] * LN2 - r) - expf(lse - r);
   const u16 pb = f2bf(pl);
   rowc[i] = c;
   dlog[((int64_t)(lab >> 6) * G + i) * 64 + (lab & 63)] = pb;
@@ -1201,7 +1250,8 @@ static int persistent_grid(int64_t ntiles) {
 
 hipError_t launch_fwd_tiles(const Shapes& s, const void* hidden, const void* weight, const void* bias, int64_t g0,
                             int64_t rows, float* part_m, float* part_s, void* p_out, int* tile_ctr,
-                            const float* rref, int* ovf, const int* only_if, hipStream_t st) {
+                            const float* rref, int* ovf, const int* only_if, const int32_t* label32, float* zy2,
+                            hipStream_t st) {
   const int n_mt = (int)(rows / TILE), n_vt = (int)(s.Vp / TILE);
   const int nb = persistent_grid((int64_t)n_mt * n_vt);
   if (nb == 0) return hipSuccess;
@@ -1211,11 +1261,11 @@ hipError_t launch_fwd_tiles(const Shapes& s, const void* hidden, const void* wei
   if (p_out)
     hipLaunchKernelGGL(k_fwd_tile<true>, grid, block, 0, st, (const u16*)hidden, s.ldh, (const u16*)weight, s.ldw,
                        (const u16*)bias, s.N, s.V, s.H, g0, rows, n_mt, n_vt, part_m, part_s, (u16*)p_out, tile_ctr,
-                       rref, ovf, only_if);
+                       rref, ovf, only_if, label32, zy2);
   else
     hipLaunchKernelGGL(k_fwd_tile<false>, grid, block, 0, st, (const u16*)hidden, s.ldh, (const u16*)weight,
                        s.ldw, (const u16*)bias, s.N, s.V, s.H, g0, rows, n_mt, n_vt, part_m, part_s, (u16*)nullptr,
-                       tile_ctr, (const float*)nullptr, (int*)nullptr, only_if);
+                       tile_ctr, (const float*)nullptr, (int*)nullptr, only_if, label32, zy2);
   return hipGetLastError();
 }
 
@@ -1228,11 +1278,11 @@ hipError_t launch_label_logit(const Shapes& s, const void* hidden, const void* w
 }
 
 hipError_t launch_finalize_rows(const Shapes& s, const float* part_m, const float* part_s, int64_t g0,
-                                int64_t rows, const float* zlab, const int32_t* label32, const int32_t* status,
+                                int64_t rows, const float* zy2, const int32_t* label32, const int32_t* status,
                                 int reduction, float* lse_ws, float* lse_out, float* rowloss_out,
                                 double* chunk_acc, hipStream_t st) {
   hipLaunchKernelGGL(k_finalize_rows, dim3((unsigned)(rows / FIN_ROWS)), dim3(64 * FIN_WAVES), 0, st, part_m, part_s, rows, g0,
-                     (int)(NQ * (s.Vp / TILE)), zlab, label32, s.N, g0, g0 + rows, s.chunk_rows, status, reduction,
+                     (int)(NQ * (s.Vp / TILE)), zy2, label32, s.N, g0, g0 + rows, s.chunk_rows, status, reduction,
                      lse_ws, lse_out, rowloss_out, chunk_acc);
   return hipGetLastError();
 }
@@ -1260,11 +1310,11 @@ hipError_t launch_prep_ref(const int32_t* label32, const float* src, int64_t g0,
   return hipGetLastError();
 }
 
-hipError_t launch_rowscale(const int32_t* label32, const float* zlab, const float* lse_ws, const float* rref,
+hipError_t launch_rowscale(const int32_t* label32, const float* zy2, const float* lse_ws, const float* rref,
                            const float* row_scale, const unsigned long long* n_valid, float grad_scale, int is_mean,
                            int64_t g0, int64_t G, void* dlog, float* rowc, const int* ovf, int retry,
                            float* gb_f32, hipStream_t st) {
-  hipLaunchKernelGGL(k_rowscale, dim3((unsigned)((G + 255) / 256)), dim3(256), 0, st, label32, zlab, lse_ws, rref,
+  hipLaunchKernelGGL(k_rowscale, dim3((unsigned)((G + 255) / 256)), dim3(256), 0, st, label32, zy2, lse_ws, rref,
                      row_scale, n_valid, grad_scale, is_mean, g0, G, (u16*)dlog, rowc, ovf, retry, gb_f32);
   return hipGetLastError();
 }
@@ -1285,12 +1335,13 @@ hipError_t launch_grad_hidden(const Shapes& s, const void* dlog, const void* wT,
 }
 
 hipError_t launch_grad_weight(const Shapes& s, const void* dlog, int64_t G, const void* hT, int64_t rows_valid,
-                              float* part, int first, float* gw_f32, void* gw_bf16, int keep32, hipStream_t st) {
+                              float* part, int64_t part_items, int first, float* gw_f32, void* gw_bf16, int keep32,
+                              hipStream_t st) {
   const int n_mt = (int)(s.Vp / TILE), n_nt = (int)((s.H + TILE - 1) / TILE);
   const int nk = (int)((rows_valid + 63) / 64);
   const int n_tiles = n_mt * n_nt;
   int n_full = n_tiles, split = 1;
-  grad_weight_split(n_tiles, nk, device_cus(), &n_full, &split);
+  grad_weight_split(n_tiles, nk, device_cus(), (int)part_items, &n_full, &split);
   hipLaunchKernelGGL(k_gemm_grad_weight, dim3((unsigned)(n_full + (n_tiles - n_full) * split)), dim3(NTHREADS), 0,
                      st, (const u16*)dlog, G, (const u16*)hT, nk, s.H, s.V, n_mt, n_nt, n_full, split, first, gw_f32,
                      part, (u16*)gw_bf16, keep32);
@@ -1301,7 +1352,7 @@ hipError_t launch_grad_weight(const Shapes& s, const void* dlog, int64_t G, cons
   return hipGetLastError();
 }
 
-void grad_weight_split(int n_tiles, int nk, int cus, int* n_full, int* split) {
+void grad_weight_split(int n_tiles, int nk, int cus, int max_items, int* n_full, int* split) {
   const int rem = n_tiles % cus;
   *n_full = n_tiles;
   *split = 1;
@@ -1309,7 +1360,8 @@ void grad_weight_split(int n_tiles, int nk, int cus, int* n_full, int* split) {
   int sp = cus / rem;
   if (sp > kMaxGwSplit) sp = kMaxGwSplit;
   if (sp > nk / 4) sp = nk / 4;
-  if (sp * rem > kMaxGwItems) sp = kMaxGwItems / rem;
+  if (max_items > kMaxGwItems) max_items = kMaxGwItems;
+  if (sp * rem > max_items) sp = max_items / rem;
   if (sp < 2) return;
   *n_full = n_tiles - rem;
   *split = sp;

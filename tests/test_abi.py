@@ -70,21 +70,84 @@ def test_workspace_sizes(lib):
     assert ws(lib, prob(), 7) == 0
 
 
-@pytest.mark.parametrize("name", ["qwen3_0p6b_head", "qwen3_4b_32k", "qwen3_4b_160k", "qwen3_8b_1m_shard"])
-def test_no_full_logits_buffer(lib, name):
-    """No [N, V] logits: the whole backward workspace stays below the fp32
-    [N, V] logits an eager loss holds, its dlogits buffers are sized by
-    rows_in_flight rather than N, and once N is many row groups it is below
-    even a bf16 [N, V]."""
+def _up(x, m):
+    return (x + m - 1) // m * m
+
+
+def group_rows(n, rows_in_flight=0):
+    """The backward row group the library uses (rounded to 256-row tiles):
+    the caller's rows_in_flight, else 16384 rows but at most a quarter of
+    the rows (at least one tile)."""
+    np_ = _up(n, 256)
+    if rows_in_flight > 0:
+        g = _up(min(rows_in_flight, 1 << 20), 256)
+    else:
+        g = min(16384, max(256, np_ // 4 // 256 * 256))
+    return min(g, np_)
+
+
+def layout(n, h, v, kind, rows_in_flight=0, chunk_rows=256):
+    """The workspace regions, in order, as the library carves them (each
+    start 256-byte aligned). kind 0 forward, 1 backward with the FP32
+    grad_weight inside, 2 backward with caller FP32 buffers."""
+    np_, vp = _up(n, 256), _up(v, 256)
+    n_vt = vp // 256
+    bwd = kind in (1, 2)
+    g = group_rows(n, rows_in_flight)
+    part_rows = g if bwd else np_
+    regions = [("label32", np_ * 4), ("n_valid", 8), ("status", 4), ("zy2", np_ * 4), ("lse", np_ * 4),
+               ("part_m", 4 * n_vt * part_rows * 4), ("part_s", 4 * n_vt * part_rows * 4),
+               ("chunk_acc", -(-n // chunk_rows) * 8), ("tile_ctr", 32)]
+    if bwd:
+        split_max = min(8, g // 256)
+        n_tiles = n_vt * -(-h // 256)
+        items = min(256, n_tiles * split_max) if split_max >= 2 else 0
+        regions += [("zlab", np_ * 4), ("wT", h * vp * 2), ("hT", h * g * 2), ("gw_part", items * 256 * 256 * 4),
+                    ("dlog", g * vp * 2), ("gb_f32", vp * 4), ("rref", g * 4), ("rowc", g * 4), ("ovf", 4)]
+        if kind == 1:
+            regions.append(("gw_f32", v * h * 4))
+    return dict(regions), sum(_up(b, 256) for _, b in regions)
+
+
+@pytest.mark.parametrize("name", ["tiny", "qwen3_0p6b_head", "qwen3_4b_32k", "qwen3_4b_160k", "qwen3_8b_1m_shard"])
+@pytest.mark.parametrize("rif", [0, 4096])
+def test_workspace_layout(lib, name, rif):
+    """lce_workspace_bytes is exactly the documented regions."""
     w = WORKLOADS[name]
-    b = ws(lib, prob(w.n_rows, w.hidden, w.vocab), 1)
-    if w.n_rows >= 8 * w.hidden:   # below that the V x H grad buffers alone exceed it
-        assert b < w.n_rows * w.vocab * 4, (b, w.n_rows * w.vocab * 4)
-    b_small = ws(lib, prob(w.n_rows, w.hidden, w.vocab, rows_in_flight=4096), 1)
-    if w.n_rows > 4096:
-        assert b - b_small >= 2 * (16384 - 4096) * w.vocab   # the bf16 p~ / G buffer of a row group
-    if w.n_rows >= 8 * 16384:
-        assert b < w.n_rows * w.vocab * 2, (b, w.n_rows * w.vocab * 2)
+    for kind in (0, 1, 2):
+        _, total = layout(w.n_rows, w.hidden, w.vocab, kind, rif, w.chunk_rows)
+        assert ws(lib, prob(w.n_rows, w.hidden, w.vocab, rows_in_flight=rif, chunk_rows=w.chunk_rows), kind) \
+            == total, (name, kind)
+
+
+@pytest.mark.parametrize("name", ["tiny", "qwen3_0p6b_head", "qwen3_4b_32k", "qwen3_4b_160k", "qwen3_8b_1m_shard"])
+def test_no_full_logits_buffer(lib, name):
+    """No [N, V] logits at any size: with the default row group every
+    logits-shaped region (the group's bf16 softmax numerators, the per-tile
+    max / sum-exp partials) is below half a bf16 [N, V], and the whole
+    backward workspace beside the FP32 grad_weight the method keeps is below
+    FP32 [N, V] logits for every workload but the tiny one (whose [N, V] is
+    smaller than its [V, H] head)."""
+    w = WORKLOADS[name]
+    n, h, v = w.n_rows, w.hidden, w.vocab
+    nv2 = n * v * 2
+    for kind in (0, 1, 2):
+        regions, total = layout(n, h, v, kind, 0, w.chunk_rows)
+        assert ws(lib, prob(n, h, v, chunk_rows=w.chunk_rows), kind) == total
+        for r in ("dlog", "part_m", "part_s"):
+            if r in regions:
+                assert regions[r] <= nv2 // 2, (name, kind, r, regions[r], nv2)
+        if name != "tiny":
+            assert total < 2 * nv2, (name, kind, total, 2 * nv2)
+    # a caller may trade memory for speed explicitly (rows_in_flight), up to all rows at once
+    regions, _ = layout(n, h, v, 1, n, w.chunk_rows)
+    assert regions["dlog"] == _up(n, 256) * _up(v, 256) * 2
+
+
+def test_group_rows_default():
+    assert [group_rows(n) for n in (1, 256, 257, 1000, 1024, 2048, 32768, 65536, 131072, 163840)] == \
+        [256, 256, 256, 256, 256, 512, 8192, 16384, 16384, 16384]
+    assert group_rows(1000, 512) == 512 and group_rows(300, 4096) == 512 and group_rows(10, 1) == 256
 
 
 def fwd(lib, p, hidden=FAKE, weight=FAKE, labels=FAKE, loss=FAKE, wsp=FAKE, wsb=1 << 40):
@@ -179,3 +242,47 @@ def test_scale_host_errors(lib):
     assert lib.lce_scale(FAKE, 0, 10, None, None) == 1
     assert lib.lce_scale(FAKE, 7, 10, FAKE, None) == 1
     assert lib.lce_scale(None, 0, 0, None, None) == 0                # nothing to do
+
+
+def test_python_layer_rejects_bad_bias_labels_and_outputs():
+    """The binding checks what the C ABI cannot see through raw pointers:
+    bias dtype / shape / layout, label layout and caller-given outputs."""
+    n, h, v = 6, 64, 10
+    hid = torch.zeros(n, h, dtype=torch.bfloat16)
+    w = torch.zeros(v, h, dtype=torch.bfloat16)
+    y = torch.zeros(n, dtype=torch.int64)
+    lce._problem(hid, w, y, -100, 256, "sum", None, torch.zeros(v, dtype=torch.bfloat16))   # accepted
+    for bad in (torch.zeros(v, dtype=torch.float32),                # an FP32 master bias
+                torch.zeros(v - 1, dtype=torch.bfloat16),           # shorter than V
+                torch.zeros(v + 1, dtype=torch.bfloat16),
+                torch.zeros(v, 2, dtype=torch.bfloat16)[:, 0],      # strided
+                torch.zeros(1, v, dtype=torch.bfloat16)):           # not 1-D
+        with pytest.raises(ValueError, match="bias"):
+            lce._problem(hid, w, y, -100, 256, "sum", None, bad)
+    with pytest.raises(ValueError, match="labels"):
+        lce._problem(hid, w, torch.zeros(2 * n, dtype=torch.int64)[::2], -100, 256, "sum", None)
+    with pytest.raises(ValueError, match="labels"):
+        lce._problem(hid, w, torch.zeros(n, dtype=torch.int32), -100, 256, "sum", None)
+
+    def good_out():
+        return lce.LceOutput(torch.empty(()), torch.empty(n), torch.empty(1), torch.empty((), dtype=torch.int64),
+                             torch.empty((), dtype=torch.int32), torch.empty(n, h, dtype=torch.bfloat16),
+                             torch.empty(v, h, dtype=torch.bfloat16), torch.empty(v, dtype=torch.bfloat16),
+                             torch.empty(v, h), torch.empty(v))
+    dev = hid.device
+    lce._check_out(good_out(), n, h, v, "sum", 256, dev)
+    for field, bad in (("loss", torch.empty(n)), ("lse", torch.empty(n + 1)), ("chunk_loss", torch.empty(2)),
+                       ("n_valid", torch.empty((), dtype=torch.int32)), ("status", None),
+                       ("grad_hidden", torch.empty(n, h)), ("grad_weight", torch.empty(h, v, dtype=torch.bfloat16)),
+                       ("grad_bias", torch.empty(v - 1, dtype=torch.bfloat16)),
+                       ("grad_weight_f32", torch.empty(v, h, dtype=torch.bfloat16)),
+                       ("grad_bias_f32", torch.empty(2 * v)[::2])):
+        o = good_out()
+        setattr(o, field, bad)
+        with pytest.raises(ValueError, match=field):
+            lce._check_out(o, n, h, v, "sum", 256, dev)
+    o = good_out()
+    o.loss = torch.empty(n)
+    lce._check_out(o, n, h, v, "none", 256, dev)   # per-row loss for reduction none
+    with pytest.raises(ValueError, match="workspace"):
+        lce._check_workspace(torch.empty(16, dtype=torch.float32), dev)

@@ -109,6 +109,54 @@ def test_row_groups_match(cuda):
         check_all(out, ref, inp, "sum")
 
 
+def test_confident_rows_have_nonnegative_loss(cuda):
+    """Rows whose label logit exceeds every other logit by ~30 have a loss of
+    ~1e-9. The label logit is taken from the same FP32 accumulators that
+    give the row's maximum and sum, so l_i = lse_i - z_{i,y_i} can round to
+    0 but never below it; it must also match the oracle to ~1e-6."""
+    import dataclasses
+    from lce_inputs import bf16_bits
+    inp = make_case(600, 256, 5000, seed=41, bias_std=0.05, ignore_frac=0.1, weight_std=0.05)
+    h = inp.hidden_f32().copy()
+    w = inp.weight_f32()
+    conf = np.flatnonzero(inp.labels >= 0)[::3]                 # a third of the valid rows
+    h[conf] = 50.0 * w[inp.labels[conf]]
+    inp = dataclasses.replace(inp, hidden_bits=bf16_bits(h))
+    ref = oracle_of(inp)
+    assert ref.row_loss[conf].max() < 1e-6
+    hd, wd, bd, yd = to_device(inp, cuda)
+    say("[gpu] confident rows: forward, reduction none")
+    f = lce.lce_forward(hd, wd, bd, yd, reduction="none")
+    say("[gpu] confident rows: forward_backward")
+    out = lce.lce_forward_backward(hd, wd, bd, yd)
+    torch.cuda.synchronize()
+    rl = np32(f.loss)
+    assert rl.min() >= 0.0, rl.min()
+    np.testing.assert_allclose(rl[conf], ref.row_loss[conf], rtol=0, atol=2e-6)
+    assert_rows_close(rl, ref.row_loss, "row loss")
+    check_all(out, ref, inp, "sum")
+
+
+def test_split_last_group_without_f32_outputs(cuda):
+    """The path the benchmark times, at a small size: several row groups,
+    grad_weight's last round split along K (274 vocabulary tiles on 256
+    CUs leave 18, each split 2 ways: 8 K stages of 64 rows in each group),
+    the second group adding into the FP32 accumulator (first = 0) and, with
+    no FP32 output requested, writing only the bf16 result (keep32 = 0)."""
+    inp = make_case(1000, 256, 70000, seed=31, bias_std=0.05, ignore_frac=0.1, weight_std=0.05)
+    hd, wd, bd, yd = to_device(inp, cuda)
+    say("[gpu] split last group: bf16 outputs only")
+    out = lce.lce_forward_backward(hd, wd, bd, yd, rows_in_flight=512, want_f32=False)
+    say("[gpu] split last group: with FP32 outputs")
+    o32 = lce.lce_forward_backward(hd, wd, bd, yd, rows_in_flight=512, want_f32=True)
+    torch.cuda.synchronize()
+    assert out.grad_weight_f32 is None and o32.grad_weight_f32 is not None
+    check_all(out, oracle_of(inp), inp, "sum")
+    assert torch.equal(out.grad_hidden, o32.grad_hidden)
+    assert torch.equal(out.grad_weight, o32.grad_weight_f32.to(torch.bfloat16))
+    assert torch.equal(o32.grad_weight, o32.grad_weight_f32.to(torch.bfloat16))
+
+
 @pytest.mark.parametrize("g,reduction", [(256, "sum"), (0, "sum"), (256, "mean")])
 def test_far_label_logit_retry(cuda, g, reduction):
     """Rows whose largest logit lies far above their label logit (over 60):

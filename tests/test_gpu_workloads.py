@@ -24,6 +24,45 @@ pytestmark = pytest.mark.gpu
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
 
+def _out_bytes(out) -> int:
+    return sum(t.numel() * t.element_size() for t in (out.loss, out.lse, out.chunk_loss, out.n_valid, out.status,
+                                                       out.grad_hidden, out.grad_weight, out.grad_bias,
+                                                       out.grad_weight_f32, out.grad_bias_f32) if t is not None)
+
+
+def _timed_call_with_peak(cuda, w, hd, wd, bd, yd, **kw):
+    """The benchmark's call (bf16 outputs, FP32 accumulators in workspace,
+    default row group) with the peak HBM it adds beyond inputs and outputs;
+    no [N, V] logits exist, so it stays below FP32 [N, V] logits."""
+    torch.cuda.synchronize()
+    base = torch.cuda.memory_allocated(cuda)
+    torch.cuda.reset_peak_memory_stats(cuda)
+    out = lce.lce_forward_backward(hd, wd, bd, yd, chunk_rows=w.chunk_rows, reduction=w.reduction,
+                                   want_f32=False, **kw)
+    torch.cuda.synchronize()
+    extra = torch.cuda.max_memory_allocated(cuda) - base - _out_bytes(out)
+    logits32 = 4 * w.n_rows * w.vocab
+    say(f"[gpu] workload {w.name}: peak extra HBM {extra / 1e9:.3f} GB, FP32 [N,V] logits {logits32 / 1e9:.3f} GB")
+    assert extra < logits32, (extra, logits32)
+    return out
+
+
+def _check_row_losses(cuda, w, hd, wd, bd, yd, lse_ref=None):
+    """Per-row losses from the forward: l_i >= 0 for every row (and exactly 0
+    for ignored rows), and they add up to the loss."""
+    say(f"[gpu] workload {w.name}: per-row losses")
+    f = lce.lce_forward(hd, wd, bd, yd, chunk_rows=w.chunk_rows, reduction="none")
+    torch.cuda.synchronize()
+    rl = f.loss.double()
+    ign = yd == -100
+    if bool(ign.any()):
+        assert float(rl[ign].abs().max()) == 0.0
+    assert float(rl.min()) >= 0.0, f"negative per-row loss {float(rl.min())!r}"
+    if lse_ref is not None:
+        assert_rows_close(np32(f.lse), lse_ref, "lse (reduction none)")
+    return float(rl.sum())
+
+
 @pytest.mark.parametrize("name", ["tiny", "qwen3_0p6b_head"])
 def test_small_workloads_full(cuda, name):
     w = WORKLOADS[name]
@@ -34,6 +73,11 @@ def test_small_workloads_full(cuda, name):
     out = lce.lce_forward_backward(hd, wd, bd, yd, chunk_rows=w.chunk_rows, reduction=w.reduction,
                                    want_chunk_loss=True)
     torch.cuda.synchronize()
+    if name != "tiny":   # the tiny workload's [N, V] is smaller than its [V, H] head
+        timed = _timed_call_with_peak(cuda, w, hd, wd, bd, yd)
+        assert torch.equal(timed.grad_hidden, out.grad_hidden)
+        assert torch.equal(timed.grad_weight, out.grad_weight)
+    row_sum = _check_row_losses(cuda, w, hd, wd, bd, yd)
     say(f"[gpu] workload {name}: oracle")
     ref = O.forward_backward(inp.hidden_f32(), inp.weight_f32(), inp.bias_f32(), inp.labels,
                              reduction=w.reduction, chunk_rows=w.chunk_rows)
@@ -43,6 +87,7 @@ def test_small_workloads_full(cuda, name):
     assert_rows_close(np32(out.chunk_loss), ref.chunk_loss, "chunk sums")
     assert_grad_close(np32(out.grad_hidden), ref.grad_hidden, "grad_hidden")
     assert_grad_close(np32(out.grad_weight), ref.grad_weight, "grad_weight")
+    assert_loss_close(row_sum, ref.loss, "sum of per-row losses")
 
 
 def _golden(name):
@@ -75,6 +120,21 @@ def _check_large(cuda, name, chunk_sweep=None):
     for o in outs[1:]:
         assert torch.equal(o.grad_hidden, out.grad_hidden)
         assert torch.equal(o.grad_weight, out.grad_weight)
+    del outs
+
+    # the exact call the benchmark times: bf16 outputs only (FP32 accumulator
+    # in workspace, last row group's split tiles writing bf16 without keeping
+    # FP32); bit-identical products, grad_bias checked on the vocabulary subset
+    say(f"[gpu] workload {name}: the benchmark's call (bf16 outputs only)")
+    timed = _timed_call_with_peak(cuda, w, hd, wd, bd, yd)
+    assert int(timed.status.item()) == 0
+    assert int(timed.n_valid.item()) == meta["n_valid"]
+    assert_loss_close(float(timed.loss.item()), meta["loss_sum"])
+    assert timed.grad_weight_f32 is None
+    assert torch.equal(timed.grad_hidden, out.grad_hidden)
+    assert torch.equal(timed.grad_weight, out.grad_weight_f32.to(torch.bfloat16))
+    timed_gb = timed.grad_bias
+    del timed
 
     # the forward-only call: every row in one pass, no stored softmax
     say(f"[gpu] workload {name}: forward only")
@@ -85,6 +145,8 @@ def _check_large(cuda, name, chunk_sweep=None):
     assert_loss_close(float(f.loss.item()), meta["loss_sum"])
     assert_rows_close(np32(f.lse), lse_ref, "forward-only lse (all rows)")
     assert abs(float(f.chunk_loss.double().sum()) - meta["loss_sum"]) <= 2e-3 * abs(meta["loss_sum"])
+    del f
+    assert_loss_close(_check_row_losses(cuda, w, hd, wd, bd, yd, lse_ref), meta["loss_sum"], "sum of per-row losses")
 
     h32, w32, b32 = inp.hidden_f32(), inp.weight_f32(), inp.bias_f32()
     rows = sample_rows(w, inp.labels)
@@ -107,6 +169,7 @@ def _check_large(cuda, name, chunk_sweep=None):
         say(f"[gpu] workload {name}: cold-id grad_weight relative error {rel:.2e}")
     if b32 is not None:
         assert_grad_close(np32(out.grad_bias[ci]), c_gb, "grad_bias cols")
+        assert_grad_close(np32(timed_gb[ci]), c_gb, "grad_bias cols (benchmark call)")
         gb = out.grad_bias_f32.double()
         assert abs(float(gb.sum())) <= 1e-3 * float(gb.abs().max()) * np.sqrt(w.vocab)
     gw_colsum = out.grad_weight_f32.double().sum(dim=0)
