@@ -26,7 +26,8 @@ from ._lib import LceProblem
 IGNORE_INDEX = -100
 DEFAULT_CHUNK_ROWS = 256
 
-__all__ = ["lce_forward", "lce_forward_backward", "lce_workspace_bytes", "lce_scale", "linear_cross_entropy",
+__all__ = ["lce_forward", "lce_forward_backward", "lce_forward_noalloc", "noalloc_outputs", "lce_workspace_bytes",
+           "lce_scale", "linear_cross_entropy",
            "LinearCrossEntropyFunction", "LceOutput", "LceError", "IGNORE_INDEX", "DEFAULT_CHUNK_ROWS"]
 
 
@@ -196,6 +197,34 @@ def lce_forward(hidden: torch.Tensor, weight: torch.Tensor, bias: torch.Tensor |
     if code != _lib.LCE_OK:
         _raise(code, "lce_forward")
     return out
+
+
+def lce_forward_noalloc(hidden: torch.Tensor, weight: torch.Tensor, bias: torch.Tensor | None,
+                        labels: torch.Tensor, *, out: LceOutput, ignore_index: int = IGNORE_INDEX,
+                        chunk_rows: int | None = DEFAULT_CHUNK_ROWS, reduction: str = "sum") -> LceOutput:
+    """lce_forward for callers that cannot allocate: the library's fixed
+    per-GPU scratch is the workspace, and ``out`` (caller-allocated, e.g. by
+    :func:`noalloc_outputs`) receives the results. Calls on one GPU must not
+    overlap. Raises LceError with LCE_ERR_TOO_LARGE when the problem does not
+    fit the scratch."""
+    lib = _lib.load()
+    _device_checks(hidden, weight, bias, labels)
+    p = _problem(hidden, weight, labels, ignore_index, chunk_rows, reduction, None, bias)
+    _check_out(out, hidden.shape[0], hidden.shape[1], weight.shape[0], reduction, p.chunk_rows, hidden.device)
+    stream = torch.cuda.current_stream(hidden.device).cuda_stream
+    code = lib.lce_forward_noalloc(ctypes.byref(p), _ptr(hidden), _ptr(weight), _ptr(bias), _ptr(labels),
+                                   _ptr(out.loss), _ptr(out.lse), _ptr(out.chunk_loss), _ptr(out.n_valid),
+                                   _ptr(out.status), stream)
+    if code != _lib.LCE_OK:
+        _raise(code, "lce_forward_noalloc")
+    return out
+
+
+def noalloc_outputs(n: int, device, *, reduction: str = "sum", chunk_rows: int | None = DEFAULT_CHUNK_ROWS,
+                    want_lse: bool = True, want_chunk_loss: bool = False) -> LceOutput:
+    """Output buffers for :func:`lce_forward_noalloc`, allocated ahead of time."""
+    c = chunk_rows if chunk_rows is not None else max(n, 1)
+    return LceOutput(*_common_outputs(n, reduction, c, want_lse, want_chunk_loss, torch.device(device)))
 
 
 def lce_forward_backward(hidden: torch.Tensor, weight: torch.Tensor, bias: torch.Tensor | None,

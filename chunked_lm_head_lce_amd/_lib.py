@@ -17,6 +17,8 @@ LCE_ERR_UNSUPPORTED = 2
 LCE_ERR_WORKSPACE = 3
 LCE_ERR_HIP = 4
 LCE_ERR_LABEL_RANGE = 5
+LCE_ERR_TOO_LARGE = 6
+LCE_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 LCE_REDUCTION = {"none": 0, "sum": 1, "mean": 2}
 LCE_DTYPE_BF16 = 0
@@ -27,7 +29,7 @@ LCE_WS_BACKWARD_EXTERNAL_F32 = 2
 
 EXPORTED = ("lce_workspace_bytes", "lce_forward", "lce_forward_backward", "lce_forward_traced",
             "lce_forward_backward_traced", "lce_forward_backward_ex", "lce_scale", "lce_status_string",
-            "lce_abi_version")
+            "lce_abi_version", "lce_forward_noalloc")
 
 KERNEL_KINDS = ("zero", "prepare_labels", "fwd_lse", "finalize_rows", "finalize_loss", "transpose",
                 "bwd_dlogits", "grad_hidden", "grad_weight", "cast", "label_logit", "row_ref", "fwd_retry",
@@ -94,6 +96,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.lce_forward_backward_traced.restype = i32
     lib.lce_forward_backward_ex.argtypes = lib.lce_forward_backward.argtypes + [ctypes.POINTER(LceBackwardOptions), T]
     lib.lce_forward_backward_ex.restype = i32
+    lib.lce_forward_noalloc.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.lce_forward_noalloc.restype = i32
     lib.lce_scale.argtypes = [vp, i32, ctypes.c_int64, vp, vp]
     lib.lce_scale.restype = i32
     lib.lce_status_string.argtypes = [i32]

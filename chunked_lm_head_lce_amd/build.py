@@ -13,7 +13,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "liblce.so")
-SOURCES = ["lce_kernels.hip", "lce_api.cpp"]
+SOURCES = ["lce_kernels.hip", "lce_api.cpp", "lce_noalloc.hip"]
 ARCH = "gfx950"
 
 

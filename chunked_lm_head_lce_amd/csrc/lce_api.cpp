@@ -273,7 +273,7 @@ int run_rows(Common& c, const void* hidden, const void* weight, const void* bias
 
 extern "C" {
 
-int lce_abi_version(void) { return 103; }
+int lce_abi_version(void) { return 104; }
 
 const char* lce_status_string(int status) {
   switch (status) {
@@ -283,6 +283,7 @@ const char* lce_status_string(int status) {
     case LCE_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
     case LCE_ERR_HIP: return "HIP launch failed";
     case LCE_ERR_LABEL_RANGE: return "label outside [0, vocab) that is not ignore_index";
+    case LCE_ERR_TOO_LARGE: return "problem needs more than the allocation-free entry point's scratch";
     default: return "unknown status";
   }
 }

@@ -53,7 +53,8 @@ typedef enum {
                                 above 2^22, NONE backward without per-row scales */
   LCE_ERR_WORKSPACE = 3,     /* workspace null or smaller than lce_workspace_bytes() */
   LCE_ERR_HIP = 4,           /* a kernel launch failed */
-  LCE_ERR_LABEL_RANGE = 5    /* device-side: a label outside [0,V) and != ignore_index */
+  LCE_ERR_LABEL_RANGE = 5,   /* device-side: a label outside [0,V) and != ignore_index */
+  LCE_ERR_TOO_LARGE = 6      /* lce_forward_noalloc: the problem needs more than its fixed scratch */
 } lce_status;
 
 typedef enum {
@@ -209,6 +210,27 @@ int lce_forward_backward_ex(const lce_problem* p, const void* hidden, const void
  * Returns LCE_ERR_INVALID_ARG for n < 0, a NULL pointer with n > 0 or an
  * unknown dtype. */
 int lce_scale(void* data, int32_t dtype, int64_t n, const float* scale, hipStream_t stream);
+
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): lce_forward
+ * without a workspace argument. Its workspace is a fixed device array of
+ * LCE_NOALLOC_SCRATCH_BYTES inside the library, one per GPU, held from the
+ * first load of the library's code on that GPU until the process ends; the
+ * call itself allocates nothing (no hipMalloc, no allocating library call).
+ * Results are those of lce_forward (arguments and outputs the same), with
+ * the forward's per-tile (max, sum-exp) partials held for as many rows at a
+ * time as fit in the array. About 12 bytes per row (padded to 256 rows) plus
+ * 8 per loss chunk must fit beside the partials of 256 rows
+ * (32 * ceil(V / 256) * 256 bytes); a larger problem returns
+ * LCE_ERR_TOO_LARGE before anything is enqueued.
+ * Every call on a GPU uses that GPU's one array and leaves its contents
+ * behind; each call clears what it needs zeroed itself. Calls that overlap
+ * on one GPU (several streams or threads at once) race on the array: the
+ * caller must order them. */
+#define LCE_NOALLOC_SCRATCH_BYTES (64ull << 20)
+int lce_forward_noalloc(const lce_problem* p, const void* hidden, const void* weight, const void* bias,
+                        const int64_t* labels, float* loss, float* lse, float* chunk_loss, int64_t* n_valid,
+                        int32_t* status, hipStream_t stream);
 
 /* Static string for an lce_status value (never NULL). */
 const char* lce_status_string(int status);

@@ -48,8 +48,8 @@ def test_exports_every_declared_function(lib):
 
 
 def test_version_and_strings(lib):
-    assert lib.lce_abi_version() == 103
-    for code in range(6):
+    assert lib.lce_abi_version() == 104
+    for code in range(7):
         assert _lib.status_string(code) != "unknown status"
     assert _lib.status_string(99) == "unknown status"
 
@@ -286,3 +286,18 @@ def test_python_layer_rejects_bad_bias_labels_and_outputs():
     lce._check_out(o, n, h, v, "none", 256, dev)   # per-row loss for reduction none
     with pytest.raises(ValueError, match="workspace"):
         lce._check_workspace(torch.empty(16, dtype=torch.float32), dev)
+
+
+def test_noalloc_rejects_on_the_host(lib):
+    """The allocation-free forward refuses, before touching any device, a
+    problem whose workspace cannot fit its fixed scratch even 256 rows at a
+    time (12 bytes per row alone pass 64 MiB near 5.6M rows), and reports
+    argument errors like lce_forward."""
+    def call(p):
+        return lib.lce_forward_noalloc(ctypes.byref(p), FAKE, FAKE, None, FAKE, FAKE, None, None, None, None, None)
+    assert call(prob(n=6_000_000, h=64, v=4096)) == _lib.LCE_ERR_TOO_LARGE
+    assert call(prob(n=512, h=64, v=1 << 22)) == _lib.LCE_ERR_TOO_LARGE     # 256 rows of partials alone: 128 MiB
+    assert call(prob(chunk_rows=0)) == _lib.LCE_ERR_INVALID_ARG
+    assert call(prob(dtype=1)) == _lib.LCE_ERR_UNSUPPORTED
+    assert lib.lce_forward_noalloc(None, FAKE, FAKE, None, FAKE, FAKE, None, None, None, None, None) == 1
+    assert _lib.LCE_NOALLOC_SCRATCH_BYTES == 64 << 20
