@@ -1,7 +1,7 @@
 // Host side of the C ABI declared in include/lce.h: argument validation,
 // workspace carve-up and the launch sequence on the caller's stream. The
 // library allocates nothing and keeps no state.
-#include "../../include/lce.h"
+#include "lce.h"
 
 #include <hip/hip_runtime_api.h>
 #include <stdint.h>
@@ -442,7 +442,8 @@ int lce_forward_backward_ex(const lce_problem* p, const void* hidden, const void
       LCE_LAUNCH(tr, LCE_K_BWD_DLOGITS, rows_valid, s.V, 0,
                  lce::launch_rowscale(c.label32, c.zy2, c.lse_ws, rref, row_scale, c.n_valid, grad_scale, is_mean,
                                       g0, Gc, dlog, rowc, ovf, 1, need_gb ? gb : nullptr, stream));
-      if (need_gb)
+      // grad_bias column sums: inside grad_weight's K loop when it runs
+      if (need_gb && !need_gw)
         LCE_LAUNCH(tr, LCE_K_BIAS_SUMS, rows_valid, s.V, 0, lce::launch_bias_sums(s, dlog, rowc, Gc, gb, stream));
       if (need_gh)
         LCE_LAUNCH(tr, LCE_K_GRAD_HIDDEN, rows_valid, s.H, s.V,
@@ -455,7 +456,7 @@ int lce_forward_backward_ex(const lce_problem* p, const void* hidden, const void
                                            (g0 == 0 && !accumulate) ? 1 : 0,
                                            gw, last ? grad_weight : nullptr,
                                            (!last || grad_weight == nullptr || grad_weight_f32 != nullptr) ? 1 : 0,
-                                           stream));
+                                           rowc, need_gb ? gb : nullptr, stream));
         if (last) gw_cast_done = true;
       }
     }

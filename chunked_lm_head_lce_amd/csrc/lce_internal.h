@@ -4,7 +4,7 @@
 #include <hip/hip_runtime_api.h>
 #include <stdint.h>
 
-#include "../../include/lce.h"
+#include "lce.h"
 
 namespace lce {
 
@@ -76,7 +76,8 @@ hipError_t launch_rowscale(const int32_t* label32, const float* zy2, const float
                            const float* row_scale, const unsigned long long* n_valid, float grad_scale, int is_mean,
                            int64_t g0, int64_t G, void* dlog, float* rowc, const int* ovf, int retry,
                            float* gb_f32, hipStream_t st);
-// gb_f32[v] += sum_i rowc[i] dlog[i][v] over the group's G rows.
+// gb_f32[v] += sum_i rowc[i] dlog[i][v] over the group's G rows (used when
+// grad_weight is not computed; otherwise its kernel adds these sums).
 hipError_t launch_bias_sums(const Shapes& s, const void* dlog, const float* rowc, int64_t G, float* gb_f32,
                             hipStream_t st);
 // data[k] *= *scale (bf16 or f32 elements).
@@ -90,10 +91,12 @@ hipError_t launch_grad_hidden(const Shapes& s, const void* dlog, const void* wT,
 // K-slabs [G/64][H][64], zero past N). part: part_items * 256 * 256 floats
 // of scratch for split tiles (no more pieces are made). first: store instead
 // of add. gw_bf16 (nullable): also write each final sum rounded to bf16 (the
-// last row group); keep32 = 0: do not write the FP32 sums back.
+// last row group); keep32 = 0: do not write the FP32 sums back. gb_f32
+// (nullable): also add the group's grad_bias column sums, sum_i rowc[i]
+// dlog[i][v] (FP32 atomics; rowc [G], the group's row scales).
 hipError_t launch_grad_weight(const Shapes& s, const void* dlog, int64_t G, const void* hT, int64_t rows_valid,
                               float* part, int64_t part_items, int first, float* gw_f32, void* gw_bf16, int keep32,
-                              hipStream_t st);
+                              const float* rowc, float* gb_f32, hipStream_t st);
 // grad_weight's tiles: the first n_full run whole (a multiple of the CU
 // count), the rest are split `split` ways along K (split = 1: none) so that
 // they fill one round; at most min(max_items, kMaxGwItems) split pieces.

@@ -211,6 +211,15 @@ __device__ __forceinline__ const void* uniform_ptr(const void* p) {
   return (const void*)(uintptr_t)((hi << 32) | lo);
 }
 
+// 16 x the lane index, computed where it is used: kept live across the K
+// loop it would be spilled, and its reload waits for every store in flight.
+__device__ __forceinline__ uint32_t lane_x16() {
+  uint32_t v;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0\n\tv_lshlrev_b32 %0, 4, %0"
+               : "=v"(v));
+  return v;
+}
+
 // Issues load f (0..7) of stage s: f < 4 fill X rows, f >= 4 fill Y rows.
 __device__ __forceinline__ void stage_load(const TileLoads& t, int s, int f) {
   const uint32_t buf = t.lds_wave + (uint32_t)((s & 1) * STAGE);
@@ -245,6 +254,10 @@ struct FragK {
     if (n < NBJ) f.b[n] = frag(buf + OPERAND_STAGE, rB + n * 16, sub * 4 + q);
     else f.a[n - NBJ] = frag(buf, rA + (n - NBJ) * 16, sub * 4 + q);
   }
+  // work beside the fragment reads and the loads of each slot (none here;
+  // see FragATBias)
+  __device__ __forceinline__ void side(int, int, const LDS_AS char*) {}
+  __device__ __forceinline__ void side_load(int, int, int) const {}
 };
 
 // K-major stage layout, for operands whose rows run along K in memory: tile
@@ -284,6 +297,90 @@ struct FragAT {
     if (n < NBJ) f.b[n] = frag(buf + OPERAND_STAGE, rB + n * 16, sub * 4 + q);
     else f.a[n - NBJ] = frag_tr(buf + a[n - NBJ] + sub * 32 * TR_ROW);
   }
+  __device__ __forceinline__ void side(int, int, const LDS_AS char*) {}
+  __device__ __forceinline__ void side_load(int, int, int) const {}
+};
+
+// FragAT for grad_weight with grad_bias folded in: grad_bias[v] = sum_k
+// c_k G'[k][v] over the group's rows k is a column sum of the A operand
+// already in LDS. Stage s of vocabulary tile tm is summed by the tile of
+// that tm whose hidden-tile index tn = s mod n_nt (every stage once, spread
+// evenly over the tiles). In such a stage wave w takes K rows 8w .. 8w+7,
+// each lane the ids 4 lane .. +3, in two halves of four rows: reads in slot
+// 6, sums and the second half's reads in slot 8, its sums in slot 10 (slots
+// 6..9 have no fragment reads; the stage's buffer is read-only until the
+// barrier of slot 10). The row scales c_k of every stage come into LDS
+// (s_c, one 256-byte direct load by wave 0, issued with the stage's operand
+// loads and published by the same wait and barrier), so all waits stay in
+// LDS order. gb[] holds this lane's sums over the tile's stages.
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ void lds_dma4(const void* gbase, uint32_t voff, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, %2"
+               :: "s"(lds_addr), "v"(voff), "s"(gbase) : "memory", "m0");
+}
+struct FragATBias : FragAT {
+  float gb[4];
+  const float* rowc;     // row scales of the tile's first K row (uniform)
+  uint32_t c_lds;        // LDS byte address of s_c[2][64]
+  int next;              // next stage (local index) whose bias sums this tile takes
+  int next_c;            // next such stage whose row scales are not yet requested
+  int n_nt;
+  int wave;
+  __device__ __forceinline__ FragATBias(int wave_, int lane, const float* rowc_, uint32_t c_lds_, int first,
+                                        int n_nt_)
+      : FragAT(wave_, lane), rowc(rowc_), c_lds(c_lds_), next(first), next_c(first), n_nt(n_nt_), wave(wave_) {
+    while (next_c < 2) next_c += n_nt;   // stages 0 and 1 are requested before the K loop
+#pragma unroll
+    for (int e = 0; e < 4; ++e) gb[e] = 0.f;
+  }
+  // the 64 row scales of stage s into s_c[s & 1] (wave 0)
+  __device__ __forceinline__ void load_c(int s) const {
+    lds_dma4(uniform_ptr(rowc + (int64_t)s * 64), lane_x16() >> 2, c_lds + (uint32_t)((s & 1) * 256));
+  }
+  // byte address of row 8 wave + u of the stage, ids 4 lane .. +3: the
+  // 16-byte chunk lane/2 sits at slot (lane/2) ^ 2 tr_swz(row)
+  __device__ __forceinline__ uint32_t addr(int u) const {
+    const uint32_t x = (uint32_t)(2 * ((u & 3) | ((wave & 1) << 2))) << 4;
+    return (uint32_t)((wave * 8 + u) * TR_ROW) + ((lane_x16() >> 1) ^ x);
+  }
+  __device__ __forceinline__ void fma4(u32x2 x, float c) {
+    gb[0] = fmaf(c, __builtin_bit_cast(float, x.x << 16), gb[0]);
+    gb[1] = fmaf(c, __builtin_bit_cast(float, x.x & 0xFFFF0000u), gb[1]);
+    gb[2] = fmaf(c, __builtin_bit_cast(float, x.y << 16), gb[2]);
+    gb[3] = fmaf(c, __builtin_bit_cast(float, x.y & 0xFFFF0000u), gb[3]);
+  }
+  u32x2 rd[4];           // one half's reads in flight
+  f32x4 c4;              // and its four row scales
+  __device__ __forceinline__ void read_half(int s, int h, const LDS_AS char* cur) {
+    c4 = *(const LDS_AS f32x4*)((const LDS_AS char*)0 + c_lds + (uint32_t)((s & 1) * 256 + (wave * 8 + 4 * h) * 4));
+#pragma unroll
+    for (int u = 0; u < 4; ++u) rd[u] = *(const LDS_AS u32x2*)(cur + addr(4 * h + u));
+  }
+  __device__ __forceinline__ void sum_half() {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) fma4(rd[u], c4[u]);
+  }
+  __device__ __forceinline__ void side(int slot, int s, const LDS_AS char* cur) {
+    if (s == next) {   // wave-uniform
+      if (slot == 6) read_half(s, 0, cur);
+      if (slot == 8) {
+        sum_half();
+        read_half(s, 1, cur);
+      }
+      if (slot == 10) {
+        sum_half();
+        next += n_nt;
+      }
+    }
+  }
+  // row scales of stage s + 2 when it is one of this tile's bias stages,
+  // issued with that stage's operand loads (stages 0 and 1: before the K loop)
+  __device__ __forceinline__ void side_load(int slot, int s, int nk) {
+    if (slot == 10 && s + 2 == next_c) {   // wave-uniform
+      if (wave == 0 && s + 2 < nk) load_c(s + 2);
+      next_c += n_nt;
+    }
+  }
 };
 
 // Schedule of one 64-deep stage s, in 16 slots of 4 MFMAs (slots 0..7:
@@ -308,7 +405,7 @@ struct FragAT {
 // the previous stage (slots 10..15), loads 6..7 go out in slots 0..1.
 template <class FS>
 __device__ __forceinline__ void mainloop_stage(Acc& acc, Frags& f0, Frags& f1, int s, int nk, LDS_AS char* smem,
-                                               const TileLoads& t, const FS& fs) {
+                                               const TileLoads& t, FS& fs) {
   LDS_AS char* cur = smem + (s & 1) * STAGE;
   LDS_AS char* nxt = smem + ((s + 1) & 1) * STAGE;
 #pragma unroll
@@ -332,10 +429,12 @@ __device__ __forceinline__ void mainloop_stage(Acc& acc, Frags& f0, Frags& f1, i
     } else if (slot >= 10) {
       if (s + 2 < nk) stage_load(t, s + 2, slot - 10);
     }
+    fs.side_load(slot, s, nk);
     if (FS::kPrioLoads) __builtin_amdgcn_s_setprio(0);
     // fragment reads: f1 of this stage in slots 0..5, f0 of the next in 10..15
     if (slot < 6) fs.read(f1, cur, 1, 2 * slot);
     else if (slot >= 10) fs.read(f0, nxt, 0, 2 * (slot - 10));
+    fs.side(slot, s, cur);
     FENCE();
     if (FS::kPrio) __builtin_amdgcn_s_setprio(1);
     acc.v[i][2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.a[i], f.b[2], acc.v[i][2], 0, 0, 0);
@@ -385,17 +484,14 @@ __device__ __forceinline__ void tile_prologue(const TileLoads& t, int nk) {
 #pragma unroll
     for (int f = 0; f < 6; ++f) stage_load(t, 1, f);
 }
-template <class FS = FragK>
-__device__ __forceinline__ void tile_run(Acc& acc, const TileLoads& t, int nk, LDS_AS char* smem) {
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+template <class FS>
+__device__ __forceinline__ void tile_run(Acc& acc, const TileLoads& t, int nk, LDS_AS char* smem, FS& fs) {
 #pragma unroll
   for (int i = 0; i < NB; ++i)
 #pragma unroll
     for (int j = 0; j < NBJ; ++j)
 #pragma unroll
       for (int r = 0; r < 4; ++r) acc.v[i][j][r] = 0.f;
-  const FS fs(wave, lane);
   if (nk > 1) __builtin_amdgcn_s_waitcnt(WAIT_VM(6));
   else __builtin_amdgcn_s_waitcnt(WAIT_VM0);
   __syncthreads();
@@ -404,6 +500,11 @@ __device__ __forceinline__ void tile_run(Acc& acc, const TileLoads& t, int nk, L
   for (int n = 0; n < NB + NBJ; ++n) fs.read(f0, smem, 0, n);
   for (int s = 0; s < nk; ++s) mainloop_stage(acc, f0, f1, s, nk, smem, t, fs);
   __builtin_amdgcn_s_waitcnt(WAIT_LGKM0);
+}
+__device__ __forceinline__ void tile_run(Acc& acc, const TileLoads& t, int nk, LDS_AS char* smem) {
+  const int tid = threadIdx.x;
+  FragK fs(__builtin_amdgcn_readfirstlane(tid >> 6), tid & 63);
+  tile_run(acc, t, nk, smem, fs);
 }
 __device__ __forceinline__ void gemm_tile(Acc& acc, const u16* __restrict__ X, int64_t ldx, int64_t kx,
                                           int64_t x_row0, int64_t x_rows, const u16* __restrict__ Y, int64_t ldy,
@@ -459,14 +560,6 @@ __global__ void __launch_bounds__(256) k_prepare_labels(const int64_t* __restric
 constexpr int PST_LD = 72;                     // u16 per staged row
 constexpr int PST_WAVE = 16 * PST_LD;          // u16 per wave
 
-// 16 x the lane index, computed where it is used: kept live across the K
-// loop it would be spilled, and its reload waits for every store in flight.
-__device__ __forceinline__ uint32_t lane_x16() {
-  uint32_t v;
-  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0\n\tv_lshlrev_b32 %0, 4, %0"
-               : "=v"(v));
-  return v;
-}
 
 // Forward tiles: z = h W^T + b for 256 rows x 256 vocabulary ids, reduced in
 // the epilogue to each row's (max, sum exp(z - max)) over each wave's
@@ -1095,11 +1188,14 @@ __device__ __forceinline__ void tr_slot(int wave, int lane, int b, int& k, int& 
 // The n_tiles - n_full left over would run as one thin last round, so each
 // is split over `split` workgroups by K; those write FP32 partial tiles to
 // part ([item][256][256]) and k_gw_reduce adds them in a fixed order.
+template <bool BIAS>
 __global__ void __launch_bounds__(NTHREADS, 1)
 k_gemm_grad_weight(const u16* __restrict__ G, int64_t slab_rows, const u16* __restrict__ hT, int nk, int64_t H,
                    int64_t V, int n_mt, int n_nt, int n_full, int split, int first, float* __restrict__ gw_f32,
-                   float* __restrict__ part, u16* __restrict__ gw_bf16, int keep32) {
+                   float* __restrict__ part, u16* __restrict__ gw_bf16, int keep32, const float* __restrict__ rowc,
+                   float* __restrict__ gb_f32) {
   __shared__ __attribute__((aligned(16))) char smem_raw[MAINLOOP_LDS];
+  __shared__ __attribute__((aligned(16))) float s_c[BIAS ? 2 * 64 : 4];   // row scales of two stages
   LDS_AS char* smem = (LDS_AS char*)smem_raw;
   int tm, tn, s0 = 0, s1 = nk, item = -1;
   if ((int)blockIdx.x < n_full) {
@@ -1132,8 +1228,35 @@ k_gemm_grad_weight(const u16* __restrict__ G, int64_t slab_rows, const u16* __re
   t.ky = H * BK * 2;
   t.lds_wave = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)smem + (uint32_t)wave * 32 * 128);
   Acc acc;
-  tile_prologue(t, s1 - s0);
-  tile_run<FragAT>(acc, t, s1 - s0, smem);
+  if (BIAS) {
+    // local stages s (global s0 + s) with (s0 + s) mod n_nt == tn carry the bias sums
+    const int first_local = ((tn - s0) % n_nt + n_nt) % n_nt;
+    FragATBias fs(wave, lane, rowc + (int64_t)s0 * 64,
+                  (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(LDS_AS char*)s_c), first_local,
+                  n_nt);
+    // the row scales of the bias stages among the first two go out before
+    // the operand loads, so tile_run's first wait covers them
+    if (wave == 0)
+      for (int sb = first_local; sb < 2 && sb < s1 - s0; sb += n_nt) fs.load_c(sb);
+    tile_prologue(t, s1 - s0);
+    tile_run(acc, t, s1 - s0, smem, fs);
+    if (first_local < s1 - s0) {   // this tile summed at least one stage: add its 256 column sums
+      __syncthreads();             // every wave is past its last read of the stage buffers
+      LDS_AS float* red = (LDS_AS float*)smem;
+      *(LDS_AS f32x4*)(red + wave * TILE + lane * 4) = (f32x4){fs.gb[0], fs.gb[1], fs.gb[2], fs.gb[3]};
+      __syncthreads();
+      if (tid < TILE) {
+        float sum = 0.f;
+#pragma unroll
+        for (int w = 0; w < NTHREADS / 64; ++w) sum += red[w * TILE + tid];
+        if (row0 + tid < V) atomicAdd(gb_f32 + row0 + tid, sum);
+      }
+    }
+  } else {
+    FragAT fs(wave, lane);
+    tile_prologue(t, s1 - s0);
+    tile_run(acc, t, s1 - s0, smem, fs);
+  }
   if (item >= 0) {   // partial tile of a split item: plain stores, summed by k_gw_reduce
     float* dst = part + (int64_t)item * TILE * TILE + wn * 64 + (lane & 15);
 #pragma unroll
@@ -1336,15 +1459,20 @@ hipError_t launch_grad_hidden(const Shapes& s, const void* dlog, const void* wT,
 
 hipError_t launch_grad_weight(const Shapes& s, const void* dlog, int64_t G, const void* hT, int64_t rows_valid,
                               float* part, int64_t part_items, int first, float* gw_f32, void* gw_bf16, int keep32,
-                              hipStream_t st) {
+                              const float* rowc, float* gb_f32, hipStream_t st) {
   const int n_mt = (int)(s.Vp / TILE), n_nt = (int)((s.H + TILE - 1) / TILE);
   const int nk = (int)((rows_valid + 63) / 64);
   const int n_tiles = n_mt * n_nt;
   int n_full = n_tiles, split = 1;
   grad_weight_split(n_tiles, nk, device_cus(), (int)part_items, &n_full, &split);
-  hipLaunchKernelGGL(k_gemm_grad_weight, dim3((unsigned)(n_full + (n_tiles - n_full) * split)), dim3(NTHREADS), 0,
-                     st, (const u16*)dlog, G, (const u16*)hT, nk, s.H, s.V, n_mt, n_nt, n_full, split, first, gw_f32,
-                     part, (u16*)gw_bf16, keep32);
+  const dim3 grid((unsigned)(n_full + (n_tiles - n_full) * split)), block(NTHREADS);
+  if (gb_f32 != nullptr)
+    hipLaunchKernelGGL(k_gemm_grad_weight<true>, grid, block, 0, st, (const u16*)dlog, G, (const u16*)hT, nk, s.H,
+                       s.V, n_mt, n_nt, n_full, split, first, gw_f32, part, (u16*)gw_bf16, keep32, rowc, gb_f32);
+  else
+    hipLaunchKernelGGL(k_gemm_grad_weight<false>, grid, block, 0, st, (const u16*)dlog, G, (const u16*)hT, nk, s.H,
+                       s.V, n_mt, n_nt, n_full, split, first, gw_f32, part, (u16*)gw_bf16, keep32,
+                       (const float*)nullptr, (float*)nullptr);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || n_full == n_tiles) return e;
   hipLaunchKernelGGL(k_gw_reduce, dim3(TILE, (unsigned)(n_tiles - n_full)), dim3(64), 0, st, part, n_full, split,

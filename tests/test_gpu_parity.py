@@ -209,6 +209,12 @@ def test_optional_outputs_and_f32(cuda):
     torch.cuda.synchronize()
     assert o.grad_weight is None and o.grad_bias is None
     assert_grad_close(np32(o.grad_hidden), ref.grad_hidden, "grad_hidden")
+    say("[gpu] grad_bias without grad_weight (its own column-sum pass)")
+    o = lce.lce_forward_backward(hd, wd, bd, yd, want_grad_hidden=False, want_grad_weight=False,
+                                 want_grad_bias=True, rows_in_flight=256)
+    torch.cuda.synchronize()
+    assert o.grad_weight is None and o.grad_hidden is None
+    assert_grad_close(np32(o.grad_bias), ref.grad_bias, "grad_bias alone")
     say("[gpu] only weight grads, fp32 exposed")
     o = lce.lce_forward_backward(hd, wd, bd, yd, want_grad_hidden=False, want_f32=True)
     torch.cuda.synchronize()

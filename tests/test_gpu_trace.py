@@ -66,12 +66,13 @@ def test_traced_forward_backward_matches_untraced(cuda):
         names = [_lib.KERNEL_KINDS[kinds[i]] for i in range(t.count)]
         groups = 3
         # per row group: the forward tiles, their retry (a no-op here), the
-        # row scales (and their retry), both row-reference steps, the bias
-        # sums and the two gradient products
+        # row scales (and their retry), both row-reference steps and the two
+        # gradient products; grad_bias is summed inside grad_weight's kernel
         for k, per_group in (("fwd_lse", 1), ("fwd_retry", 1), ("bwd_dlogits", 2), ("row_ref", 2),
-                             ("bias_sums", 1), ("grad_hidden", 1), ("grad_weight", 1), ("finalize_rows", 1)):
+                             ("grad_hidden", 1), ("grad_weight", 1), ("finalize_rows", 1)):
             assert names.count(k) == per_group * groups, (k, names)
         assert names.count("label_logit") == 1 and names.count("finalize_loss") == 1
+        assert names.count("bias_sums") == 0
         # product dims: grad_hidden rows x H x V, grad_weight V x H x the group's valid rows
         valid_rows = [g, g, n - 2 * g]
         gh = [i for i, k in enumerate(names) if k == "grad_hidden"]
