@@ -34,6 +34,13 @@
  *    first H used; weight: [V, ld_weight], first H used (nn.Linear layout, row
  *    j is vocabulary id j); labels: int64 [N], already aligned with the rows
  *    (any causal shift happens upstream).
+ *  - Reproducibility: n_valid, lse, per-row losses (NONE), grad_hidden and
+ *    grad_weight (bf16 and FP32) are bit-identical from call to call on the
+ *    same device and inputs (fixed summation orders). The SUM / MEAN loss and
+ *    the chunk sums add rows with float64 atomics, and grad_bias adds column
+ *    sums with FP32 atomics: their last bits may differ between calls.
+ *  - The label logit in l_i comes from the same FP32 accumulators as the
+ *    row's lse, so l_i >= 0 for every row.
  */
 #ifndef LCE_H
 #define LCE_H
