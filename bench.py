@@ -5,7 +5,8 @@
 A step is one lce_forward_backward call (every step of the method: label
 count, logits tiles with the online log-sum-exp, per-row NLL and chunk sums,
 dlogits, grad_hidden = G W, FP32 grad_weight = G^T h and grad_bias, the final
-bf16 casts) over the whole workload, with inputs, outputs and workspace
+bf16 casts; outputs the loss and the three gradients, as the pages' loss
+function does) over the whole workload, with inputs, outputs and workspace
 resident in HBM before the timed region starts. Prints ONE JSON line.
 
 Default workload: the Qwen3-8B-shaped head at one GPU's share of a 1M-token
@@ -327,7 +328,10 @@ def main() -> int:
     torch.cuda.reset_peak_memory_stats(dev)
 
     rif = args.rows_in_flight or None
-    kw = dict(chunk_rows=w.chunk_rows, reduction=w.reduction, rows_in_flight=rif, want_f32=False)
+    # The call the pages' loss function makes: the loss and the gradients
+    # (per-row lse is an optional diagnostic output of the library and is
+    # not asked for; ignored rows then need no work at all).
+    kw = dict(chunk_rows=w.chunk_rows, reduction=w.reduction, rows_in_flight=rif, want_f32=False, want_lse=False)
     log("[bench] first call")
     out = lce.lce_forward_backward(hd, wd, bd, yd, **kw)
     torch.cuda.synchronize()
@@ -416,7 +420,8 @@ def main() -> int:
         "config": {"workload": w.name, "n_rows": N, "hidden": H, "vocab": V, "bias": w.bias_std is not None,
                    "labels": w.labels + (f"({w.zipf_s})" if w.labels == "zipf" else ""),
                    "ignored_rows": w.n_ignored, "chunk_rows": w.chunk_rows, "reduction": w.reduction,
-                   "rows_in_flight": rif or 16384, "parallelism": "single GPU"},
+                   "rows_in_flight": rif or 16384, "parallelism": "single GPU",
+                   "outputs": "loss, grad_hidden, grad_weight, grad_bias (bf16; FP32 accumulation)"},
         "pct_peak_bf16": pct,
         "step_ms_min": per_step[0] if per_step else None,
         "step_ms_median": per_step[len(per_step) // 2] if per_step else None,

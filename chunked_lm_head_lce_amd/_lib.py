@@ -33,7 +33,7 @@ EXPORTED = ("lce_workspace_bytes", "lce_forward", "lce_forward_backward", "lce_f
 
 KERNEL_KINDS = ("zero", "prepare_labels", "fwd_lse", "finalize_rows", "finalize_loss", "transpose",
                 "bwd_dlogits", "grad_hidden", "grad_weight", "cast", "label_logit", "row_ref", "fwd_retry",
-                "bias_sums")
+                "bias_sums", "partition", "gather_rows")
 
 
 class LceProblem(ctypes.Structure):

@@ -26,6 +26,7 @@ struct Layout {
          tile_ctr = 0;
   // backward
   size_t zlab = 0, wT = 0, hT = 0, gw_part = 0, dlog = 0, gw_f32 = 0, gb_f32 = 0, rref = 0, rowc = 0, ovf = 0;
+  size_t block_cnt = 0, block_off = 0, perm = 0, labp = 0, hperm = 0;   // valid rows first
   size_t total = 0;
 };
 
@@ -100,7 +101,11 @@ Layout make_layout(const lce_problem* p, int kind, int64_t fwd_group = 0) {
   const Shapes s = shapes_of(p);
   Layout L;
   size_t off = 0;
+  // Regions of 1 MiB or more start on 2 MiB boundaries (relative to the
+  // workspace start): the operand streams of the product kernels then keep
+  // the same placement across DRAM pages whatever precedes them.
   auto take = [&](size_t bytes) {
+    if (bytes >= (size_t(1) << 20)) off = (off + (size_t(2) << 20) - 1) & ~((size_t(2) << 20) - 1);
     const size_t at = off;
     off = align256(off + bytes);
     return at;
@@ -122,6 +127,13 @@ Layout make_layout(const lce_problem* p, int kind, int64_t fwd_group = 0) {
   if (bwd) {
     const int64_t G = group_rows(p, s);
     L.zlab = take((size_t)s.Np * 4);   // label logits by a gather: the row references
+    // rows in the valid-first order: per-block counts and offsets, the
+    // permutation, its labels and the hidden rows gathered in that order
+    L.block_cnt = take((size_t)(s.Np / kTile) * 4);
+    L.block_off = take((size_t)(s.Np / kTile) * 4);
+    L.perm = take((size_t)s.Np * 4);
+    L.labp = take((size_t)s.Np * 4);
+    L.hperm = take((size_t)s.Np * s.H * 2);
     // W^T, the group's h^T and its p~ / G, all stored as K-slabs
     // [K/64][rows][64]
     L.wT = take((size_t)s.H * s.Vp * 2);
@@ -191,6 +203,12 @@ struct Common {
   float* zy2;
   double* chunk_acc;
   int* tile_ctr;
+  // valid-first row order (backward calls): row i of the work is the
+  // caller's row perm[i]; the forward covers rows below *fwd_limit and the
+  // backward rows below *bwd_limit (null: every row)
+  const int32_t* perm = nullptr;
+  const unsigned long long* fwd_limit = nullptr;
+  const unsigned long long* bwd_limit = nullptr;
 
   int64_t T;
 };
@@ -219,7 +237,7 @@ int check_common(const lce_problem* p, const void* hidden, const void* weight, c
 // every later step, including the MEAN scale of the first row group's
 // gradients, sees the final n_valid.
 int run_prepare(Common& c, const int64_t* labels, int64_t* n_valid_out, int32_t* status_out, hipStream_t st,
-                Tracer& tr) {
+                Tracer& tr, bool block_counts = false) {
   const Shapes& s = c.s;
   char* ws = c.ws;
   c.label32 = (int32_t*)(ws + c.L.label32);
@@ -238,7 +256,29 @@ int run_prepare(Common& c, const int64_t* labels, int64_t* n_valid_out, int32_t*
   if (s.N == 0) return LCE_OK;
   LCE_LAUNCH(tr, LCE_K_PREPARE_LABELS, 0, 0, 0,
              lce::launch_prepare_labels(labels, s.N, s.Np, s.V, c.p->ignore_index, c.label32, c.n_valid,
-                                        c.status, st));
+                                        c.status, block_counts ? (int32_t*)(ws + c.L.block_cnt) : nullptr, st));
+  return LCE_OK;
+}
+
+// Puts the rows in the valid-first order (labels and gathered hidden rows)
+// and makes every later step work on it: returns the gathered hidden rows.
+int run_valid_first(Common& c, const void* hidden, bool lse_for_all_rows, hipStream_t st, Tracer& tr,
+                    const void** hidden_out) {
+  char* ws = c.ws;
+  int32_t* perm = (int32_t*)(ws + c.L.perm);
+  int32_t* labp = (int32_t*)(ws + c.L.labp);
+  void* hperm = ws + c.L.hperm;
+  LCE_LAUNCH(tr, LCE_K_PARTITION, 0, 0, 0,
+             lce::launch_partition_rows(c.label32, (const int32_t*)(ws + c.L.block_cnt), (int32_t*)(ws + c.L.block_off),
+                                        c.n_valid, c.s.Np, perm, labp, st));
+  LCE_LAUNCH(tr, LCE_K_GATHER_ROWS, c.s.N, c.s.H, 0,
+             lce::launch_gather_rows(hidden, c.s.ldh, perm, c.s.N, c.s.H, hperm, st));
+  c.label32 = labp;
+  c.perm = perm;
+  c.s.ldh = c.s.H;
+  c.bwd_limit = c.n_valid;
+  c.fwd_limit = lse_for_all_rows ? nullptr : c.n_valid;
+  *hidden_out = hperm;
   return LCE_OK;
 }
 
@@ -261,11 +301,12 @@ int run_rows(Common& c, const void* hidden, const void* weight, const void* bias
   const int64_t rows_valid = (s.N - g0) < rows ? (s.N - g0) : rows;
   LCE_LAUNCH(tr, LCE_K_FWD_LSE, rows_valid, s.V, s.H,
              lce::launch_fwd_tiles(s, hidden, weight, bias, g0, rows, c.part_m, c.part_s, p_out, c.tile_ctr, rref,
-                                   ovf, nullptr, c.label32, c.zy2, st));
+                                   ovf, nullptr, c.label32, c.zy2, c.fwd_limit, st));
   LCE_LAUNCH(tr, LCE_K_FINALIZE_ROWS, 0, 0, 0,
              lce::launch_finalize_rows(s, c.part_m, c.part_s, g0, rows, c.zy2, c.label32, c.status,
                                        c.p->reduction, c.lse_ws, lse_out,
-                                       c.p->reduction == LCE_REDUCTION_NONE ? loss : nullptr, c.chunk_acc, st));
+                                       c.p->reduction == LCE_REDUCTION_NONE ? loss : nullptr, c.chunk_acc,
+                                       c.fwd_limit, c.perm, st));
   return LCE_OK;
 }
 
@@ -273,7 +314,7 @@ int run_rows(Common& c, const void* hidden, const void* weight, const void* bias
 
 extern "C" {
 
-int lce_abi_version(void) { return 104; }
+int lce_abi_version(void) { return 105; }
 
 const char* lce_status_string(int status) {
   switch (status) {
@@ -379,8 +420,17 @@ int lce_forward_backward_ex(const lce_problem* p, const void* hidden, const void
   tr.t = trace;
   tr.st = stream;
   if (trace) trace->count = 0;
-  st = run_prepare(c, labels, n_valid, status, stream, tr);
+  const bool any_grad = need_gh || need_gw || need_gb;
+  st = run_prepare(c, labels, n_valid, status, stream, tr, any_grad);
   if (st != LCE_OK) return st;
+  // the gradients only need the rows with a label: valid rows first, and
+  // the backward stops at the device-side valid count (the forward too,
+  // unless every row's lse or loss is an output)
+  const void* hid = hidden;
+  if (any_grad && c.s.N > 0) {
+    st = run_valid_first(c, hidden, lse != nullptr || p->reduction == LCE_REDUCTION_NONE, stream, tr, &hid);
+    if (st != LCE_OK) return st;
+  }
 
   const Shapes& s = c.s;
   char* ws = c.ws;
@@ -408,9 +458,8 @@ int lce_forward_backward_ex(const lce_problem* p, const void* hidden, const void
     float* rowc = (float*)(ws + c.L.rowc);
     int* ovf = (int*)(ws + c.L.ovf);
     const int is_mean = p->reduction == LCE_REDUCTION_MEAN;
-    const bool any_grad = need_gh || need_gw || need_gb;
     if (any_grad) {
-      st = run_label_logits(c, hidden, weight, bias, stream, tr);
+      st = run_label_logits(c, hid, weight, bias, stream, tr);
       if (st != LCE_OK) return st;
     }
     if (need_gh)
@@ -421,42 +470,42 @@ int lce_forward_backward_ex(const lce_problem* p, const void* hidden, const void
       const int64_t Gc = (s.Np - g0) < G ? (s.Np - g0) : G;
       const int64_t rows_valid = (s.N - g0) < Gc ? (s.N - g0) : Gc;
       if (!any_grad) {
-        st = run_rows(c, hidden, weight, bias, g0, Gc, nullptr, loss, lse, stream, tr);
+        st = run_rows(c, hid, weight, bias, g0, Gc, nullptr, loss, lse, stream, tr);
         if (st != LCE_OK) return st;
         continue;
       }
       LCE_LAUNCH(tr, LCE_K_ROW_REF, 0, 0, 0,
                  lce::launch_prep_ref(c.label32, c.zlab, g0, Gc, rref, nullptr, stream));
       LCE_LAUNCH(tr, LCE_K_ZERO, 0, 0, 0, lce::launch_zero(ovf, 4, stream));
-      st = run_rows(c, hidden, weight, bias, g0, Gc, dlog, loss, lse, stream, tr, rref, ovf);
+      st = run_rows(c, hid, weight, bias, g0, Gc, dlog, loss, lse, stream, tr, rref, ovf);
       if (st != LCE_OK) return st;
       LCE_LAUNCH(tr, LCE_K_BWD_DLOGITS, rows_valid, s.V, 0,
                  lce::launch_rowscale(c.label32, c.zy2, c.lse_ws, rref, row_scale, c.n_valid, grad_scale, is_mean,
-                                      g0, Gc, dlog, rowc, ovf, 0, need_gb ? gb : nullptr, stream));
+                                      g0, Gc, dlog, rowc, ovf, 0, need_gb ? gb : nullptr, c.perm, stream));
       // retry, only when the overflow flag is set
       LCE_LAUNCH(tr, LCE_K_ROW_REF, 0, 0, 0,
                  lce::launch_prep_ref(c.label32, c.lse_ws, g0, Gc, rref, ovf, stream));
       LCE_LAUNCH(tr, LCE_K_FWD_RETRY, 0, 0, 0,
-                 lce::launch_fwd_tiles(s, hidden, weight, bias, g0, Gc, c.part_m, c.part_s, dlog, c.tile_ctr, rref,
-                                       nullptr, ovf, c.label32, c.zy2, stream));
+                 lce::launch_fwd_tiles(s, hid, weight, bias, g0, Gc, c.part_m, c.part_s, dlog, c.tile_ctr, rref,
+                                       nullptr, ovf, c.label32, c.zy2, c.fwd_limit, stream));
       LCE_LAUNCH(tr, LCE_K_BWD_DLOGITS, rows_valid, s.V, 0,
                  lce::launch_rowscale(c.label32, c.zy2, c.lse_ws, rref, row_scale, c.n_valid, grad_scale, is_mean,
-                                      g0, Gc, dlog, rowc, ovf, 1, need_gb ? gb : nullptr, stream));
+                                      g0, Gc, dlog, rowc, ovf, 1, need_gb ? gb : nullptr, c.perm, stream));
       // grad_bias column sums: inside grad_weight's K loop when it runs
       if (need_gb && !need_gw)
         LCE_LAUNCH(tr, LCE_K_BIAS_SUMS, rows_valid, s.V, 0, lce::launch_bias_sums(s, dlog, rowc, Gc, gb, stream));
       if (need_gh)
         LCE_LAUNCH(tr, LCE_K_GRAD_HIDDEN, rows_valid, s.H, s.V,
-                   lce::launch_grad_hidden(s, dlog, wT, g0, Gc, rowc, grad_hidden, stream));
+                   lce::launch_grad_hidden(s, dlog, wT, g0, Gc, rowc, grad_hidden, c.bwd_limit, c.perm, stream));
       if (need_gw) {
         LCE_LAUNCH(tr, LCE_K_TRANSPOSE, 0, 0, 0,
-                   lce::launch_transpose(hidden, s.ldh, g0, rows_valid, s.H, hT, Gc, rowc, stream));
+                   lce::launch_transpose(hid, s.ldh, g0, rows_valid, s.H, hT, Gc, rowc, stream));
         LCE_LAUNCH(tr, LCE_K_GRAD_WEIGHT, s.V, s.H, rows_valid,
                    lce::launch_grad_weight(s, dlog, Gc, hT, rows_valid, gw_part, gw_part_items(s, G),
                                            (g0 == 0 && !accumulate) ? 1 : 0,
                                            gw, last ? grad_weight : nullptr,
                                            (!last || grad_weight == nullptr || grad_weight_f32 != nullptr) ? 1 : 0,
-                                           rowc, need_gb ? gb : nullptr, stream));
+                                           rowc, need_gb ? gb : nullptr, c.bwd_limit, g0, stream));
         if (last) gw_cast_done = true;
       }
     }

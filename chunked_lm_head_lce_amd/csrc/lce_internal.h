@@ -26,9 +26,19 @@ struct Shapes {
 };
 
 hipError_t launch_zero(void* p, int64_t bytes, hipStream_t st);
+// block_cnt (nullable): valid rows of each 256-row block (for the partition).
 hipError_t launch_prepare_labels(const int64_t* labels, int64_t N, int64_t Np, int64_t V, int64_t ignore,
                                  int32_t* label32, unsigned long long* n_valid, int32_t* status,
+                                 int32_t* block_cnt, hipStream_t st);
+// Valid rows first: perm[slot] = original row, labp[slot] = its label, valid
+// rows (label32 >= 0) in order in slots [0, n_valid), the others after them
+// in order (rows N..Np-1 last). block_off: Np/256 ints of scratch.
+hipError_t launch_partition_rows(const int32_t* label32, const int32_t* block_cnt, int32_t* block_off,
+                                 const unsigned long long* n_valid, int64_t Np, int32_t* perm, int32_t* labp,
                                  hipStream_t st);
+// out [N][H] (row stride H) = in[perm[slot]] (row stride ld_in), H % 8 == 0.
+hipError_t launch_gather_rows(const void* in, int64_t ld_in, const int32_t* perm, int64_t N, int64_t H, void* out,
+                              hipStream_t st);
 // Forward tiles for rows [g0, g0 + rows) (rows a multiple of 256): quarter-tile
 // (max, sumexp) partials into part_m/part_s [4 * Vp/256][rows] and, when
 // p_out is non-null, bf16 softmax numerators into p_out, stored as K-slabs
@@ -40,20 +50,24 @@ hipError_t launch_prepare_labels(const int64_t* labels, int64_t N, int64_t Np, i
 // *only_if != 0. Partials are base 2: (max t, sum 2^(t - max t)), t =
 // z log2(e). label32 [Np] (-1: no label): for each row with a label the
 // tile holding that column writes its t to zy2[row] (zy2 [Np], global rows).
+// row_limit (nullable): only rows below *row_limit (global index) get tiles.
 hipError_t launch_fwd_tiles(const Shapes& s, const void* hidden, const void* weight, const void* bias, int64_t g0,
                             int64_t rows, float* part_m, float* part_s, void* p_out, int* tile_ctr,
                             const float* rref, int* ovf, const int* only_if, const int32_t* label32, float* zy2,
-                            hipStream_t st);
+                            const unsigned long long* row_limit, hipStream_t st);
 // zlab[i] = h_i . W_{y_i} + b_{y_i} for valid rows (FP32 dot product: the
 // backward's per-row references, needed before the row's tiles run).
 hipError_t launch_label_logit(const Shapes& s, const void* hidden, const void* weight, const void* bias,
                               const int32_t* label32, float* zlab, hipStream_t st);
 // lse and l_i of rows [g0, g0 + rows) from the base-2 partials and the label
-// values zy2 written by the forward tiles.
+// values zy2 written by the forward tiles; rows at or past *row_limit
+// (nullable) are skipped. perm (nullable): row i is the caller's row
+// perm[i] for lse_out, rowloss_out and its chunk.
 hipError_t launch_finalize_rows(const Shapes& s, const float* part_m, const float* part_s, int64_t g0,
                                 int64_t rows, const float* zy2, const int32_t* label32, const int32_t* status,
                                 int reduction, float* lse_ws, float* lse_out, float* rowloss_out,
-                                double* chunk_acc, hipStream_t st);
+                                double* chunk_acc, const unsigned long long* row_limit, const int32_t* perm,
+                                hipStream_t st);
 hipError_t launch_finalize_loss(const double* chunk_acc, int64_t T, const unsigned long long* n_valid,
                                 const int32_t* status, int reduction, float* loss, float* chunk_out,
                                 hipStream_t st);
@@ -72,10 +86,11 @@ hipError_t launch_prep_ref(const int32_t* label32, const float* src, int64_t g0,
 // exp(z_y - rref_i) - exp(lse_i - rref_i), z_y = zy2 ln 2. Runs when
 // (*ovf != 0) == retry. gb_f32 (nullable) receives rowc[i] times the bf16
 // rounding of that entry.
+// perm (nullable): row_scale is indexed by the caller's row perm[row].
 hipError_t launch_rowscale(const int32_t* label32, const float* zy2, const float* lse_ws, const float* rref,
                            const float* row_scale, const unsigned long long* n_valid, float grad_scale, int is_mean,
                            int64_t g0, int64_t G, void* dlog, float* rowc, const int* ovf, int retry,
-                           float* gb_f32, hipStream_t st);
+                           float* gb_f32, const int32_t* perm, hipStream_t st);
 // gb_f32[v] += sum_i rowc[i] dlog[i][v] over the group's G rows (used when
 // grad_weight is not computed; otherwise its kernel adds these sums).
 hipError_t launch_bias_sums(const Shapes& s, const void* dlog, const float* rowc, int64_t G, float* gb_f32,
@@ -84,8 +99,11 @@ hipError_t launch_bias_sums(const Shapes& s, const void* dlog, const float* rowc
 hipError_t launch_scale(void* data, bool f32, int64_t n, const float* scale, hipStream_t st);
 // grad_hidden rows [g0, g0 + G): row i = rowc[i] (dlog wT^T)_i over K = Vp
 // (dlog: K-slabs [Vp/64][G][64], wT: [Vp/64][H][64]).
+// Row tiles at or past *row_limit (nullable) only write zero rows. perm
+// (nullable): row i goes to the caller's row perm[i].
 hipError_t launch_grad_hidden(const Shapes& s, const void* dlog, const void* wT, int64_t g0, int64_t G,
-                              const float* rowc, void* grad_hidden, hipStream_t st);
+                              const float* rowc, void* grad_hidden, const unsigned long long* row_limit,
+                              const int32_t* perm, hipStream_t st);
 // gw (+)= sum over the group's rows i < rows_valid of G[i][v] h[g0 + i][:]
 // (dlog: K-slabs [Vp/64][G][64] holding G; hT: the group's rows of h as
 // K-slabs [G/64][H][64], zero past N). part: part_items * 256 * 256 floats
@@ -94,9 +112,11 @@ hipError_t launch_grad_hidden(const Shapes& s, const void* dlog, const void* wT,
 // last row group); keep32 = 0: do not write the FP32 sums back. gb_f32
 // (nullable): also add the group's grad_bias column sums, sum_i rowc[i]
 // dlog[i][v] (FP32 atomics; rowc [G], the group's row scales).
+// row_limit (nullable): K stays below row *row_limit - g0 of the group.
 hipError_t launch_grad_weight(const Shapes& s, const void* dlog, int64_t G, const void* hT, int64_t rows_valid,
                               float* part, int64_t part_items, int first, float* gw_f32, void* gw_bf16, int keep32,
-                              const float* rowc, float* gb_f32, hipStream_t st);
+                              const float* rowc, float* gb_f32, const unsigned long long* row_limit, int64_t g0,
+                              hipStream_t st);
 // grad_weight's tiles: the first n_full run whole (a multiple of the CU
 // count), the rest are split `split` ways along K (split = 1: none) so that
 // they fill one round; at most min(max_items, kMaxGwItems) split pieces.

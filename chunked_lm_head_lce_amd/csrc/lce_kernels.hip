@@ -527,11 +527,12 @@ __global__ void k_zero(uint32_t* __restrict__ p, int64_t n_words) {
 
 // label32[i] = y_i if valid and in range, else -1 (rows N..Np-1 too).
 // n_valid += #valid rows; *status = LCE_ERR_LABEL_RANGE if any label is out of range.
+// block_cnt (nullable): valid rows of each 256-row block.
 __global__ void __launch_bounds__(256) k_prepare_labels(const int64_t* __restrict__ labels, int64_t N,
                                                         int64_t V, int64_t ignore_index,
                                                         int32_t* __restrict__ label32,
                                                         unsigned long long* __restrict__ n_valid,
-                                                        int32_t* __restrict__ status) {
+                                                        int32_t* __restrict__ status, int32_t* __restrict__ block_cnt) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   int lab = -1, bad = 0;
   if (i < N) {
@@ -547,6 +548,80 @@ __global__ void __launch_bounds__(256) k_prepare_labels(const int64_t* __restric
   if (threadIdx.x == 0) {
     if (cnt) atomicAdd(n_valid, (unsigned long long)cnt);
     if (anybad) *status = 5;  // LCE_ERR_LABEL_RANGE
+    if (block_cnt) block_cnt[blockIdx.x] = cnt;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Valid rows first. The backward only needs the rows with a label, so the
+// rows are put in a stable order with every valid row before every ignored
+// one (perm[slot] = original row; rows past N, which count as ignored, stay
+// last) and the hidden rows are gathered in that order. Every backward
+// kernel then stops at the device-side valid count: the host, which does not
+// know that count, launches for all rows, and the launches past it return
+// at once (grad_hidden writes the zero rows of ignored rows there).
+// ---------------------------------------------------------------------------
+// block_off[b] = sum of block_cnt[0 .. b-1]; one workgroup of 1024 threads.
+__global__ void __launch_bounds__(1024) k_scan_blocks(const int32_t* __restrict__ block_cnt, int64_t nb,
+                                                      int32_t* __restrict__ block_off) {
+  __shared__ int32_t s_w[16];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int32_t carry = 0;
+  for (int64_t base = 0; base < nb; base += 1024) {
+    const int64_t i = base + tid;
+    const int32_t v = i < nb ? block_cnt[i] : 0;
+    int32_t x = v;   // inclusive scan within the wave
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int32_t y = __shfl_up(x, d, 64);
+      if (lane >= d) x += y;
+    }
+    if (lane == 63) s_w[wave] = x;
+    __syncthreads();
+    int32_t before = 0;
+    for (int w = 0; w < wave; ++w) before += s_w[w];
+    int32_t total = 0;
+    for (int w = 0; w < 16; ++w) total += s_w[w];
+    if (i < nb) block_off[i] = carry + before + x - v;
+    carry += total;
+    __syncthreads();
+  }
+}
+
+// Slot of each row in the valid-first order; perm[slot] = row, labp[slot] =
+// its label (-1 ignored). 256 rows per workgroup, ranks by wave ballots.
+__global__ void __launch_bounds__(256) k_partition_rows(const int32_t* __restrict__ label32,
+                                                        const int32_t* __restrict__ block_off,
+                                                        const unsigned long long* __restrict__ n_valid, int64_t Np,
+                                                        int32_t* __restrict__ perm, int32_t* __restrict__ labp) {
+  __shared__ int32_t s_w[4];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t b = blockIdx.x, row = b * 256 + tid;
+  const int32_t lab = label32[row];
+  const uint64_t m = __ballot(lab >= 0);
+  if (lane == 0) s_w[wave] = (int32_t)__popcll(m);
+  __syncthreads();
+  int32_t rank = (int32_t)__popcll(m & ((1ull << lane) - 1ull));   // valid rows before this one in the wave
+  for (int w = 0; w < wave; ++w) rank += s_w[w];
+  const int64_t off = block_off[b];
+  const int64_t slot = lab >= 0 ? off + rank
+                                : (int64_t)*n_valid + (b * 256 - off) + (tid - rank);   // ignored rows in order
+  if (slot >= 0 && slot < Np) {   // always (the counts add up to Np); a guard against a stale count
+    perm[slot] = (int32_t)row;
+    labp[slot] = lab;
+  }
+}
+
+// out[slot][:] = in[perm[slot]][:] for slot < N (H columns, 16-byte copies).
+__global__ void __launch_bounds__(256) k_gather_rows(const u16* __restrict__ in, int64_t ld_in,
+                                                     const int32_t* __restrict__ perm, int64_t N, int64_t H,
+                                                     u16* __restrict__ out) {
+  const int64_t chunks = H / 8;
+  const int64_t total = N * chunks;
+  for (int64_t k = (int64_t)blockIdx.x * 256 + threadIdx.x; k < total; k += (int64_t)gridDim.x * 256) {
+    const int64_t slot = k / chunks, c = k - slot * chunks;
+    const u32x4 v = *(const u32x4*)(in + (int64_t)perm[slot] * ld_in + c * 8);
+    *(u32x4*)(out + slot * H + c * 8) = v;
   }
 }
 
@@ -595,13 +670,19 @@ k_fwd_tile(const u16* __restrict__ hidden, int64_t ldh, const u16* __restrict__ 
            const u16* __restrict__ bias, int64_t N, int64_t V, int64_t H, int64_t g0, int64_t ld_part, int n_mt,
            int n_vt, float* __restrict__ part_m, float* __restrict__ part_s, u16* __restrict__ p_out,
            int* __restrict__ tile_ctr, const float* __restrict__ rref, int* __restrict__ ovf,
-           const int* __restrict__ only_if, const int32_t* __restrict__ label32, float* __restrict__ zy2) {
+           const int* __restrict__ only_if, const int32_t* __restrict__ label32, float* __restrict__ zy2,
+           const unsigned long long* __restrict__ row_limit) {
   __shared__ __attribute__((aligned(16))) char smem_raw[MAINLOOP_LDS];
   __shared__ __attribute__((aligned(16))) u16 s_pst[STORE_P ? 8 * PST_WAVE : 8];
   __shared__ __attribute__((aligned(16))) float s_ref[STORE_P ? 2 * TILE : 4];   // per-row references, two tiles
   __shared__ __attribute__((aligned(16))) int s_lab[2 * TILE];                    // per-row labels, two tiles
   __shared__ int s_next;
   if (only_if != nullptr && *only_if == 0) return;   // a retry launch with nothing to retry
+  if (row_limit != nullptr) {   // only the row tiles below the device-side limit (global row index)
+    const int64_t lim = (int64_t)*row_limit - g0;
+    const int64_t mt = lim <= 0 ? 0 : (lim + TILE - 1) / TILE;
+    if (mt < n_mt) n_mt = (int)mt;
+  }
   LDS_AS char* smem = (LDS_AS char*)smem_raw;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int wm = wave >> 2, wn = wave & 3;
@@ -836,11 +917,15 @@ __global__ void __launch_bounds__(64 * FIN_WAVES) k_finalize_rows(
     int n_part, const float* __restrict__ zy2, const int32_t* __restrict__ label32, int64_t N,
     int64_t row_begin, int64_t row_end, int64_t chunk_rows, const int32_t* __restrict__ status, int reduction,
     float* __restrict__ lse_ws, float* __restrict__ lse_out, float* __restrict__ rowloss_out,
-    double* __restrict__ chunk_acc) {
+    double* __restrict__ chunk_acc, const unsigned long long* __restrict__ row_limit,
+    const int32_t* __restrict__ perm) {
   __shared__ float s_m[FIN_WAVES][FIN_ROWS], s_s[FIN_WAVES][FIN_ROWS];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t i = row_begin + (int64_t)blockIdx.x * FIN_ROWS + lane;
-  const bool live = i < row_end && i < N;
+  // rows at or past the device-side limit had no tiles (their partials are stale)
+  const int64_t lim = row_limit != nullptr ? (int64_t)*row_limit : N;
+  if (row_begin + (int64_t)blockIdx.x * FIN_ROWS >= lim) return;   // uniform: the whole block
+  const bool live = i < row_end && i < N && i < lim;
   float M = -INFINITY, S = 0.f;
   if (live) {
     // four independent running (max, sum) pairs, so that four loads and four
@@ -868,7 +953,7 @@ __global__ void __launch_bounds__(64 * FIN_WAVES) k_finalize_rows(
   s_s[wave][lane] = S;
   __syncthreads();
   if (wave != 0 || i >= row_end) return;
-  if (i >= N) {
+  if (i >= N || i >= lim) {
     lse_ws[i] = 0.f;
     return;
   }
@@ -880,9 +965,10 @@ __global__ void __launch_bounds__(64 * FIN_WAVES) k_finalize_rows(
   const int lab = label32[i];
   const float l = lab >= 0 ? LN2 * ((M - zy2[i]) + L) : 0.f;   // M >= t_y: never negative
   lse_ws[i] = lse;
-  if (lse_out) lse_out[i] = lse;
-  if (reduction == 0 && rowloss_out) rowloss_out[i] = (*status != 0) ? NAN : l;
-  atomicAdd(&chunk_acc[i / chunk_rows], (double)l);
+  const int64_t oi = perm != nullptr ? (int64_t)perm[i] : i;   // the caller's row
+  if (lse_out) lse_out[oi] = lse;
+  if (reduction == 0 && rowloss_out) rowloss_out[oi] = (*status != 0) ? NAN : l;
+  atomicAdd(&chunk_acc[oi / chunk_rows], (double)l);
 }
 
 // One block: total loss from the chunk sums (float64), MEAN scaling, NaN on a
@@ -1012,7 +1098,7 @@ __global__ void __launch_bounds__(256) k_rowscale(const int32_t* __restrict__ la
                                                   const unsigned long long* __restrict__ n_valid, float grad_scale,
                                                   int is_mean, int64_t g0, int64_t G, u16* __restrict__ dlog,
                                                   float* __restrict__ rowc, const int* __restrict__ ovf, int retry,
-                                                  float* __restrict__ gb_f32) {
+                                                  float* __restrict__ gb_f32, const int32_t* __restrict__ perm) {
   if ((*ovf != 0) != (retry != 0)) return;
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (i >= G) return;
@@ -1028,7 +1114,7 @@ __global__ void __launch_bounds__(256) k_rowscale(const int32_t* __restrict__ la
     scale = grad_scale / (float)(nv > 0 ? nv : 1ull);
   }
   const float r = rref[i], lse = lse_ws[row];
-  const float c = scale * (row_scale != nullptr ? row_scale[row] : 1.f) * expf(r - lse);
+  const float c = scale * (row_scale != nullptr ? row_scale[perm != nullptr ? perm[row] : row] : 1.f) * expf(r - lse);
   const float pl = expf(zy2[row] * LN2 - r) - expf(lse - r);
   const u16 pb = f2bf(pl);
   rowc[i] = c;
@@ -1087,7 +1173,8 @@ __global__ void __launch_bounds__(256) k_bias_sums(const u16* __restrict__ dlog,
 __global__ void __launch_bounds__(NTHREADS, 1)
 k_gemm_grad_hidden(const u16* __restrict__ dlog, const u16* __restrict__ wT, int64_t Vp, int64_t H,
                    int64_t N, int64_t g0, int64_t G, int n_mt, int n_nt, const float* __restrict__ rowc,
-                   u16* __restrict__ grad_hidden) {
+                   u16* __restrict__ grad_hidden, const unsigned long long* __restrict__ row_limit,
+                   const int32_t* __restrict__ perm) {
   __shared__ __attribute__((aligned(16))) char smem_raw[MAINLOOP_LDS];
   LDS_AS char* smem = (LDS_AS char*)smem_raw;
   int tm, tn;
@@ -1095,6 +1182,17 @@ k_gemm_grad_hidden(const u16* __restrict__ dlog, const u16* __restrict__ wT, int
   const int64_t lrow0 = (int64_t)tm * TILE, col0 = (int64_t)tn * TILE;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int wm = wave >> 2, wn = wave & 3;
+  if (row_limit != nullptr && g0 + lrow0 >= (int64_t)*row_limit) {
+    // rows without a label (all of this tile's): their grad_hidden is zero
+    const int64_t c0 = col0 + tid % 32 * 8;
+    if (c0 < H)
+      for (int r = tid / 32; r < TILE; r += NTHREADS / 32) {
+        const int64_t row = g0 + lrow0 + r;
+        if (row >= N) break;
+        *(u32x4*)(grad_hidden + (int64_t)(perm != nullptr ? perm[row] : row) * H + c0) = (u32x4){0, 0, 0, 0};
+      }
+    return;
+  }
   Acc acc;
   gemm_tile(acc, dlog, BK, G * BK * 2, lrow0, G, wT, BK, H * BK * 2, col0, H, Vp, smem);
 #pragma unroll
@@ -1104,10 +1202,11 @@ k_gemm_grad_hidden(const u16* __restrict__ dlog, const u16* __restrict__ wT, int
       const int64_t row = g0 + lrow0 + acc_row(wm, i, r, lane);
       if (row >= N) continue;
       const float c = rowc[lrow0 + acc_row(wm, i, r, lane)];
+      const int64_t orow = perm != nullptr ? (int64_t)perm[row] : row;   // the caller's row
 #pragma unroll
       for (int j = 0; j < NBJ; ++j) {
         const int64_t col = col0 + acc_col(wn, j, lane);
-        if (col < H) grad_hidden[row * H + col] = f2bf(c * acc.v[i][j][r]);
+        if (col < H) grad_hidden[orow * H + col] = f2bf(c * acc.v[i][j][r]);
       }
     }
 }
@@ -1193,7 +1292,7 @@ __global__ void __launch_bounds__(NTHREADS, 1)
 k_gemm_grad_weight(const u16* __restrict__ G, int64_t slab_rows, const u16* __restrict__ hT, int nk, int64_t H,
                    int64_t V, int n_mt, int n_nt, int n_full, int split, int first, float* __restrict__ gw_f32,
                    float* __restrict__ part, u16* __restrict__ gw_bf16, int keep32, const float* __restrict__ rowc,
-                   float* __restrict__ gb_f32) {
+                   float* __restrict__ gb_f32, const unsigned long long* __restrict__ row_limit, int64_t g0) {
   __shared__ __attribute__((aligned(16))) char smem_raw[MAINLOOP_LDS];
   __shared__ __attribute__((aligned(16))) float s_c[BIAS ? 2 * 64 : 4];   // row scales of two stages
   LDS_AS char* smem = (LDS_AS char*)smem_raw;
@@ -1208,6 +1307,12 @@ k_gemm_grad_weight(const u16* __restrict__ G, int64_t slab_rows, const u16* __re
     tile_from_index<GW_GROUP_M>(n_full + item / split, n_mt, n_nt, tm, tn);
     s0 = (int)((int64_t)nk * sp / split);
     s1 = (int)((int64_t)nk * (sp + 1) / split);
+  }
+  if (row_limit != nullptr) {   // K stages past the device-side row limit hold only rows without a label
+    const int64_t lim = (int64_t)*row_limit - g0;
+    const int nk_lim = lim <= 0 ? 0 : (int)((lim + 63) / 64);
+    if (s1 > nk_lim) s1 = nk_lim;
+    if (s0 > s1) s0 = s1;
   }
   const int64_t row0 = (int64_t)tm * TILE, col0 = (int64_t)tn * TILE;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -1228,7 +1333,12 @@ k_gemm_grad_weight(const u16* __restrict__ G, int64_t slab_rows, const u16* __re
   t.ky = H * BK * 2;
   t.lds_wave = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)smem + (uint32_t)wave * 32 * 128);
   Acc acc;
-  if (BIAS) {
+  if (s1 == s0) {   // nothing below the row limit: the tile adds zero
+#pragma unroll
+    for (int i = 0; i < NB; ++i)
+#pragma unroll
+      for (int j = 0; j < NBJ; ++j) acc.v[i][j] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  } else if (BIAS) {
     // local stages s (global s0 + s) with (s0 + s) mod n_nt == tn carry the bias sums
     const int first_local = ((tn - s0) % n_nt + n_nt) % n_nt;
     FragATBias fs(wave, lane, rowc + (int64_t)s0 * 64,
@@ -1342,9 +1452,29 @@ hipError_t launch_zero(void* p, int64_t bytes, hipStream_t st) {
 
 hipError_t launch_prepare_labels(const int64_t* labels, int64_t N, int64_t Np, int64_t V, int64_t ignore,
                                  int32_t* label32, unsigned long long* n_valid, int32_t* status,
-                                 hipStream_t st) {
+                                 int32_t* block_cnt, hipStream_t st) {
   hipLaunchKernelGGL(k_prepare_labels, dim3((unsigned)(Np / 256)), dim3(256), 0, st, labels, N, V, ignore,
-                     label32, n_valid, status);
+                     label32, n_valid, status, block_cnt);
+  return hipGetLastError();
+}
+
+hipError_t launch_partition_rows(const int32_t* label32, const int32_t* block_cnt, int32_t* block_off,
+                                 const unsigned long long* n_valid, int64_t Np, int32_t* perm, int32_t* labp,
+                                 hipStream_t st) {
+  const int64_t nb = Np / 256;
+  hipLaunchKernelGGL(k_scan_blocks, dim3(1), dim3(1024), 0, st, block_cnt, nb, block_off);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_partition_rows, dim3((unsigned)nb), dim3(256), 0, st, label32, block_off, n_valid, Np, perm,
+                     labp);
+  return hipGetLastError();
+}
+
+hipError_t launch_gather_rows(const void* in, int64_t ld_in, const int32_t* perm, int64_t N, int64_t H, void* out,
+                              hipStream_t st) {
+  if (N <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_gather_rows, dim3(grid_1d(N * (H / 8), 256, 16384)), dim3(256), 0, st, (const u16*)in, ld_in,
+                     perm, N, H, (u16*)out);
   return hipGetLastError();
 }
 
@@ -1374,7 +1504,7 @@ static int persistent_grid(int64_t ntiles) {
 hipError_t launch_fwd_tiles(const Shapes& s, const void* hidden, const void* weight, const void* bias, int64_t g0,
                             int64_t rows, float* part_m, float* part_s, void* p_out, int* tile_ctr,
                             const float* rref, int* ovf, const int* only_if, const int32_t* label32, float* zy2,
-                            hipStream_t st) {
+                            const unsigned long long* row_limit, hipStream_t st) {
   const int n_mt = (int)(rows / TILE), n_vt = (int)(s.Vp / TILE);
   const int nb = persistent_grid((int64_t)n_mt * n_vt);
   if (nb == 0) return hipSuccess;
@@ -1384,11 +1514,11 @@ hipError_t launch_fwd_tiles(const Shapes& s, const void* hidden, const void* wei
   if (p_out)
     hipLaunchKernelGGL(k_fwd_tile<true>, grid, block, 0, st, (const u16*)hidden, s.ldh, (const u16*)weight, s.ldw,
                        (const u16*)bias, s.N, s.V, s.H, g0, rows, n_mt, n_vt, part_m, part_s, (u16*)p_out, tile_ctr,
-                       rref, ovf, only_if, label32, zy2);
+                       rref, ovf, only_if, label32, zy2, row_limit);
   else
     hipLaunchKernelGGL(k_fwd_tile<false>, grid, block, 0, st, (const u16*)hidden, s.ldh, (const u16*)weight,
                        s.ldw, (const u16*)bias, s.N, s.V, s.H, g0, rows, n_mt, n_vt, part_m, part_s, (u16*)nullptr,
-                       tile_ctr, (const float*)nullptr, (int*)nullptr, only_if, label32, zy2);
+                       tile_ctr, (const float*)nullptr, (int*)nullptr, only_if, label32, zy2, row_limit);
   return hipGetLastError();
 }
 
@@ -1403,10 +1533,11 @@ hipError_t launch_label_logit(const Shapes& s, const void* hidden, const void* w
 hipError_t launch_finalize_rows(const Shapes& s, const float* part_m, const float* part_s, int64_t g0,
                                 int64_t rows, const float* zy2, const int32_t* label32, const int32_t* status,
                                 int reduction, float* lse_ws, float* lse_out, float* rowloss_out,
-                                double* chunk_acc, hipStream_t st) {
+                                double* chunk_acc, const unsigned long long* row_limit, const int32_t* perm,
+                                hipStream_t st) {
   hipLaunchKernelGGL(k_finalize_rows, dim3((unsigned)(rows / FIN_ROWS)), dim3(64 * FIN_WAVES), 0, st, part_m, part_s, rows, g0,
                      (int)(NQ * (s.Vp / TILE)), zy2, label32, s.N, g0, g0 + rows, s.chunk_rows, status, reduction,
-                     lse_ws, lse_out, rowloss_out, chunk_acc);
+                     lse_ws, lse_out, rowloss_out, chunk_acc, row_limit, perm);
   return hipGetLastError();
 }
 
@@ -1436,9 +1567,9 @@ hipError_t launch_prep_ref(const int32_t* label32, const float* src, int64_t g0,
 hipError_t launch_rowscale(const int32_t* label32, const float* zy2, const float* lse_ws, const float* rref,
                            const float* row_scale, const unsigned long long* n_valid, float grad_scale, int is_mean,
                            int64_t g0, int64_t G, void* dlog, float* rowc, const int* ovf, int retry,
-                           float* gb_f32, hipStream_t st) {
+                           float* gb_f32, const int32_t* perm, hipStream_t st) {
   hipLaunchKernelGGL(k_rowscale, dim3((unsigned)((G + 255) / 256)), dim3(256), 0, st, label32, zy2, lse_ws, rref,
-                     row_scale, n_valid, grad_scale, is_mean, g0, G, (u16*)dlog, rowc, ovf, retry, gb_f32);
+                     row_scale, n_valid, grad_scale, is_mean, g0, G, (u16*)dlog, rowc, ovf, retry, gb_f32, perm);
   return hipGetLastError();
 }
 
@@ -1450,16 +1581,19 @@ hipError_t launch_bias_sums(const Shapes& s, const void* dlog, const float* rowc
 }
 
 hipError_t launch_grad_hidden(const Shapes& s, const void* dlog, const void* wT, int64_t g0, int64_t G,
-                              const float* rowc, void* grad_hidden, hipStream_t st) {
+                              const float* rowc, void* grad_hidden, const unsigned long long* row_limit,
+                              const int32_t* perm, hipStream_t st) {
   const int n_mt = (int)(G / TILE), n_nt = (int)((s.H + TILE - 1) / TILE);
   hipLaunchKernelGGL(k_gemm_grad_hidden, dim3((unsigned)(n_mt * n_nt)), dim3(NTHREADS), 0, st,
-                     (const u16*)dlog, (const u16*)wT, s.Vp, s.H, s.N, g0, G, n_mt, n_nt, rowc, (u16*)grad_hidden);
+                     (const u16*)dlog, (const u16*)wT, s.Vp, s.H, s.N, g0, G, n_mt, n_nt, rowc, (u16*)grad_hidden,
+                     row_limit, perm);
   return hipGetLastError();
 }
 
 hipError_t launch_grad_weight(const Shapes& s, const void* dlog, int64_t G, const void* hT, int64_t rows_valid,
                               float* part, int64_t part_items, int first, float* gw_f32, void* gw_bf16, int keep32,
-                              const float* rowc, float* gb_f32, hipStream_t st) {
+                              const float* rowc, float* gb_f32, const unsigned long long* row_limit, int64_t g0,
+                              hipStream_t st) {
   const int n_mt = (int)(s.Vp / TILE), n_nt = (int)((s.H + TILE - 1) / TILE);
   const int nk = (int)((rows_valid + 63) / 64);
   const int n_tiles = n_mt * n_nt;
@@ -1468,11 +1602,12 @@ hipError_t launch_grad_weight(const Shapes& s, const void* dlog, int64_t G, cons
   const dim3 grid((unsigned)(n_full + (n_tiles - n_full) * split)), block(NTHREADS);
   if (gb_f32 != nullptr)
     hipLaunchKernelGGL(k_gemm_grad_weight<true>, grid, block, 0, st, (const u16*)dlog, G, (const u16*)hT, nk, s.H,
-                       s.V, n_mt, n_nt, n_full, split, first, gw_f32, part, (u16*)gw_bf16, keep32, rowc, gb_f32);
+                       s.V, n_mt, n_nt, n_full, split, first, gw_f32, part, (u16*)gw_bf16, keep32, rowc, gb_f32,
+                       row_limit, g0);
   else
     hipLaunchKernelGGL(k_gemm_grad_weight<false>, grid, block, 0, st, (const u16*)dlog, G, (const u16*)hT, nk, s.H,
                        s.V, n_mt, n_nt, n_full, split, first, gw_f32, part, (u16*)gw_bf16, keep32,
-                       (const float*)nullptr, (float*)nullptr);
+                       (const float*)nullptr, (float*)nullptr, row_limit, g0);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || n_full == n_tiles) return e;
   hipLaunchKernelGGL(k_gw_reduce, dim3(TILE, (unsigned)(n_tiles - n_full)), dim3(64), 0, st, part, n_full, split,

@@ -146,12 +146,16 @@ int lce_forward_backward(const lce_problem* p, const void* hidden, const void* w
  * group's row references; LCE_K_FWD_RETRY recomputes a group's stored
  * numerators against r_i = lse_i when a row's maximum lies more than 60
  * above its label logit (otherwise it returns at once); LCE_K_BIAS_SUMS
- * adds the group's grad_bias column sums. */
+ * adds the group's grad_bias column sums (only when grad_weight is not
+ * computed: otherwise its kernel adds them); LCE_K_PARTITION orders the rows
+ * with a label before the others (two launches, recorded as one) and
+ * LCE_K_GATHER_ROWS copies the hidden rows into that order: the backward
+ * then works on the rows with a label only. */
 typedef enum {
   LCE_K_ZERO = 0, LCE_K_PREPARE_LABELS = 1, LCE_K_FWD_LSE = 2, LCE_K_FINALIZE_ROWS = 3,
   LCE_K_FINALIZE_LOSS = 4, LCE_K_TRANSPOSE = 5, LCE_K_BWD_DLOGITS = 6, LCE_K_GRAD_HIDDEN = 7,
   LCE_K_GRAD_WEIGHT = 8, LCE_K_CAST = 9, LCE_K_LABEL_LOGIT = 10, LCE_K_ROW_REF = 11, LCE_K_FWD_RETRY = 12,
-  LCE_K_BIAS_SUMS = 13, LCE_K_COUNT = 14
+  LCE_K_BIAS_SUMS = 13, LCE_K_PARTITION = 14, LCE_K_GATHER_ROWS = 15, LCE_K_COUNT = 16
 } lce_kernel_kind;
 
 typedef struct {

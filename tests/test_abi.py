@@ -48,7 +48,7 @@ def test_exports_every_declared_function(lib):
 
 
 def test_version_and_strings(lib):
-    assert lib.lce_abi_version() == 104
+    assert lib.lce_abi_version() == 105
     for code in range(7):
         assert _lib.status_string(code) != "unknown status"
     assert _lib.status_string(99) == "unknown status"
@@ -102,11 +102,18 @@ def layout(n, h, v, kind, rows_in_flight=0, chunk_rows=256):
         split_max = min(8, g // 256)
         n_tiles = n_vt * -(-h // 256)
         items = min(256, n_tiles * split_max) if split_max >= 2 else 0
-        regions += [("zlab", np_ * 4), ("wT", h * vp * 2), ("hT", h * g * 2), ("gw_part", items * 256 * 256 * 4),
+        regions += [("zlab", np_ * 4), ("block_cnt", np_ // 256 * 4), ("block_off", np_ // 256 * 4),
+                    ("perm", np_ * 4), ("labp", np_ * 4), ("hperm", np_ * h * 2),
+                    ("wT", h * vp * 2), ("hT", h * g * 2), ("gw_part", items * 256 * 256 * 4),
                     ("dlog", g * vp * 2), ("gb_f32", vp * 4), ("rref", g * 4), ("rowc", g * 4), ("ovf", 4)]
         if kind == 1:
             regions.append(("gw_f32", v * h * 4))
-    return dict(regions), sum(_up(b, 256) for _, b in regions)
+    off = 0
+    for _, b in regions:   # regions of 1 MiB or more start on 2 MiB boundaries
+        if b >= 1 << 20:
+            off = _up(off, 2 << 20)
+        off = _up(off + b, 256)
+    return dict(regions), off
 
 
 @pytest.mark.parametrize("name", ["tiny", "qwen3_0p6b_head", "qwen3_4b_32k", "qwen3_4b_160k", "qwen3_8b_1m_shard"])

@@ -109,6 +109,51 @@ def test_row_groups_match(cuda):
         check_all(out, ref, inp, "sum")
 
 
+@pytest.mark.parametrize("reduction,want_lse", [("sum", True), ("sum", False), ("mean", False)])
+def test_mostly_ignored_rows(cuda, reduction, want_lse):
+    """A masked prompt plus scattered ignored rows (70% in all) over six row
+    groups: the backward works on the labelled rows only (valid rows first,
+    stopping at the device-side count), so whole groups and tiles have no
+    work; every output must still match the oracle, ignored rows' grad_hidden
+    must be exactly zero and, when asked for, their lse must be right too."""
+    import dataclasses
+    inp = make_case(1500, 128, 3000, seed=44, bias_std=0.05, ignore_frac=0.1, weight_std=0.05)
+    y = inp.labels.copy()
+    y[:900] = IGNORE_INDEX                                   # the prompt
+    inp = dataclasses.replace(inp, labels=y)
+    hd, wd, bd, yd = to_device(inp, cuda)
+    say(f"[gpu] mostly ignored rows reduction={reduction} lse={want_lse}")
+    out = lce.lce_forward_backward(hd, wd, bd, yd, reduction=reduction, rows_in_flight=256, want_lse=want_lse,
+                                   want_chunk_loss=True)
+    torch.cuda.synchronize()
+    ref = oracle_of(inp, reduction)
+    assert int(out.n_valid.item()) == ref.n_valid == int((y >= 0).sum())
+    assert_loss_close(float(out.loss.item()), ref.loss)
+    assert_rows_close(np32(out.chunk_loss), ref.chunk_loss, "chunk sums")
+    if want_lse:
+        assert_rows_close(np32(out.lse), ref.lse, "lse, every row")
+    assert_grad_close(np32(out.grad_hidden), ref.grad_hidden, "grad_hidden")
+    assert_grad_close(np32(out.grad_weight), ref.grad_weight, "grad_weight")
+    assert_grad_close(np32(out.grad_bias), ref.grad_bias, "grad_bias")
+    ign = torch.from_numpy(y == IGNORE_INDEX).to(cuda)
+    assert torch.count_nonzero(out.grad_hidden[ign]) == 0
+
+
+def test_no_valid_rows_backward(cuda):
+    """Every row ignored: zero loss and zero gradients from a backward that
+    has no row to work on."""
+    inp = make_case(700, 128, 900, seed=45, bias_std=0.05, ignore_frac=0.0)
+    hd, wd, bd, _ = to_device(inp, cuda)
+    yd = torch.full((700,), IGNORE_INDEX, dtype=torch.int64, device=cuda)
+    for reduction in ("sum", "mean"):
+        say(f"[gpu] no valid rows, {reduction}")
+        out = lce.lce_forward_backward(hd, wd, bd, yd, reduction=reduction, rows_in_flight=256, want_f32=True)
+        torch.cuda.synchronize()
+        assert int(out.n_valid.item()) == 0 and float(out.loss.item()) == 0.0
+        for t in (out.grad_hidden, out.grad_weight, out.grad_bias, out.grad_weight_f32, out.grad_bias_f32):
+            assert torch.count_nonzero(t) == 0
+
+
 def test_confident_rows_have_nonnegative_loss(cuda):
     """Rows whose label logit exceeds every other logit by ~30 have a loss of
     ~1e-9. The label logit is taken from the same FP32 accumulators that

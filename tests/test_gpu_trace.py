@@ -73,6 +73,7 @@ def test_traced_forward_backward_matches_untraced(cuda):
             assert names.count(k) == per_group * groups, (k, names)
         assert names.count("label_logit") == 1 and names.count("finalize_loss") == 1
         assert names.count("bias_sums") == 0
+        assert names.count("partition") == 1 and names.count("gather_rows") == 1   # valid rows first
         # product dims: grad_hidden rows x H x V, grad_weight V x H x the group's valid rows
         valid_rows = [g, g, n - 2 * g]
         gh = [i for i, k in enumerate(names) if k == "grad_hidden"]

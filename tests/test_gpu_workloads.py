@@ -31,14 +31,15 @@ def _out_bytes(out) -> int:
 
 
 def _timed_call_with_peak(cuda, w, hd, wd, bd, yd, **kw):
-    """The benchmark's call (bf16 outputs, FP32 accumulators in workspace,
-    default row group) with the peak HBM it adds beyond inputs and outputs;
-    no [N, V] logits exist, so it stays below FP32 [N, V] logits."""
+    """The benchmark's call (loss and bf16 gradients only: no per-row lse,
+    FP32 accumulators in workspace, default row group) with the peak HBM it
+    adds beyond inputs and outputs; no [N, V] logits exist, so it stays
+    below FP32 [N, V] logits."""
     torch.cuda.synchronize()
     base = torch.cuda.memory_allocated(cuda)
     torch.cuda.reset_peak_memory_stats(cuda)
     out = lce.lce_forward_backward(hd, wd, bd, yd, chunk_rows=w.chunk_rows, reduction=w.reduction,
-                                   want_f32=False, **kw)
+                                   want_f32=False, want_lse=False, **kw)
     torch.cuda.synchronize()
     extra = torch.cuda.max_memory_allocated(cuda) - base - _out_bytes(out)
     logits32 = 4 * w.n_rows * w.vocab
