@@ -421,6 +421,7 @@ int lce_forward_backward_ex(const lce_problem* p, const void* hidden, const void
   tr.st = stream;
   if (trace) trace->count = 0;
   const bool any_grad = need_gh || need_gw || need_gb;
+  const bool gb_in_gw = need_gb && need_gw && lce::grad_weight_sums_bias(c.s.H);
   st = run_prepare(c, labels, n_valid, status, stream, tr, any_grad);
   if (st != LCE_OK) return st;
   // the gradients only need the rows with a label: valid rows first, and
@@ -491,8 +492,8 @@ int lce_forward_backward_ex(const lce_problem* p, const void* hidden, const void
       LCE_LAUNCH(tr, LCE_K_BWD_DLOGITS, rows_valid, s.V, 0,
                  lce::launch_rowscale(c.label32, c.zy2, c.lse_ws, rref, row_scale, c.n_valid, grad_scale, is_mean,
                                       g0, Gc, dlog, rowc, ovf, 1, need_gb ? gb : nullptr, c.perm, stream));
-      // grad_bias column sums: inside grad_weight's K loop when it runs
-      if (need_gb && !need_gw)
+      // grad_bias column sums: inside grad_weight's K loop when it runs and can
+      if (need_gb && !gb_in_gw)
         LCE_LAUNCH(tr, LCE_K_BIAS_SUMS, rows_valid, s.V, 0, lce::launch_bias_sums(s, dlog, rowc, Gc, gb, stream));
       if (need_gh)
         LCE_LAUNCH(tr, LCE_K_GRAD_HIDDEN, rows_valid, s.H, s.V,
@@ -505,7 +506,7 @@ int lce_forward_backward_ex(const lce_problem* p, const void* hidden, const void
                                            (g0 == 0 && !accumulate) ? 1 : 0,
                                            gw, last ? grad_weight : nullptr,
                                            (!last || grad_weight == nullptr || grad_weight_f32 != nullptr) ? 1 : 0,
-                                           rowc, need_gb ? gb : nullptr, c.bwd_limit, g0, stream));
+                                           rowc, gb_in_gw ? gb : nullptr, c.bwd_limit, g0, stream));
         if (last) gw_cast_done = true;
       }
     }

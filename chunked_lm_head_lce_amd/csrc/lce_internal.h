@@ -92,7 +92,7 @@ hipError_t launch_rowscale(const int32_t* label32, const float* zy2, const float
                            int64_t g0, int64_t G, void* dlog, float* rowc, const int* ovf, int retry,
                            float* gb_f32, const int32_t* perm, hipStream_t st);
 // gb_f32[v] += sum_i rowc[i] dlog[i][v] over the group's G rows (used when
-// grad_weight is not computed; otherwise its kernel adds these sums).
+// grad_weight is not computed or cannot add these sums itself).
 hipError_t launch_bias_sums(const Shapes& s, const void* dlog, const float* rowc, int64_t G, float* gb_f32,
                             hipStream_t st);
 // data[k] *= *scale (bf16 or f32 elements).
@@ -110,8 +110,9 @@ hipError_t launch_grad_hidden(const Shapes& s, const void* dlog, const void* wT,
 // of scratch for split tiles (no more pieces are made). first: store instead
 // of add. gw_bf16 (nullable): also write each final sum rounded to bf16 (the
 // last row group); keep32 = 0: do not write the FP32 sums back. gb_f32
-// (nullable): also add the group's grad_bias column sums, sum_i rowc[i]
-// dlog[i][v] (FP32 atomics; rowc [G], the group's row scales).
+// (nullable, only when grad_weight_sums_bias(H)): also add the group's
+// grad_bias column sums, sum_i rowc[i] dlog[i][v] (FP32 atomics; rowc [G],
+// the group's row scales).
 // row_limit (nullable): K stays below row *row_limit - g0 of the group.
 hipError_t launch_grad_weight(const Shapes& s, const void* dlog, int64_t G, const void* hT, int64_t rows_valid,
                               float* part, int64_t part_items, int first, float* gw_f32, void* gw_bf16, int keep32,
@@ -123,6 +124,9 @@ hipError_t launch_grad_weight(const Shapes& s, const void* dlog, int64_t G, cons
 constexpr int kMaxGwSplit = 8;
 constexpr int kMaxGwItems = 256;
 void grad_weight_split(int n_tiles, int nk, int cus, int max_items, int* n_full, int* split);
+// Whether launch_grad_weight can add the grad_bias column sums for hidden
+// size H (at least 16 hidden tiles of 256); otherwise launch_bias_sums does.
+bool grad_weight_sums_bias(int64_t H);
 int device_cus();
 hipError_t launch_cast(const float* in, void* out, int64_t n, hipStream_t st);
 

@@ -303,83 +303,60 @@ struct FragAT {
 
 // FragAT for grad_weight with grad_bias folded in: grad_bias[v] = sum_k
 // c_k G'[k][v] over the group's rows k is a column sum of the A operand
-// already in LDS. Stage s of vocabulary tile tm is summed by the tile of
-// that tm whose hidden-tile index tn = s mod n_nt (every stage once, spread
-// evenly over the tiles). In such a stage wave w takes K rows 8w .. 8w+7,
-// each lane the ids 4 lane .. +3, in two halves of four rows: reads in slot
-// 6, sums and the second half's reads in slot 8, its sums in slot 10 (slots
-// 6..9 have no fragment reads; the stage's buffer is read-only until the
-// barrier of slot 10). The row scales c_k of every stage come into LDS
-// (s_c, one 256-byte direct load by wave 0, issued with the stage's operand
-// loads and published by the same wait and barrier), so all waits stay in
-// LDS order. gb[] holds this lane's sums over the tile's stages.
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+// already in LDS. All n_nt tiles of vocabulary tile tm see every stage of
+// G'; the one with hidden-tile index tn sums rows r = tn + j n_nt (j = 0..3)
+// of each stage, which covers the 64 rows once over the n_nt tiles when
+// n_nt >= 16 (kGwBiasMinTiles; smaller heads take the separate column-sum
+// pass). Wave w takes row j = w/2 and ids 128 (w%2) + 2 lane, +1: in slot 6
+// of every stage one 4-byte read of G' and one of c_r, in slot 8 two FMAs
+// (slots 6..9 have no fragment reads, and the stage's buffer is read-only
+// until the barrier of slot 10). A wave whose row would be past 63 reads
+// row 0 and drops its sums. Each wave brings the 64 row scales of every
+// stage into two LDS slots of its own (one 256-byte direct load issued with
+// the stage's operand loads and covered by the same wait), so every wait
+// stays in LDS order and the K loop takes no extra branch. (Summing whole
+// stages in one tile out of n_nt instead, behind per-slot tests of the stage
+// index, measured 2-3% slower for grad_weight even with the sums removed.)
+constexpr int kGwBiasMinTiles = 16;
 __device__ __forceinline__ void lds_dma4(const void* gbase, uint32_t voff, uint32_t lds_addr) {
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, %2"
                :: "s"(lds_addr), "v"(voff), "s"(gbase) : "memory", "m0");
 }
 struct FragATBias : FragAT {
-  float gb[4];
+  float gb[2];
   const float* rowc;     // row scales of the tile's first K row (uniform)
-  uint32_t c_lds;        // LDS byte address of s_c[2][64]
-  int next;              // next stage (local index) whose bias sums this tile takes
-  int next_c;            // next such stage whose row scales are not yet requested
-  int n_nt;
-  int wave;
-  __device__ __forceinline__ FragATBias(int wave_, int lane, const float* rowc_, uint32_t c_lds_, int first,
-                                        int n_nt_)
-      : FragAT(wave_, lane), rowc(rowc_), c_lds(c_lds_), next(first), next_c(first), n_nt(n_nt_), wave(wave_) {
-    while (next_c < 2) next_c += n_nt;   // stages 0 and 1 are requested before the K loop
-#pragma unroll
-    for (int e = 0; e < 4; ++e) gb[e] = 0.f;
+  uint32_t c_lds;        // LDS byte address of this wave's two slots of 64 row scales
+  uint32_t c_row;        // byte offset of this wave's row in a slot
+  uint32_t g_off;        // byte offset of this lane's two G' values in a stage
+  uint32_t x;            // the stage's G' pair ...
+  float c;               // ... and row scale, read in slot 6
+  __device__ __forceinline__ FragATBias(int wave, int lane, const float* rowc_, uint32_t c_lds_, int row)
+      : FragAT(wave, lane), rowc(rowc_), c_lds(c_lds_) {
+    const int r = row < 64 ? row : 0;
+    c_row = (uint32_t)r * 4;
+    // the 16-byte chunk (lane/4) of half w%2 sits at slot chunk ^ 2 tr_swz(r)
+    const uint32_t chunk = (uint32_t)(((wave & 1) << 4) | (lane >> 2)) ^ (uint32_t)(2 * tr_swz(r));
+    g_off = (uint32_t)r * TR_ROW + (chunk << 4) + 4 * (uint32_t)(lane & 3);
+    gb[0] = gb[1] = 0.f;
   }
-  // the 64 row scales of stage s into s_c[s & 1] (wave 0)
+  // the 64 row scales of stage s into this wave's slot s & 1
   __device__ __forceinline__ void load_c(int s) const {
     lds_dma4(uniform_ptr(rowc + (int64_t)s * 64), lane_x16() >> 2, c_lds + (uint32_t)((s & 1) * 256));
   }
-  // byte address of row 8 wave + u of the stage, ids 4 lane .. +3: the
-  // 16-byte chunk lane/2 sits at slot (lane/2) ^ 2 tr_swz(row)
-  __device__ __forceinline__ uint32_t addr(int u) const {
-    const uint32_t x = (uint32_t)(2 * ((u & 3) | ((wave & 1) << 2))) << 4;
-    return (uint32_t)((wave * 8 + u) * TR_ROW) + ((lane_x16() >> 1) ^ x);
-  }
-  __device__ __forceinline__ void fma4(u32x2 x, float c) {
-    gb[0] = fmaf(c, __builtin_bit_cast(float, x.x << 16), gb[0]);
-    gb[1] = fmaf(c, __builtin_bit_cast(float, x.x & 0xFFFF0000u), gb[1]);
-    gb[2] = fmaf(c, __builtin_bit_cast(float, x.y << 16), gb[2]);
-    gb[3] = fmaf(c, __builtin_bit_cast(float, x.y & 0xFFFF0000u), gb[3]);
-  }
-  u32x2 rd[4];           // one half's reads in flight
-  f32x4 c4;              // and its four row scales
-  __device__ __forceinline__ void read_half(int s, int h, const LDS_AS char* cur) {
-    c4 = *(const LDS_AS f32x4*)((const LDS_AS char*)0 + c_lds + (uint32_t)((s & 1) * 256 + (wave * 8 + 4 * h) * 4));
-#pragma unroll
-    for (int u = 0; u < 4; ++u) rd[u] = *(const LDS_AS u32x2*)(cur + addr(4 * h + u));
-  }
-  __device__ __forceinline__ void sum_half() {
-#pragma unroll
-    for (int u = 0; u < 4; ++u) fma4(rd[u], c4[u]);
-  }
   __device__ __forceinline__ void side(int slot, int s, const LDS_AS char* cur) {
-    if (s == next) {   // wave-uniform
-      if (slot == 6) read_half(s, 0, cur);
-      if (slot == 8) {
-        sum_half();
-        read_half(s, 1, cur);
-      }
-      if (slot == 10) {
-        sum_half();
-        next += n_nt;
-      }
+    if (slot == 6) {
+      x = *(const LDS_AS uint32_t*)(cur + g_off);
+      c = *(const LDS_AS float*)((const LDS_AS char*)0 + c_lds + (uint32_t)((s & 1) * 256) + c_row);
+    }
+    if (slot == 8) {
+      gb[0] = fmaf(c, __builtin_bit_cast(float, x << 16), gb[0]);
+      gb[1] = fmaf(c, __builtin_bit_cast(float, x & 0xFFFF0000u), gb[1]);
     }
   }
-  // row scales of stage s + 2 when it is one of this tile's bias stages,
-  // issued with that stage's operand loads (stages 0 and 1: before the K loop)
-  __device__ __forceinline__ void side_load(int slot, int s, int nk) {
-    if (slot == 10 && s + 2 == next_c) {   // wave-uniform
-      if (wave == 0 && s + 2 < nk) load_c(s + 2);
-      next_c += n_nt;
-    }
+  // row scales of stage s + 2, issued with its operand loads (stages 0 and
+  // 1: before the K loop)
+  __device__ __forceinline__ void side_load(int slot, int s, int nk) const {
+    if (slot == 10 && s + 2 < nk) load_c(s + 2);
   }
 };
 
@@ -1294,7 +1271,7 @@ k_gemm_grad_weight(const u16* __restrict__ G, int64_t slab_rows, const u16* __re
                    float* __restrict__ part, u16* __restrict__ gw_bf16, int keep32, const float* __restrict__ rowc,
                    float* __restrict__ gb_f32, const unsigned long long* __restrict__ row_limit, int64_t g0) {
   __shared__ __attribute__((aligned(16))) char smem_raw[MAINLOOP_LDS];
-  __shared__ __attribute__((aligned(16))) float s_c[BIAS ? 2 * 64 : 4];   // row scales of two stages
+  __shared__ __attribute__((aligned(16))) float s_c[BIAS ? NTHREADS / 64 * 2 * 64 : 4];   // per wave, two stages
   LDS_AS char* smem = (LDS_AS char*)smem_raw;
   int tm, tn, s0 = 0, s1 = nk, item = -1;
   if ((int)blockIdx.x < n_full) {
@@ -1339,26 +1316,26 @@ k_gemm_grad_weight(const u16* __restrict__ G, int64_t slab_rows, const u16* __re
 #pragma unroll
       for (int j = 0; j < NBJ; ++j) acc.v[i][j] = (f32x4){0.f, 0.f, 0.f, 0.f};
   } else if (BIAS) {
-    // local stages s (global s0 + s) with (s0 + s) mod n_nt == tn carry the bias sums
-    const int first_local = ((tn - s0) % n_nt + n_nt) % n_nt;
+    const int row = tn + (wave >> 1) * n_nt;   // this wave's row of every stage
     FragATBias fs(wave, lane, rowc + (int64_t)s0 * 64,
-                  (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(LDS_AS char*)s_c), first_local,
-                  n_nt);
-    // the row scales of the bias stages among the first two go out before
-    // the operand loads, so tile_run's first wait covers them
-    if (wave == 0)
-      for (int sb = first_local; sb < 2 && sb < s1 - s0; sb += n_nt) fs.load_c(sb);
+                  (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(LDS_AS char*)s_c) +
+                      (uint32_t)wave * 2 * 256,
+                  row);
+    // the row scales of stages 0 and 1 go out before the operand loads, so
+    // tile_run's first wait covers them
+    for (int sb = 0; sb < 2 && sb < s1 - s0; ++sb) fs.load_c(sb);
     tile_prologue(t, s1 - s0);
     tile_run(acc, t, s1 - s0, smem, fs);
-    if (first_local < s1 - s0) {   // this tile summed at least one stage: add its 256 column sums
-      __syncthreads();             // every wave is past its last read of the stage buffers
+    if (tn < 64) {      // some wave summed a row: add the tile's 256 column sums
+      __syncthreads();  // every wave is past its last read of the stage buffers
       LDS_AS float* red = (LDS_AS float*)smem;
-      *(LDS_AS f32x4*)(red + wave * TILE + lane * 4) = (f32x4){fs.gb[0], fs.gb[1], fs.gb[2], fs.gb[3]};
+      red[wave * 128 + 2 * lane] = row < 64 ? fs.gb[0] : 0.f;
+      red[wave * 128 + 2 * lane + 1] = row < 64 ? fs.gb[1] : 0.f;
       __syncthreads();
-      if (tid < TILE) {
+      if (tid < TILE) {   // id tid: waves 2 j + tid / 128, j = 0..3
         float sum = 0.f;
 #pragma unroll
-        for (int w = 0; w < NTHREADS / 64; ++w) sum += red[w * TILE + tid];
+        for (int j = 0; j < NTHREADS / 128; ++j) sum += red[(2 * j + (tid >> 7)) * 128 + (tid & 127)];
         if (row0 + tid < V) atomicAdd(gb_f32 + row0 + tid, sum);
       }
     }
@@ -1614,6 +1591,8 @@ hipError_t launch_grad_weight(const Shapes& s, const void* dlog, int64_t G, cons
                      n_mt, n_nt, s.H, s.V, first, gw_f32, (u16*)gw_bf16, keep32);
   return hipGetLastError();
 }
+
+bool grad_weight_sums_bias(int64_t H) { return (H + TILE - 1) / TILE >= kGwBiasMinTiles; }
 
 void grad_weight_split(int n_tiles, int nk, int cus, int max_items, int* n_full, int* split) {
   const int rem = n_tiles % cus;

@@ -147,10 +147,10 @@ int lce_forward_backward(const lce_problem* p, const void* hidden, const void* w
  * numerators against r_i = lse_i when a row's maximum lies more than 60
  * above its label logit (otherwise it returns at once); LCE_K_BIAS_SUMS
  * adds the group's grad_bias column sums (only when grad_weight is not
- * computed: otherwise its kernel adds them); LCE_K_PARTITION orders the rows
- * with a label before the others (two launches, recorded as one) and
- * LCE_K_GATHER_ROWS copies the hidden rows into that order: the backward
- * then works on the rows with a label only. */
+ * computed or H <= 3840: otherwise grad_weight's kernel adds them);
+ * LCE_K_PARTITION orders the rows with a label before the others (two
+ * launches, recorded as one) and LCE_K_GATHER_ROWS copies the hidden rows
+ * into that order: the backward then works on the rows with a label only. */
 typedef enum {
   LCE_K_ZERO = 0, LCE_K_PREPARE_LABELS = 1, LCE_K_FWD_LSE = 2, LCE_K_FINALIZE_ROWS = 3,
   LCE_K_FINALIZE_LOSS = 4, LCE_K_TRANSPOSE = 5, LCE_K_BWD_DLOGITS = 6, LCE_K_GRAD_HIDDEN = 7,

@@ -378,6 +378,21 @@ def test_repeatable(cuda):
     assert torch.equal(fa.loss, fb.loss) and torch.equal(fa.lse, a.lse)
 
 
+# grad_bias summed inside grad_weight's K loop (at least 16 hidden tiles):
+# 16 tiles, every wave on a row; 17 tiles, the waves of row 3 idle in most
+# tiles; 65 tiles, the last tile has no row. Several row groups, a partial
+# last stage and (fewer tiles than CUs) tiles split along K.
+@pytest.mark.parametrize("shape", [(700, 4096, 1000), (300, 4160, 600), (257, 16448, 300)])
+def test_grad_bias_inside_grad_weight(cuda, shape):
+    n, h, v = shape
+    say(f"[gpu] grad_bias inside grad_weight shape={shape}")
+    inp = make_case(n, h, v, seed=h + v, bias_std=0.05, ignore_frac=0.1, weight_std=0.02)
+    hd, wd, bd, yd = to_device(inp, cuda)
+    out = lce.lce_forward_backward(hd, wd, bd, yd, reduction="sum", rows_in_flight=256)
+    torch.cuda.synchronize()
+    check_all(out, oracle_of(inp, "sum"), inp, "sum")
+
+
 def test_grad_weight_whole_and_split_tiles(cuda):
     """274 grad_weight tiles (V = 70000 over 256-row tiles, one column tile):
     on a GPU with fewer CUs the tiles past the last whole round are split

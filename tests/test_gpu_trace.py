@@ -67,12 +67,12 @@ def test_traced_forward_backward_matches_untraced(cuda):
         groups = 3
         # per row group: the forward tiles, their retry (a no-op here), the
         # row scales (and their retry), both row-reference steps and the two
-        # gradient products; grad_bias is summed inside grad_weight's kernel
+        # gradient products; at H = 256 (one hidden tile) grad_bias takes its
+        # own column-sum pass
         for k, per_group in (("fwd_lse", 1), ("fwd_retry", 1), ("bwd_dlogits", 2), ("row_ref", 2),
-                             ("grad_hidden", 1), ("grad_weight", 1), ("finalize_rows", 1)):
+                             ("grad_hidden", 1), ("grad_weight", 1), ("finalize_rows", 1), ("bias_sums", 1)):
             assert names.count(k) == per_group * groups, (k, names)
         assert names.count("label_logit") == 1 and names.count("finalize_loss") == 1
-        assert names.count("bias_sums") == 0
         assert names.count("partition") == 1 and names.count("gather_rows") == 1   # valid rows first
         # product dims: grad_hidden rows x H x V, grad_weight V x H x the group's valid rows
         valid_rows = [g, g, n - 2 * g]
@@ -87,6 +87,29 @@ def test_traced_forward_backward_matches_untraced(cuda):
             assert ev.ms(2 * i, 2 * i + 1) >= 0.0
             if i:
                 assert ev.ms(2 * (i - 1) + 1, 2 * i) >= 0.0
+    finally:
+        ev.close()
+
+
+def test_grad_bias_inside_grad_weight_trace(cuda):
+    """At H = 4096 (16 hidden tiles) grad_weight's kernel adds the grad_bias
+    column sums itself: no separate pass, same results as untraced."""
+    n, h, v, g = 600, 4096, 700, 256          # three row groups
+    inp = make_case(n, h, v, seed=33, bias_std=0.05, ignore_frac=0.1, weight_std=0.02)
+    hd, wd, bd, yd = to_device(inp, cuda)
+    cap = 64
+    ev = _Events(2 * cap)
+    try:
+        t, kinds, _ = _trace(ev, cap)
+        say("[gpu] traced forward+backward at H=4096, 3 row groups")
+        a = lce.lce_forward_backward(hd, wd, bd, yd, rows_in_flight=g, trace=t)
+        b = lce.lce_forward_backward(hd, wd, bd, yd, rows_in_flight=g)
+        torch.cuda.synchronize()
+        names = [_lib.KERNEL_KINDS[kinds[i]] for i in range(t.count)]
+        assert names.count("grad_weight") == 3 and names.count("bias_sums") == 0, names
+        assert torch.equal(a.grad_weight, b.grad_weight) and torch.equal(a.grad_hidden, b.grad_hidden)
+        # FP32 atomics: equal up to their order
+        torch.testing.assert_close(a.grad_bias_f32, b.grad_bias_f32, rtol=1e-5, atol=1e-6)
     finally:
         ev.close()
 
