@@ -379,10 +379,11 @@ def test_repeatable(cuda):
 
 
 # grad_bias summed inside grad_weight's K loop (at least 16 hidden tiles):
-# 16 tiles, every wave on a row; 17 tiles, the waves of row 3 idle in most
-# tiles; 65 tiles, the last tile has no row. Several row groups, a partial
-# last stage and (fewer tiles than CUs) tiles split along K.
-@pytest.mark.parametrize("shape", [(700, 4096, 1000), (300, 4160, 600), (257, 16448, 300)])
+# 16 tiles, every wave on a row; 16 tiles of which the last holds 64 hidden
+# columns (H = 3904, the smallest such H); 17 tiles, the waves of row 3 idle
+# in most tiles; 65 tiles, the last tile has no row. Several row groups, a
+# partial last stage and (fewer tiles than CUs) tiles split along K.
+@pytest.mark.parametrize("shape", [(700, 4096, 1000), (300, 3904, 700), (300, 4160, 600), (257, 16448, 300)])
 def test_grad_bias_inside_grad_weight(cuda, shape):
     n, h, v = shape
     say(f"[gpu] grad_bias inside grad_weight shape={shape}")
