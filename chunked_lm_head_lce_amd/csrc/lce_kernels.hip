@@ -84,6 +84,38 @@ __device__ __forceinline__ float sum16(float v) {
   return v + dpp<DPP_MIRROR>(v);
 }
 
+// Max / sum over the 16 lanes of each row group for four rows at once, by
+// the same butterfly (xor 1, xor 2, half mirror, mirror): every lane ends
+// with its row's result. One block of fused DPP instructions: the compiler
+// lowers fmaxf over a DPP move to a zeroing move, the move, a canonicalising
+// max and the max. The leading s_nop 4 covers the DPP hazards (a VALU write
+// of the source needs 2 wait states before a DPP read of it, an EXEC write
+// 5); inside the block each source was written four instructions earlier.
+#define LCE_DPP_STEP4(OP, CTRL)                                      \
+  OP " %0, %0, %0 " CTRL " row_mask:0xf bank_mask:0xf\n\t"          \
+  OP " %1, %1, %1 " CTRL " row_mask:0xf bank_mask:0xf\n\t"          \
+  OP " %2, %2, %2 " CTRL " row_mask:0xf bank_mask:0xf\n\t"          \
+  OP " %3, %3, %3 " CTRL " row_mask:0xf bank_mask:0xf\n\t"
+#define LCE_DPP_BUTTERFLY4(OP)                                       \
+  "s_nop 4\n\t"                                                     \
+  LCE_DPP_STEP4(OP, "quad_perm:[1,0,3,2]")                           \
+  LCE_DPP_STEP4(OP, "quad_perm:[2,3,0,1]")                           \
+  LCE_DPP_STEP4(OP, "row_half_mirror")                               \
+  LCE_DPP_STEP4(OP, "row_mirror")
+__device__ __forceinline__ void max16x4(float (&v)[4]) {
+  asm volatile(LCE_DPP_BUTTERFLY4("v_max_f32_dpp") : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]));
+}
+__device__ __forceinline__ void sum16x4(float (&v)[4]) {
+  asm volatile(LCE_DPP_BUTTERFLY4("v_add_f32_dpp") : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]));
+}
+// Two floats to bf16 (round to nearest even) in one v_cvt_pk_bf16_f32: a in
+// the low half, b in the high half.
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t f2bf2(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){a, b}, bf16x2));
+}
+
 // ---------------------------------------------------------------------------
 // Tile order. Workgroups are dispatched round-robin over the 8 XCDs, so
 // dispatch id b runs on XCD b % 8. Remap so each XCD walks a contiguous range
@@ -737,6 +769,7 @@ k_fwd_tile(const u16* __restrict__ hidden, int64_t ldh, const u16* __restrict__ 
     // the same value that enters the row's maximum and sum below.
     const LDS_AS int* labs = (const LDS_AS int*)s_lab + par * TILE + wm * 128;
     const int cw = (int)col0 + wn * 64;
+    bool overflow = false;   // some row of this lane needs the retry
     uint64_t hit_lo, hit_hi;
     {
       const LDS_AS int* lp = (const LDS_AS int*)((const LDS_AS char*)labs + (lane_x16() >> 2));
@@ -775,47 +808,44 @@ k_fwd_tile(const u16* __restrict__ hidden, int64_t ldh, const u16* __restrict__ 
 #pragma unroll
         for (int j = 0; j < NBJ; ++j) m[r] = fmaxf(m[r], acc.v[i][j][r]);
       }
-#pragma unroll
-      for (int r = 0; r < 4; ++r) m[r] = fmaxf(m[r], dpp<DPP_XOR1>(m[r]));
-#pragma unroll
-      for (int r = 0; r < 4; ++r) m[r] = fmaxf(m[r], dpp<DPP_XOR2>(m[r]));
-#pragma unroll
-      for (int r = 0; r < 4; ++r) m[r] = fmaxf(m[r], dpp<DPP_HALF_MIRROR>(m[r]));
-#pragma unroll
-      for (int r = 0; r < 4; ++r) m[r] = fmaxf(m[r], dpp<DPP_MIRROR>(m[r]));
-      float sm[4];
+      max16x4(m);
+      // Stored p~ = exp(z - ref): ref is the row's reference (its label
+      // logit) when it has one, else the quarter maximum. fr = exp(m - ref),
+      // capped at e^60; a valid row whose maximum lies more than 60 above its
+      // reference raises the overflow flag (the group is redone).
+      float ms[4], fr[4], sm[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const float ms = m[r] == -INFINITY ? 0.f : m[r];   // all columns past V: every e = 0
-        // Stored p~ = exp(z - ref): ref is the row's reference (its label
-        // logit) when it has one, else the quarter maximum. fr = exp(m - ref),
-        // capped at e^60; a valid row whose maximum lies more than 60 above
-        // its reference raises the overflow flag (the group is redone).
-        float fr = 1.f;
-        if (use_ref) {
-          const float rr = ((const LDS_AS float*)s_ref)[par * TILE + wm * 128 + i * 16 + 4 * (lane >> 4) + r];
-          if (!__builtin_isnan(rr)) {
-            const float d = ms - rr * LOG2E;
-            if (m[r] != -INFINITY && d > REF_CAP2 && ovf != nullptr) *ovf = 1;   // rare: the group is redone
-            fr = __builtin_amdgcn_exp2f(fminf(d, REF_CAP2));
-          }
-        }
+        ms[r] = m[r] == -INFINITY ? 0.f : m[r];   // all columns past V: every e = 0
+        fr[r] = 1.f;
         sm[r] = 0.f;
+      }
+      if (use_ref) {
 #pragma unroll
-        for (int j = 0; j < NBJ; ++j) {
-          const float e = __builtin_amdgcn_exp2f(acc.v[i][j][r] - ms);
-          sm[r] += e;
-          if (STORE_P) pst[(4 * (lane >> 4) + r) * PST_LD + j * 16 + (lane & 15)] = f2bf(e * fr);
+        for (int r = 0; r < 4; ++r) {
+          const float rr = ((const LDS_AS float*)s_ref)[par * TILE + wm * 128 + i * 16 + 4 * (lane >> 4) + r];
+          const float d = ms[r] - rr * LOG2E;      // NaN when the row has no reference
+          overflow |= m[r] != -INFINITY && d > REF_CAP2;
+          fr[r] = __builtin_isnan(rr) ? 1.f : __builtin_amdgcn_exp2f(fminf(d, REF_CAP2));
         }
       }
 #pragma unroll
-      for (int r = 0; r < 4; ++r) sm[r] += dpp<DPP_XOR1>(sm[r]);
+      for (int j = 0; j < NBJ; ++j) {
+        float e[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) sm[r] += dpp<DPP_XOR2>(sm[r]);
+        for (int r = 0; r < 4; ++r) {
+          e[r] = __builtin_amdgcn_exp2f(acc.v[i][j][r] - ms[r]);
+          sm[r] += e[r];
+        }
+        if (STORE_P)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) sm[r] += dpp<DPP_HALF_MIRROR>(sm[r]);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) sm[r] += dpp<DPP_MIRROR>(sm[r]);
+          for (int r = 0; r < 4; r += 2) {
+            const uint32_t pk = f2bf2(e[r] * fr[r], e[r + 1] * fr[r + 1]);
+            pst[(4 * (lane >> 4) + r) * PST_LD + j * 16 + (lane & 15)] = (u16)pk;
+            pst[(4 * (lane >> 4) + r + 1) * PST_LD + j * 16 + (lane & 15)] = (u16)(pk >> 16);
+          }
+      }
+      sum16x4(sm);
       if ((lane & 15) == 0) {   // rows 4*(lane/16) .. +3 of the block, in base-2 units
         *(f32x4*)(pm + i * 16) = (f32x4){m[0], m[1], m[2], m[3]};
         *(f32x4*)(ps + i * 16) = (f32x4){sm[0], sm[1], sm[2], sm[3]};
@@ -833,6 +863,7 @@ k_fwd_tile(const u16* __restrict__ hidden, int64_t ldh, const u16* __restrict__ 
         asm volatile("" ::: "memory");
       }
     }
+    if (overflow && ovf != nullptr) *ovf = 1;   // rare: the group is redone
     // First use of `claimed`, so the compiler's wait for the atomic lands
     // here. (The library is built with the atomic optimizer off: its
     // wave-wide rewrite of a uniform-address atomic reads the result at once.)
