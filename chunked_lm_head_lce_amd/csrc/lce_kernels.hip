@@ -277,6 +277,7 @@ struct Frags {
 // blocks first (every MFMA of the first row block needs all of them), then A.
 // FragK: both operands K-contiguous in LDS (the layout above).
 struct FragK {
+  static constexpr int kBar = 9;
   static constexpr bool kPrio = true;        // raise the wave's priority around its MFMAs
   static constexpr bool kPrioLoads = true;   // ... and while it issues its direct loads (see mainloop_stage)
   int rA, rB, q;
@@ -315,6 +316,7 @@ __device__ __forceinline__ bf16x8 frag_tr(const LDS_AS char* p) {
 // B K-contiguous (as FragK). (Raising the wave priority as FragK does
 // measured no faster here.)
 struct FragAT {
+  static constexpr int kBar = 10;
   static constexpr bool kPrio = false;
   static constexpr bool kPrioLoads = false;
   uint32_t a[NB];
@@ -342,7 +344,7 @@ struct FragAT {
 // pass). Wave w takes row j = w/2 and ids 128 (w%2) + 2 lane, +1: in slot 6
 // of every stage one 4-byte read of G' and one of c_r, in slot 8 two FMAs
 // (slots 6..9 have no fragment reads, and the stage's buffer is read-only
-// until the barrier of slot 10). A wave whose row would be past 63 reads
+// until the barrier of slot 10, FragAT's kBar). A wave whose row would be past 63 reads
 // row 0 and drops its sums. Each wave brings the 64 row scales of every
 // stage into two LDS slots of its own (one 256-byte direct load issued with
 // the stage's operand loads and covered by the same wait), so every wait
@@ -388,40 +390,46 @@ struct FragATBias : FragAT {
   // row scales of stage s + 2, issued with its operand loads (stages 0 and
   // 1: before the K loop)
   __device__ __forceinline__ void side_load(int slot, int s, int nk) const {
-    if (slot == 10 && s + 2 < nk) load_c(s + 2);
+    if (slot == kBar && s + 2 < nk) load_c(s + 2);
   }
 };
 
 // Schedule of one 64-deep stage s, in 16 slots of 4 MFMAs (slots 0..7:
 // sub-step 0 from fragment set f0, slots 8..15: sub-step 1 from f1), two
-// waves per SIMD:
+// waves per SIMD, with the barrier in slot B = FS::kBar (9 for FragK, 10
+// for FragAT):
 //   slots 0..5    read f1 (stage s, sub-step 1), two fragments per slot
-//   slot 10       wait for this wave's loads of stage s+1 and its LDS reads,
+//   slot B        wait for this wave's loads of stage s+1 and its LDS reads,
 //                 barrier: stage s+1 is visible from every wave, and buffer
 //                 s&1 is no longer read (f0 and f1 of stage s are in registers)
-//   slots 10..15  read f0 of stage s+1, two per slot
-//   slots 10..15, and 0..1 of stage s+1: the 8 global->LDS loads of stage s+2
-//                 into buffer s&1, one per slot (after the second MFMA)
+//   slots B..15   read f0 of stage s+1 (12 fragments spread over 16 - B slots)
+//   slots B..15, and 0..B-9 of stage s+1: the 8 global->LDS loads of stage
+//                 s+2 into buffer s&1, one per slot (after the second MFMA)
 // so every load has at least eight slots to land before the barrier that
 // publishes it. (Measured: two waves per SIMD with this schedule beat one
 // wave per SIMD with 128 x 128 per wave by 1.5-5%; issuing the loads two per
-// slot was slower here.) With FragK the wave raises its priority for its
-// MFMA pairs and while it issues its direct loads, so that when both waves
-// of a SIMD are ready those go before fragment reads: measured 1.3-1.6%
-// faster for the MFMA pairs alone, then another 0.5% (grad_hidden) to 3.8%
-// (the forward tiles) with the loads.
-// At entry: f0 holds stage s sub-step 0; loads 0..5 of stage s+1 went out in
-// the previous stage (slots 10..15), loads 6..7 go out in slots 0..1.
+// slot was slower here. The barrier in slot 9 instead of 10 made the
+// forward tiles 1% faster and grad_hidden no slower, slot 11 or 8 slower;
+// grad_weight is best with 10.) With FragK the wave raises its priority for
+// its MFMA pairs and while it issues its direct loads, so that when both
+// waves of a SIMD are ready those go before fragment reads: measured
+// 1.3-1.6% faster for the MFMA pairs alone, then another 0.5% (grad_hidden)
+// to 3.8% (the forward tiles) with the loads.
+// At entry: f0 holds stage s sub-step 0; loads 0..15-B of stage s+1 went out
+// in the previous stage (slots B..15), the rest go out in slots 0..B-9.
 template <class FS>
 __device__ __forceinline__ void mainloop_stage(Acc& acc, Frags& f0, Frags& f1, int s, int nk, LDS_AS char* smem,
                                                const TileLoads& t, FS& fs) {
+  // f1's reads (slots 0..5) and FragATBias's (slot 6) precede the barrier;
+  // the loads of stage s+1 left for this stage fit in slots 0..kBar-9
+  static_assert(FS::kBar >= 8 && FS::kBar <= 15, "barrier slot out of range");
   LDS_AS char* cur = smem + (s & 1) * STAGE;
   LDS_AS char* nxt = smem + ((s + 1) & 1) * STAGE;
 #pragma unroll
   for (int slot = 0; slot < 16; ++slot) {
     const int i = slot & 7;
     Frags& f = slot < 8 ? f0 : f1;
-    if (slot == 10) {
+    if (slot == FS::kBar) {
       if (s + 1 < nk) __builtin_amdgcn_s_waitcnt(WAIT_VM0);
       __builtin_amdgcn_s_waitcnt(WAIT_LGKM0);
       bare_barrier();
@@ -433,16 +441,21 @@ __device__ __forceinline__ void mainloop_stage(Acc& acc, Frags& f0, Frags& f1, i
     if (FS::kPrio) __builtin_amdgcn_s_setprio(0);
     FENCE();
     if (FS::kPrioLoads) __builtin_amdgcn_s_setprio(1);
-    if (slot < 2) {
-      if (s + 1 < nk) stage_load(t, s + 1, 6 + slot);
-    } else if (slot >= 10) {
-      if (s + 2 < nk) stage_load(t, s + 2, slot - 10);
+    if (slot < FS::kBar - 8) {
+      if (s + 1 < nk) stage_load(t, s + 1, (16 - FS::kBar) + slot);
+    } else if (slot >= FS::kBar) {
+      if (s + 2 < nk) stage_load(t, s + 2, slot - FS::kBar);
     }
     fs.side_load(slot, s, nk);
     if (FS::kPrioLoads) __builtin_amdgcn_s_setprio(0);
     // fragment reads: f1 of this stage in slots 0..5, f0 of the next in 10..15
+    constexpr int NS = 16 - FS::kBar;   // slots for the 12 reads of the next f0
+    const int rlo = slot >= FS::kBar ? (slot - FS::kBar) * 12 / NS : 0;
+    const int rhi = slot >= FS::kBar ? (slot - FS::kBar + 1) * 12 / NS : 0;
+    const int rmid = rlo + (rhi - rlo + 1) / 2;
     if (slot < 6) fs.read(f1, cur, 1, 2 * slot);
-    else if (slot >= 10) fs.read(f0, nxt, 0, 2 * (slot - 10));
+    else if (slot >= FS::kBar)
+      for (int n = rlo; n < rmid; ++n) fs.read(f0, nxt, 0, n);
     fs.side(slot, s, cur);
     FENCE();
     if (FS::kPrio) __builtin_amdgcn_s_setprio(1);
@@ -451,7 +464,8 @@ __device__ __forceinline__ void mainloop_stage(Acc& acc, Frags& f0, Frags& f1, i
     if (FS::kPrio) __builtin_amdgcn_s_setprio(0);
     FENCE();
     if (slot < 6) fs.read(f1, cur, 1, 2 * slot + 1);
-    else if (slot >= 10) fs.read(f0, nxt, 0, 2 * (slot - 10) + 1);
+    else if (slot >= FS::kBar)
+      for (int n = rmid; n < rhi; ++n) fs.read(f0, nxt, 0, n);
   }
   FENCE();
 }
@@ -466,10 +480,11 @@ __device__ __forceinline__ void mainloop_stage(Acc& acc, Frags& f0, Frags& f1, i
 //
 // In three steps, so that a persistent kernel can issue the next tile's first
 // loads before it runs the current tile's epilogue: tile_setup (addresses
-// only), tile_prologue (stage 0 and the first six loads of stage 1; the rest
-// go out in slots 0..1 of stage 0) and tile_run (the K loop). Between
+// only), tile_prologue (stage 0 and the first 16 - kBar loads of stage 1;
+// the rest go out in the first slots of stage 0) and tile_run (the K loop),
+// both for the fragment set FS the K loop uses. Between
 // tile_prologue and tile_run the caller may issue any other memory accesses
-// except to the stage buffers: tile_run's first wait (vmcnt <= 6) is then
+// except to the stage buffers: tile_run's first wait (vmcnt <= 16 - kBar) is then
 // only stricter, since direct loads complete in issue order.
 __device__ __forceinline__ TileLoads tile_setup(const u16* __restrict__ X, int64_t ldx, int64_t kx, int64_t x_row0,
                                                 int64_t x_rows, const u16* __restrict__ Y, int64_t ldy, int64_t ky,
@@ -486,12 +501,13 @@ __device__ __forceinline__ TileLoads tile_setup(const u16* __restrict__ X, int64
   t.lds_wave = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)smem + (uint32_t)wave * 32 * 128);
   return t;
 }
+template <class FS>
 __device__ __forceinline__ void tile_prologue(const TileLoads& t, int nk) {
 #pragma unroll
   for (int f = 0; f < 2 * FILLS; ++f) stage_load(t, 0, f);
   if (nk > 1)
 #pragma unroll
-    for (int f = 0; f < 6; ++f) stage_load(t, 1, f);
+    for (int f = 0; f < 16 - FS::kBar; ++f) stage_load(t, 1, f);
 }
 template <class FS>
 __device__ __forceinline__ void tile_run(Acc& acc, const TileLoads& t, int nk, LDS_AS char* smem, FS& fs) {
@@ -501,7 +517,7 @@ __device__ __forceinline__ void tile_run(Acc& acc, const TileLoads& t, int nk, L
     for (int j = 0; j < NBJ; ++j)
 #pragma unroll
       for (int r = 0; r < 4; ++r) acc.v[i][j][r] = 0.f;
-  if (nk > 1) __builtin_amdgcn_s_waitcnt(WAIT_VM(6));
+  if (nk > 1) __builtin_amdgcn_s_waitcnt(WAIT_VM(16 - FS::kBar));
   else __builtin_amdgcn_s_waitcnt(WAIT_VM0);
   __syncthreads();
   Frags f0, f1;
@@ -521,7 +537,7 @@ __device__ __forceinline__ void gemm_tile(Acc& acc, const u16* __restrict__ X, i
                                           LDS_AS char* smem) {
   const int nk = (int)(K / BK);
   const TileLoads t = tile_setup(X, ldx, kx, x_row0, x_rows, Y, ldy, ky, y_row0, y_rows, smem);
-  tile_prologue(t, nk);
+  tile_prologue<FragK>(t, nk);
   tile_run(acc, t, nk, smem);
 }
 
@@ -711,7 +727,7 @@ k_fwd_tile(const u16* __restrict__ hidden, int64_t ldh, const u16* __restrict__ 
   if (wave == 1) lds_dma16(uniform_ptr(label32 + g0 + (int64_t)tm * TILE), lane_x16(), lab_lds);
   TileLoads t = tile_setup(hidden, ldh, BK * 2, g0 + (int64_t)tm * TILE, N, weight, ldw, BK * 2,
                            (int64_t)tn * TILE, V, smem);
-  tile_prologue(t, nk);
+  tile_prologue<FragK>(t, nk);
   for (;;) {
     const int64_t lrow0 = (int64_t)tm * TILE;       // row inside the group (or global row)
     const int64_t col0 = (int64_t)tn * TILE;
@@ -752,7 +768,7 @@ k_fwd_tile(const u16* __restrict__ hidden, int64_t ldh, const u16* __restrict__ 
         lds_dma16(uniform_ptr(label32 + g0 + (int64_t)tm * TILE), lane_x16(), lab_lds + (uint32_t)((par ^ 1) * TILE * 4));
       t = tile_setup(hidden, ldh, BK * 2, g0 + (int64_t)tm * TILE, N, weight, ldw, BK * 2, (int64_t)tn * TILE, V,
                      smem);
-      tile_prologue(t, nk);
+      tile_prologue<FragK>(t, nk);
     }
     // claim the tile after next now; the result is needed only after the
     // next K loop, and waiting for it at the end of the epilogue costs
@@ -1355,7 +1371,7 @@ k_gemm_grad_weight(const u16* __restrict__ G, int64_t slab_rows, const u16* __re
     // the row scales of stages 0 and 1 go out before the operand loads, so
     // tile_run's first wait covers them
     for (int sb = 0; sb < 2 && sb < s1 - s0; ++sb) fs.load_c(sb);
-    tile_prologue(t, s1 - s0);
+    tile_prologue<FragATBias>(t, s1 - s0);
     tile_run(acc, t, s1 - s0, smem, fs);
     if (tn < 64) {      // some wave summed a row: add the tile's 256 column sums
       __syncthreads();  // every wave is past its last read of the stage buffers
@@ -1372,7 +1388,7 @@ k_gemm_grad_weight(const u16* __restrict__ G, int64_t slab_rows, const u16* __re
     }
   } else {
     FragAT fs(wave, lane);
-    tile_prologue(t, s1 - s0);
+    tile_prologue<FragAT>(t, s1 - s0);
     tile_run(acc, t, s1 - s0, smem, fs);
   }
   if (item >= 0) {   // partial tile of a split item: plain stores, summed by k_gw_reduce
