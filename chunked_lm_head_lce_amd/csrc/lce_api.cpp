@@ -497,7 +497,8 @@ int lce_forward_backward_ex(const lce_problem* p, const void* hidden, const void
         LCE_LAUNCH(tr, LCE_K_BIAS_SUMS, rows_valid, s.V, 0, lce::launch_bias_sums(s, dlog, rowc, Gc, gb, stream));
       if (need_gh)
         LCE_LAUNCH(tr, LCE_K_GRAD_HIDDEN, rows_valid, s.H, s.V,
-                   lce::launch_grad_hidden(s, dlog, wT, g0, Gc, rowc, grad_hidden, c.bwd_limit, c.perm, stream));
+                   lce::launch_grad_hidden(s, dlog, wT, g0, Gc, rowc, grad_hidden, c.bwd_limit, c.perm, gw_part,
+                                           gw_part_items(s, G), stream));
       if (need_gw) {
         LCE_LAUNCH(tr, LCE_K_TRANSPOSE, 0, 0, 0,
                    lce::launch_transpose(hid, s.ldh, g0, rows_valid, s.H, hT, Gc, rowc, stream));

@@ -101,9 +101,12 @@ hipError_t launch_scale(void* data, bool f32, int64_t n, const float* scale, hip
 // (dlog: K-slabs [Vp/64][G][64], wT: [Vp/64][H][64]).
 // Row tiles at or past *row_limit (nullable) only write zero rows. perm
 // (nullable): row i goes to the caller's row perm[i].
+// part: part_items * 256 * 256 floats of scratch; when the group's real tiles
+// do not fill whole rounds of the GPU, the tiles left over are split along K
+// into pieces written there and summed by a second kernel (k_gh_reduce).
 hipError_t launch_grad_hidden(const Shapes& s, const void* dlog, const void* wT, int64_t g0, int64_t G,
                               const float* rowc, void* grad_hidden, const unsigned long long* row_limit,
-                              const int32_t* perm, hipStream_t st);
+                              const int32_t* perm, float* part, int64_t part_items, hipStream_t st);
 // gw (+)= sum over the group's rows i < rows_valid of G[i][v] h[g0 + i][:]
 // (dlog: K-slabs [Vp/64][G][64] holding G; hT: the group's rows of h as
 // K-slabs [G/64][H][64], zero past N). part: part_items * 256 * 256 floats

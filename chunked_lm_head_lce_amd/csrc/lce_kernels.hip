@@ -39,6 +39,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint16_t u16;
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int TILE = 256;                 // output tile edge (rows and columns)
 constexpr int BK = 64;                    // K depth of one LDS stage (two MFMA steps)
@@ -1192,22 +1193,72 @@ __global__ void __launch_bounds__(256) k_bias_sums(const u16* __restrict__ dlog,
   }
 }
 
+// How grad_hidden's tiles of one group are shared out, the same in every
+// workgroup and in k_gh_reduce: the row tiles below the device-side row limit
+// are real. When the real tiles do not fill whole rounds of the GPU, the
+// rem tiles left over are each split along K into sp pieces that together
+// fill the last round (FP32 partial tiles, summed by k_gh_reduce); the row
+// tiles past the limit only write zero rows.
+struct GhPlan {
+  int nr;       // real row tiles
+  int n_full;   // tiles computed whole
+  int rem;      // tiles split along K (0: none)
+  int sp;       // pieces per split tile
+};
+__device__ __forceinline__ GhPlan gh_plan(const unsigned long long* row_limit, int64_t g0, int n_mt, int n_nt,
+                                          int nk, int cus, int max_items) {
+  GhPlan p;
+  int64_t lim = row_limit != nullptr ? (int64_t)*row_limit - g0 : (int64_t)n_mt * TILE;
+  if (lim < 0) lim = 0;
+  const int64_t nr = (lim + TILE - 1) / TILE;
+  p.nr = nr < n_mt ? (int)nr : n_mt;
+  const int real = p.nr * n_nt;
+  p.rem = real % cus;
+  p.sp = 1;
+  if (p.rem != 0) {
+    int sp = cus / p.rem;
+    if (sp > kMaxGwSplit) sp = kMaxGwSplit;
+    if (sp > nk / 4) sp = nk / 4;   // at least four 64-deep stages per piece
+    if (sp * p.rem > max_items) sp = max_items / p.rem;
+    if (sp >= 2) p.sp = sp;
+  }
+  if (p.sp == 1) p.rem = 0;
+  p.n_full = real - p.rem;
+  return p;
+}
+
 // grad_hidden rows of one group: row i = c_i (p~' W)_i over K = Vp, cast to
 // bf16; p~' is stored as K-slabs [Vp/64][G][64], W^T as [Vp/64][H][64].
+// Workgroup b (see GhPlan): b < n_full a whole tile, then the K pieces of the
+// split tiles (partial tiles to part[item], [256][256] FP32), then the zero
+// rows of the row tiles past the limit; the rest return at once.
 __global__ void __launch_bounds__(NTHREADS, 1)
 k_gemm_grad_hidden(const u16* __restrict__ dlog, const u16* __restrict__ wT, int64_t Vp, int64_t H,
                    int64_t N, int64_t g0, int64_t G, int n_mt, int n_nt, const float* __restrict__ rowc,
                    u16* __restrict__ grad_hidden, const unsigned long long* __restrict__ row_limit,
-                   const int32_t* __restrict__ perm) {
+                   const int32_t* __restrict__ perm, float* __restrict__ part, int cus, int max_items) {
   __shared__ __attribute__((aligned(16))) char smem_raw[MAINLOOP_LDS];
   LDS_AS char* smem = (LDS_AS char*)smem_raw;
-  int tm, tn;
-  tile_coords(n_mt, n_nt, tm, tn);
-  const int64_t lrow0 = (int64_t)tm * TILE, col0 = (int64_t)tn * TILE;
+  const int nk = (int)(Vp / BK);
+  const GhPlan pl = gh_plan(row_limit, g0, n_mt, n_nt, nk, cus, max_items);
+  const int b = (int)blockIdx.x;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int wm = wave >> 2, wn = wave & 3;
-  if (row_limit != nullptr && g0 + lrow0 >= (int64_t)*row_limit) {
-    // rows without a label (all of this tile's): their grad_hidden is zero
+  int t, s0 = 0, s1 = nk, item = -1;
+  if (b < pl.n_full) {
+    t = b;
+    if ((pl.n_full & 7) == 0) t = (b & 7) * (pl.n_full >> 3) + (b >> 3);
+  } else if (b < pl.n_full + pl.rem * pl.sp) {
+    item = b - pl.n_full;
+    t = pl.n_full + item / pl.sp;
+    const int piece = item % pl.sp;
+    s0 = (int)((int64_t)nk * piece / pl.sp);
+    s1 = (int)((int64_t)nk * (piece + 1) / pl.sp);
+  } else {
+    // rows without a label (whole row tiles past the limit): zero grad_hidden
+    const int z = b - pl.n_full - pl.rem * pl.sp;
+    if (z >= (n_mt - pl.nr) * n_nt) return;
+    const int64_t lrow0 = (int64_t)(pl.nr + z / n_nt) * TILE, col0 = (int64_t)(z % n_nt) * TILE;
     const int64_t c0 = col0 + tid % 32 * 8;
     if (c0 < H)
       for (int r = tid / 32; r < TILE; r += NTHREADS / 32) {
@@ -1217,8 +1268,22 @@ k_gemm_grad_hidden(const u16* __restrict__ dlog, const u16* __restrict__ wT, int
       }
     return;
   }
+  int tm, tn;
+  tile_from_index(t, pl.nr, n_nt, tm, tn);
+  const int64_t lrow0 = (int64_t)tm * TILE, col0 = (int64_t)tn * TILE;
   Acc acc;
-  gemm_tile(acc, dlog, BK, G * BK * 2, lrow0, G, wT, BK, H * BK * 2, col0, H, Vp, smem);
+  gemm_tile(acc, dlog + (int64_t)s0 * G * BK, BK, G * BK * 2, lrow0, G, wT + (int64_t)s0 * H * BK, BK, H * BK * 2,
+            col0, H, (int64_t)(s1 - s0) * BK, smem);
+  if (item >= 0) {   // a K piece: plain FP32 stores, summed and scaled by k_gh_reduce
+    float* dst = part + (int64_t)item * TILE * TILE + wn * 64 + (lane & 15);
+#pragma unroll
+    for (int i = 0; i < NB; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int j = 0; j < NBJ; ++j) dst[acc_row(wm, i, r, lane) * TILE + j * 16] = acc.v[i][j][r];
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < NB; ++i)
 #pragma unroll
@@ -1233,6 +1298,30 @@ k_gemm_grad_hidden(const u16* __restrict__ dlog, const u16* __restrict__ wT, int
         if (col < H) grad_hidden[orow * H + col] = f2bf(c * acc.v[i][j][r]);
       }
     }
+}
+
+// grad_hidden rows of the split tiles: the sum of their K pieces in piece
+// order, times the row scale, cast to bf16. One workgroup per row of one
+// split tile (64 threads, four columns each); blockIdx.y past the plan's
+// split tiles returns at once.
+__global__ void __launch_bounds__(64) k_gh_reduce(const float* __restrict__ part, const float* __restrict__ rowc,
+                                                  u16* __restrict__ grad_hidden, const int32_t* __restrict__ perm,
+                                                  int64_t Vp, int64_t H, int64_t N, int64_t g0, int n_mt, int n_nt,
+                                                  const unsigned long long* __restrict__ row_limit, int cus,
+                                                  int max_items) {
+  const GhPlan pl = gh_plan(row_limit, g0, n_mt, n_nt, (int)(Vp / BK), cus, max_items);
+  const int lt = (int)blockIdx.y;
+  if (lt >= pl.rem) return;
+  int tm, tn;
+  tile_from_index(pl.n_full + lt, pl.nr, n_nt, tm, tn);
+  const int r = (int)blockIdx.x, c = (int)threadIdx.x * 4;
+  const int64_t lrow = (int64_t)tm * TILE + r, row = g0 + lrow, col = (int64_t)tn * TILE + c;
+  if (row >= N || col >= H) return;   // H % 64 == 0: all four columns in or out
+  f32x4 sum = (f32x4){0.f, 0.f, 0.f, 0.f};
+  for (int p = 0; p < pl.sp; ++p) sum += *(const f32x4*)(part + ((int64_t)(lt * pl.sp + p) * TILE + r) * TILE + c);
+  const float cs = rowc[lrow];
+  *(u32x2*)(grad_hidden + (int64_t)(perm != nullptr ? perm[row] : row) * H + col) =
+      (u32x2){f2bf2(cs * sum[0], cs * sum[1]), f2bf2(cs * sum[2], cs * sum[3])};
 }
 
 // gw rows of one tile (+)= the accumulators: base points at column
@@ -1606,11 +1695,23 @@ hipError_t launch_bias_sums(const Shapes& s, const void* dlog, const float* rowc
 
 hipError_t launch_grad_hidden(const Shapes& s, const void* dlog, const void* wT, int64_t g0, int64_t G,
                               const float* rowc, void* grad_hidden, const unsigned long long* row_limit,
-                              const int32_t* perm, hipStream_t st) {
+                              const int32_t* perm, float* part, int64_t part_items, hipStream_t st) {
   const int n_mt = (int)(G / TILE), n_nt = (int)((s.H + TILE - 1) / TILE);
-  hipLaunchKernelGGL(k_gemm_grad_hidden, dim3((unsigned)(n_mt * n_nt)), dim3(NTHREADS), 0, st,
+  const int cus = device_cus();
+  const int max_items = (int)(part_items < kMaxGwItems ? part_items : kMaxGwItems);
+  // whole tiles, K pieces and zero-row tiles need at most rem * (sp - 1) < min(cus, max_items)
+  // workgroups beyond one per tile
+  const int extra = max_items >= 2 ? (cus < max_items ? cus : max_items) : 0;
+  hipLaunchKernelGGL(k_gemm_grad_hidden, dim3((unsigned)(n_mt * n_nt + extra)), dim3(NTHREADS), 0, st,
                      (const u16*)dlog, (const u16*)wT, s.Vp, s.H, s.N, g0, G, n_mt, n_nt, rowc, (u16*)grad_hidden,
-                     row_limit, perm);
+                     row_limit, perm, part, cus, max_items);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || max_items < 2) return e;
+  // at most max_items / 2 split tiles (sp >= 2), and never more than there are tiles
+  int max_rem = max_items / 2;
+  if (max_rem > n_mt * n_nt) max_rem = n_mt * n_nt;
+  hipLaunchKernelGGL(k_gh_reduce, dim3(TILE, (unsigned)max_rem), dim3(64), 0, st, part, rowc, (u16*)grad_hidden,
+                     perm, s.Vp, s.H, s.N, g0, n_mt, n_nt, row_limit, cus, max_items);
   return hipGetLastError();
 }
 
