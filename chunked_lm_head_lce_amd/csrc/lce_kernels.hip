@@ -1196,9 +1196,12 @@ __global__ void __launch_bounds__(256) k_bias_sums(const u16* __restrict__ dlog,
 // How grad_hidden's tiles of one group are shared out, the same in every
 // workgroup and in k_gh_reduce: the row tiles below the device-side row limit
 // are real. When the real tiles do not fill whole rounds of the GPU, the
-// rem tiles left over are each split along K into sp pieces that together
-// fill the last round (FP32 partial tiles, summed by k_gh_reduce); the row
+// rem tiles left over are each split along K into sp <= 32 pieces that
+// together fill the last round (FP32 partial tiles, summed by k_gh_reduce); the row
 // tiles past the limit only write zero rows.
+// grad_hidden's K is the whole vocabulary (thousands of stages), so a
+// small group's few tiles can be cut finer than grad_weight's.
+constexpr int kMaxGhSplit = 32;
 struct GhPlan {
   int nr;       // real row tiles
   int n_full;   // tiles computed whole
@@ -1217,7 +1220,7 @@ __device__ __forceinline__ GhPlan gh_plan(const unsigned long long* row_limit, i
   p.sp = 1;
   if (p.rem != 0) {
     int sp = cus / p.rem;
-    if (sp > kMaxGwSplit) sp = kMaxGwSplit;
+    if (sp > kMaxGhSplit) sp = kMaxGhSplit;
     if (sp > nk / 4) sp = nk / 4;   // at least four 64-deep stages per piece
     if (sp * p.rem > max_items) sp = max_items / p.rem;
     if (sp >= 2) p.sp = sp;
