@@ -394,6 +394,23 @@ def test_grad_bias_inside_grad_weight(cuda, shape):
     check_all(out, oracle_of(inp, "sum"), inp, "sum")
 
 
+# grad_hidden's tiles of a partial last round split along K (summed by a
+# second kernel): 512-row groups of 8 tiles cut into 32 pieces each, with a
+# partly labelled third group and an unlabelled fourth; 2 tiles cut into 16
+# (the scratch's item count is the limit there).
+@pytest.mark.parametrize("shape", [(2048, 1024, 8192), (2300, 256, 4000)])
+def test_grad_hidden_split_pieces(cuda, shape):
+    n, h, v = shape
+    say(f"[gpu] grad_hidden K pieces shape={shape}")
+    inp = make_case(n, h, v, seed=n + h, bias_std=0.05, ignore_frac=0.3, weight_std=0.05)
+    hd, wd, bd, yd = to_device(inp, cuda)
+    out = lce.lce_forward_backward(hd, wd, bd, yd, reduction="sum")
+    again = lce.lce_forward_backward(hd, wd, bd, yd, reduction="sum")
+    torch.cuda.synchronize()
+    check_all(out, oracle_of(inp, "sum"), inp, "sum")
+    assert torch.equal(out.grad_hidden, again.grad_hidden)   # fixed order of the pieces
+
+
 def test_grad_weight_whole_and_split_tiles(cuda):
     """274 grad_weight tiles (V = 70000 over 256-row tiles, one column tile):
     on a GPU with fewer CUs the tiles past the last whole round are split
