@@ -150,7 +150,10 @@ int lce_forward_backward(const lce_problem* p, const void* hidden, const void* w
  * computed or H <= 3840: otherwise grad_weight's kernel adds them);
  * LCE_K_PARTITION orders the rows with a label before the others (two
  * launches, recorded as one) and LCE_K_GATHER_ROWS copies the hidden rows
- * into that order: the backward then works on the rows with a label only. */
+ * into that order: the backward then works on the rows with a label only.
+ * LCE_K_GRAD_HIDDEN and LCE_K_GRAD_WEIGHT each cover the product kernel and,
+ * when some of its tiles were split along K to fill the GPU's last round,
+ * the kernel that adds the pieces (one record for both). */
 typedef enum {
   LCE_K_ZERO = 0, LCE_K_PREPARE_LABELS = 1, LCE_K_FWD_LSE = 2, LCE_K_FINALIZE_ROWS = 3,
   LCE_K_FINALIZE_LOSS = 4, LCE_K_TRANSPOSE = 5, LCE_K_BWD_DLOGITS = 6, LCE_K_GRAD_HIDDEN = 7,
