@@ -421,7 +421,7 @@ int lce_forward_backward_ex(const lce_problem* p, const void* hidden, const void
   tr.st = stream;
   if (trace) trace->count = 0;
   const bool any_grad = need_gh || need_gw || need_gb;
-  const bool gb_in_gw = need_gb && need_gw && lce::grad_weight_sums_bias(c.s.H);
+  const bool gb_in_gw = need_gb && need_gw;   // grad_weight adds the grad_bias sums when it runs
   st = run_prepare(c, labels, n_valid, status, stream, tr, any_grad);
   if (st != LCE_OK) return st;
   // the gradients only need the rows with a label: valid rows first, and
@@ -492,7 +492,7 @@ int lce_forward_backward_ex(const lce_problem* p, const void* hidden, const void
       LCE_LAUNCH(tr, LCE_K_BWD_DLOGITS, rows_valid, s.V, 0,
                  lce::launch_rowscale(c.label32, c.zy2, c.lse_ws, rref, row_scale, c.n_valid, grad_scale, is_mean,
                                       g0, Gc, dlog, rowc, ovf, 1, need_gb ? gb : nullptr, c.perm, stream));
-      // grad_bias column sums: inside grad_weight's K loop when it runs and can
+      // grad_bias column sums: inside grad_weight's K loop when it runs
       if (need_gb && !gb_in_gw)
         LCE_LAUNCH(tr, LCE_K_BIAS_SUMS, rows_valid, s.V, 0, lce::launch_bias_sums(s, dlog, rowc, Gc, gb, stream));
       if (need_gh)

@@ -113,9 +113,8 @@ hipError_t launch_grad_hidden(const Shapes& s, const void* dlog, const void* wT,
 // of scratch for split tiles (no more pieces are made). first: store instead
 // of add. gw_bf16 (nullable): also write each final sum rounded to bf16 (the
 // last row group); keep32 = 0: do not write the FP32 sums back. gb_f32
-// (nullable, only when grad_weight_sums_bias(H)): also add the group's
-// grad_bias column sums, sum_i rowc[i] dlog[i][v] (FP32 atomics; rowc [G],
-// the group's row scales).
+// (nullable): also add the group's grad_bias column sums, sum_i rowc[i]
+// dlog[i][v] (FP32 atomics; rowc [G], the group's row scales).
 // row_limit (nullable): K stays below row *row_limit - g0 of the group.
 hipError_t launch_grad_weight(const Shapes& s, const void* dlog, int64_t G, const void* hT, int64_t rows_valid,
                               float* part, int64_t part_items, int first, float* gw_f32, void* gw_bf16, int keep32,
@@ -127,9 +126,10 @@ hipError_t launch_grad_weight(const Shapes& s, const void* dlog, int64_t G, cons
 constexpr int kMaxGwSplit = 8;
 constexpr int kMaxGwItems = 256;
 void grad_weight_split(int n_tiles, int nk, int cus, int max_items, int* n_full, int* split);
-// Whether launch_grad_weight can add the grad_bias column sums for hidden
-// size H (at least 16 hidden tiles of 256); otherwise launch_bias_sums does.
-bool grad_weight_sums_bias(int64_t H);
+// Rows of each 64-row stage that one wave of a grad_weight tile adds to the
+// grad_bias sums for hidden size H: the least power of two r with
+// r ceil(H / 256) >= 16 (four waves per column half, every tile of the row).
+int grad_weight_bias_rows(int64_t H);
 int device_cus();
 hipError_t launch_cast(const float* in, void* out, int64_t n, hipStream_t st);
 

@@ -339,54 +339,98 @@ struct FragAT {
 // FragAT for grad_weight with grad_bias folded in: grad_bias[v] = sum_k
 // c_k G'[k][v] over the group's rows k is a column sum of the A operand
 // already in LDS. All n_nt tiles of vocabulary tile tm see every stage of
-// G'; the one with hidden-tile index tn sums rows r = tn + j n_nt (j = 0..3)
-// of each stage, which covers the 64 rows once over the n_nt tiles when
-// n_nt >= 16 (kGwBiasMinTiles; smaller heads take the separate column-sum
-// pass). Wave w takes row j = w/2 and ids 128 (w%2) + 2 lane, +1: in slot 6
-// of every stage one 4-byte read of G' and one of c_r, in slot 8 two FMAs
-// (slots 6..9 have no fragment reads, and the stage's buffer is read-only
-// until the barrier of slot 10, FragAT's kBar). A wave whose row would be past 63 reads
-// row 0 and drops its sums. Each wave brings the 64 row scales of every
-// stage into two LDS slots of its own (one 256-byte direct load issued with
-// the stage's operand loads and covered by the same wait), so every wait
-// stays in LDS order and the K loop takes no extra branch. (Summing whole
-// stages in one tile out of n_nt instead, behind per-slot tests of the stage
-// index, measured 2-3% slower for grad_weight even with the sums removed.)
-constexpr int kGwBiasMinTiles = 16;
+// G'; the one with hidden-tile index tn sums rows r = tn + j n_nt of each
+// stage for j < 4 R, which covers the 64 rows once over the n_nt tiles
+// when R n_nt >= 16 (R from grad_weight_bias_rows). Wave w takes columns
+// 128 (w%2) .. +127 of rows j = w/2 + 4 m (m < R): L = 2, 4 or 8 adjacent
+// columns per lane (R = 1, 2, >= 4), so one read of 4, 8 or 16 bytes per
+// lane covers 1, 2 or 4 rows (lane groups of 64 / (L/2) lanes), and R / (L/2)
+// such reads (1, 2 or 4) cover the wave's rows. Read i and the row scales
+// of its rows go out in slot 6 + i, their FMAs follow in slot 8 (one read)
+// or in the next slot (slots 6..9 have no fragment reads, and the stage's
+// buffer is read-only until the barrier of slot 10, FragAT's kBar). A lane
+// whose row would be past 63 reads row 0 with a row scale of zero (R = 1:
+// the whole wave, whose sums are dropped at the end instead). Each wave
+// brings the 64 row scales of every stage into two LDS slots of its own (one
+// 256-byte direct load issued with the stage's operand loads and covered by
+// the same wait), so every wait stays in LDS order and the K loop takes no
+// extra branch. (Summing whole stages in one tile out of n_nt instead,
+// behind per-slot tests of the stage index, measured 2-3% slower for
+// grad_weight even with the sums removed.)
 __device__ __forceinline__ void lds_dma4(const void* gbase, uint32_t voff, uint32_t lds_addr) {
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, %2"
                :: "s"(lds_addr), "v"(voff), "s"(gbase) : "memory", "m0");
 }
+template <int W> struct LdsWord;   // one lane's read of W 32-bit words
+template <> struct LdsWord<1> { typedef uint32_t T; };
+template <> struct LdsWord<2> { typedef u32x2 T; };
+template <> struct LdsWord<4> { typedef u32x4 T; };
+__device__ __forceinline__ uint32_t word_at(uint32_t w, int) { return w; }
+__device__ __forceinline__ uint32_t word_at(u32x2 w, int e) { return w[e]; }
+__device__ __forceinline__ uint32_t word_at(u32x4 w, int e) { return w[e]; }
+template <int R>
 struct FragATBias : FragAT {
-  float gb[2];
+  static_assert(R == 1 || R == 2 || R == 4 || R == 8 || R == 16, "rows per wave and stage");
+  static constexpr int L = R == 1 ? 2 : R == 2 ? 4 : 8;   // adjacent columns per lane
+  static constexpr int RPR = L / 2;                        // rows per read
+  static constexpr int NRD = R / RPR;                      // reads per stage
+  static constexpr int D = NRD == 1 ? 2 : 1;               // slots from a read to its FMAs
+  static_assert(6 + NRD - 1 < kBar, "the reads of a stage precede its barrier");
+  typedef typename LdsWord<L / 2>::T Word;
+  float gb[L];
   const float* rowc;     // row scales of the tile's first K row (uniform)
   uint32_t c_lds;        // LDS byte address of this wave's two slots of 64 row scales
-  uint32_t c_row;        // byte offset of this wave's row in a slot
-  uint32_t g_off;        // byte offset of this lane's two G' values in a stage
-  uint32_t x;            // the stage's G' pair ...
-  float c;               // ... and row scale, read in slot 6
-  __device__ __forceinline__ FragATBias(int wave, int lane, const float* rowc_, uint32_t c_lds_, int row)
+  uint32_t x_off0;       // byte offset of this lane's read 0 in a stage: row * TR_ROW + (< TR_ROW)
+  uint32_t c_off0;       // byte offset of read 0's row scale in a slot
+  int step;              // rows from one read to the next (several reads)
+  bool ok[NRD];          // read i's row is below 64
+  Word x[NRD];           // read i's G' values ...
+  float c[NRD];          // ... and row scale
+  __device__ __forceinline__ FragATBias(int wave, int lane, const float* rowc_, uint32_t c_lds_, int tn, int n_nt)
       : FragAT(wave, lane), rowc(rowc_), c_lds(c_lds_) {
-    const int r = row < 64 ? row : 0;
-    c_row = (uint32_t)r * 4;
-    // the 16-byte chunk (lane/4) of half w%2 sits at slot chunk ^ 2 tr_swz(r)
-    const uint32_t chunk = (uint32_t)(((wave & 1) << 4) | (lane >> 2)) ^ (uint32_t)(2 * tr_swz(r));
-    g_off = (uint32_t)r * TR_ROW + (chunk << 4) + 4 * (uint32_t)(lane & 3);
-    gb[0] = gb[1] = 0.f;
+    const int lpr = 64 / RPR, g = lane / lpr, cl = lane % lpr;
+    const uint32_t byte = (uint32_t)((wave & 1) * 256 + cl * 2 * L);   // in the row, before the swizzle
+    // read i covers m = i RPR + g, row r0 + 16 i n_nt (several reads: RPR = 4)
+    const int r0 = tn + ((wave >> 1) + 4 * g) * n_nt;
+    step = 16 * (R == 16 ? 1 : n_nt);   // R = 16 only for n_nt = 1, where every row is below 64
+#pragma unroll
+    for (int i = 0; i < NRD; ++i) ok[i] = R == 16 || r0 + i * step < 64;
+    // one read: a row past 63 reads row 0. Several (R >= 8, n_nt <= 3): r0 <= 47
+    // and every row is below 128, so each read stays inside the stage buffers.
+    const int rr = NRD == 1 && !ok[0] ? 0 : r0;
+    // the 16-byte chunk byte/16 of row rr sits at slot chunk ^ 2 tr_swz(rr),
+    // and rows 16 apart share the swizzle
+    x_off0 = (uint32_t)rr * TR_ROW + ((((byte >> 4) ^ (uint32_t)(2 * tr_swz(rr)))) << 4) + (byte & 15);
+    c_off0 = (uint32_t)rr * 4;
+#pragma unroll
+    for (int e = 0; e < L; ++e) gb[e] = 0.f;
+  }
+  __device__ __forceinline__ uint32_t x_off(int i) const { return x_off0 + (uint32_t)(i * step * TR_ROW); }
+  __device__ __forceinline__ uint32_t c_off(int i) const {
+    return NRD == 1 || ok[i] ? c_off0 + (uint32_t)(i * step * 4) : 0u;
   }
   // the 64 row scales of stage s into this wave's slot s & 1
   __device__ __forceinline__ void load_c(int s) const {
     lds_dma4(uniform_ptr(rowc + (int64_t)s * 64), lane_x16() >> 2, c_lds + (uint32_t)((s & 1) * 256));
   }
   __device__ __forceinline__ void side(int slot, int s, const LDS_AS char* cur) {
-    if (slot == 6) {
-      x = *(const LDS_AS uint32_t*)(cur + g_off);
-      c = *(const LDS_AS float*)((const LDS_AS char*)0 + c_lds + (uint32_t)((s & 1) * 256) + c_row);
-    }
-    if (slot == 8) {
-      gb[0] = fmaf(c, __builtin_bit_cast(float, x << 16), gb[0]);
-      gb[1] = fmaf(c, __builtin_bit_cast(float, x & 0xFFFF0000u), gb[1]);
-    }
+#pragma unroll
+    for (int i = 0; i < NRD; ++i)
+      if (slot == 6 + i + D) {
+#pragma unroll
+        for (int e = 0; e < L / 2; ++e) {
+          const uint32_t w = word_at(x[i], e);
+          gb[2 * e] = fmaf(c[i], __builtin_bit_cast(float, w << 16), gb[2 * e]);
+          gb[2 * e + 1] = fmaf(c[i], __builtin_bit_cast(float, w & 0xFFFF0000u), gb[2 * e + 1]);
+        }
+      }
+#pragma unroll
+    for (int i = 0; i < NRD; ++i)
+      if (slot == 6 + i) {
+        x[i] = *(const LDS_AS Word*)(cur + x_off(i));
+        const float cv = *(const LDS_AS float*)((const LDS_AS char*)0 + c_lds + (uint32_t)((s & 1) * 256) + c_off(i));
+        c[i] = R == 1 || ok[i] ? cv : 0.f;   // R = 1: the row is the wave's, dropped at the end instead
+      }
   }
   // row scales of stage s + 2, issued with its operand loads (stages 0 and
   // 1: before the K loop)
@@ -1097,7 +1141,7 @@ __global__ void __launch_bounds__(256) k_transpose(const u16* __restrict__ in, i
 // FP32 label logit and lse: exp(z_y - r) - exp(lse - r), no cancellation
 // through bf16); c_i becomes a row scale of grad_hidden's output and of h^T
 // in grad_weight, and grad_bias is a c-weighted column sum of p~'
-// (k_bias_sums). A valid row whose maximum lies more than 60 above its label
+// (inside grad_weight, or k_bias_sums when grad_weight is not computed). A valid row whose maximum lies more than 60 above its label
 // logit would leave the range of the stored values: the forward tiles then
 // set the overflow flag, and the group's p~ is recomputed against r_i =
 // lse_i (k_prep_ref, k_fwd_tile and k_rowscale in their retry mode: every
@@ -1149,7 +1193,8 @@ __global__ void __launch_bounds__(256) k_rowscale(const int32_t* __restrict__ la
   if (gb_f32 != nullptr) atomicAdd(gb_f32 + lab, c * (pl - bf2f(pb)));
 }
 
-// grad_bias += sum_i c_i p~'[i][v] over one group: one workgroup per 64-id
+// grad_bias += sum_i c_i p~'[i][v] over one group, for calls without
+// grad_weight (which otherwise adds these sums): one workgroup per 64-id
 // K-slab and 1024 rows (a contiguous 128 KB block of the slab), 8 ids x 32
 // rows per thread, then 32 partial sums per id added through LDS.
 constexpr int BS_ROWS = 1024;
@@ -1403,14 +1448,14 @@ __device__ __forceinline__ void tr_slot(int wave, int lane, int b, int& k, int& 
 // The n_tiles - n_full left over would run as one thin last round, so each
 // is split over `split` workgroups by K; those write FP32 partial tiles to
 // part ([item][256][256]) and k_gw_reduce adds them in a fixed order.
-template <bool BIAS>
+template <int R>   // R > 0: also the grad_bias sums, R rows per wave and stage (FragATBias)
 __global__ void __launch_bounds__(NTHREADS, 1)
 k_gemm_grad_weight(const u16* __restrict__ G, int64_t slab_rows, const u16* __restrict__ hT, int nk, int64_t H,
                    int64_t V, int n_mt, int n_nt, int n_full, int split, int first, float* __restrict__ gw_f32,
                    float* __restrict__ part, u16* __restrict__ gw_bf16, int keep32, const float* __restrict__ rowc,
                    float* __restrict__ gb_f32, const unsigned long long* __restrict__ row_limit, int64_t g0) {
   __shared__ __attribute__((aligned(16))) char smem_raw[MAINLOOP_LDS];
-  __shared__ __attribute__((aligned(16))) float s_c[BIAS ? NTHREADS / 64 * 2 * 64 : 4];   // per wave, two stages
+  __shared__ __attribute__((aligned(16))) float s_c[R ? NTHREADS / 64 * 2 * 64 : 4];   // per wave, two stages
   LDS_AS char* smem = (LDS_AS char*)smem_raw;
   int tm, tn, s0 = 0, s1 = nk, item = -1;
   if ((int)blockIdx.x < n_full) {
@@ -1454,27 +1499,30 @@ k_gemm_grad_weight(const u16* __restrict__ G, int64_t slab_rows, const u16* __re
     for (int i = 0; i < NB; ++i)
 #pragma unroll
       for (int j = 0; j < NBJ; ++j) acc.v[i][j] = (f32x4){0.f, 0.f, 0.f, 0.f};
-  } else if (BIAS) {
-    const int row = tn + (wave >> 1) * n_nt;   // this wave's row of every stage
-    FragATBias fs(wave, lane, rowc + (int64_t)s0 * 64,
-                  (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(LDS_AS char*)s_c) +
-                      (uint32_t)wave * 2 * 256,
-                  row);
+  } else if constexpr (R > 0) {
+    FragATBias<R> fs(wave, lane, rowc + (int64_t)s0 * 64,
+                     (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(LDS_AS char*)s_c) +
+                         (uint32_t)wave * 2 * 256,
+                     tn, n_nt);
     // the row scales of stages 0 and 1 go out before the operand loads, so
     // tile_run's first wait covers them
     for (int sb = 0; sb < 2 && sb < s1 - s0; ++sb) fs.load_c(sb);
-    tile_prologue<FragATBias>(t, s1 - s0);
+    tile_prologue<FragATBias<R>>(t, s1 - s0);
     tile_run(acc, t, s1 - s0, smem, fs);
     if (tn < 64) {      // some wave summed a row: add the tile's 256 column sums
+      constexpr int L = FragATBias<R>::L, RPR = FragATBias<R>::RPR;
       __syncthreads();  // every wave is past its last read of the stage buffers
+      // wave w, lane = g 128 / L + cl: columns 128 (w%2) + cl L + e of its rows of group g
       LDS_AS float* red = (LDS_AS float*)smem;
-      red[wave * 128 + 2 * lane] = row < 64 ? fs.gb[0] : 0.f;
-      red[wave * 128 + 2 * lane + 1] = row < 64 ? fs.gb[1] : 0.f;
+#pragma unroll
+      for (int e = 0; e < L; ++e) red[wave * 128 * RPR + lane * L + e] = R > 1 || fs.ok[0] ? fs.gb[e] : 0.f;
       __syncthreads();
-      if (tid < TILE) {   // id tid: waves 2 j + tid / 128, j = 0..3
+      if (tid < TILE) {   // column tid: waves 2 j + tid / 128 (j = 0..3), their groups g
         float sum = 0.f;
 #pragma unroll
-        for (int j = 0; j < NTHREADS / 128; ++j) sum += red[(2 * j + (tid >> 7)) * 128 + (tid & 127)];
+        for (int j = 0; j < NTHREADS / 128; ++j)
+#pragma unroll
+          for (int g = 0; g < RPR; ++g) sum += red[(2 * j + (tid >> 7)) * 128 * RPR + g * 128 + (tid & 127)];
         if (row0 + tid < V) atomicAdd(gb_f32 + row0 + tid, sum);
       }
     }
@@ -1728,14 +1776,18 @@ hipError_t launch_grad_weight(const Shapes& s, const void* dlog, int64_t G, cons
   int n_full = n_tiles, split = 1;
   grad_weight_split(n_tiles, nk, device_cus(), (int)part_items, &n_full, &split);
   const dim3 grid((unsigned)(n_full + (n_tiles - n_full) * split)), block(NTHREADS);
-  if (gb_f32 != nullptr)
-    hipLaunchKernelGGL(k_gemm_grad_weight<true>, grid, block, 0, st, (const u16*)dlog, G, (const u16*)hT, nk, s.H,
-                       s.V, n_mt, n_nt, n_full, split, first, gw_f32, part, (u16*)gw_bf16, keep32, rowc, gb_f32,
-                       row_limit, g0);
-  else
-    hipLaunchKernelGGL(k_gemm_grad_weight<false>, grid, block, 0, st, (const u16*)dlog, G, (const u16*)hT, nk, s.H,
-                       s.V, n_mt, n_nt, n_full, split, first, gw_f32, part, (u16*)gw_bf16, keep32,
-                       (const float*)nullptr, (float*)nullptr, row_limit, g0);
+#define LCE_GW_LAUNCH(R_, RC, GB)                                                                              \
+  hipLaunchKernelGGL(k_gemm_grad_weight<R_>, grid, block, 0, st, (const u16*)dlog, G, (const u16*)hT, nk, s.H, s.V, \
+                     n_mt, n_nt, n_full, split, first, gw_f32, part, (u16*)gw_bf16, keep32, RC, GB, row_limit, g0)
+  switch (gb_f32 == nullptr ? 0 : grad_weight_bias_rows(s.H)) {
+    case 0: LCE_GW_LAUNCH(0, (const float*)nullptr, (float*)nullptr); break;
+    case 1: LCE_GW_LAUNCH(1, rowc, gb_f32); break;
+    case 2: LCE_GW_LAUNCH(2, rowc, gb_f32); break;
+    case 4: LCE_GW_LAUNCH(4, rowc, gb_f32); break;
+    case 8: LCE_GW_LAUNCH(8, rowc, gb_f32); break;
+    default: LCE_GW_LAUNCH(16, rowc, gb_f32); break;
+  }
+#undef LCE_GW_LAUNCH
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || n_full == n_tiles) return e;
   hipLaunchKernelGGL(k_gw_reduce, dim3(TILE, (unsigned)(n_tiles - n_full)), dim3(64), 0, st, part, n_full, split,
@@ -1743,7 +1795,12 @@ hipError_t launch_grad_weight(const Shapes& s, const void* dlog, int64_t G, cons
   return hipGetLastError();
 }
 
-bool grad_weight_sums_bias(int64_t H) { return (H + TILE - 1) / TILE >= kGwBiasMinTiles; }
+int grad_weight_bias_rows(int64_t H) {
+  const int64_t n_nt = (H + TILE - 1) / TILE;
+  int r = 1;
+  while (r * n_nt < 16) r *= 2;   // 4 waves x r rows x n_nt tiles cover the 64 rows of a stage
+  return r;
+}
 
 void grad_weight_split(int n_tiles, int nk, int cus, int max_items, int* n_full, int* split) {
   const int rem = n_tiles % cus;

@@ -147,7 +147,7 @@ int lce_forward_backward(const lce_problem* p, const void* hidden, const void* w
  * numerators against r_i = lse_i when a row's maximum lies more than 60
  * above its label logit (otherwise it returns at once); LCE_K_BIAS_SUMS
  * adds the group's grad_bias column sums (only when grad_weight is not
- * computed or H <= 3840: otherwise grad_weight's kernel adds them);
+ * computed: otherwise grad_weight's kernel adds them);
  * LCE_K_PARTITION orders the rows with a label before the others (two
  * launches, recorded as one) and LCE_K_GATHER_ROWS copies the hidden rows
  * into that order: the backward then works on the rows with a label only.

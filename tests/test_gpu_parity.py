@@ -378,12 +378,17 @@ def test_repeatable(cuda):
     assert torch.equal(fa.loss, fb.loss) and torch.equal(fa.lse, a.lse)
 
 
-# grad_bias summed inside grad_weight's K loop (at least 16 hidden tiles):
-# 16 tiles, every wave on a row; 16 tiles of which the last holds 64 hidden
-# columns (H = 3904, the smallest such H); 17 tiles, the waves of row 3 idle
-# in most tiles; 65 tiles, the last tile has no row. Several row groups, a
-# partial last stage and (fewer tiles than CUs) tiles split along K.
-@pytest.mark.parametrize("shape", [(700, 4096, 1000), (300, 3904, 700), (300, 4160, 600), (257, 16448, 300)])
+# grad_bias summed inside grad_weight's K loop, each wave of a tile on R
+# rows of every 64-row stage with R ceil(H / 256) >= 16: one hidden tile of
+# 64 or 256 columns (R = 16); 2 and 3 tiles (R = 8, some rows past the stage
+# at 3); 4 and 5 tiles (R = 4); 10 tiles (R = 2); 16 tiles, every wave on a
+# row; 16 tiles of which the last holds 64 hidden columns (H = 3904); 17
+# tiles, the waves of row 3 idle in most tiles; 65 tiles, the last tile has
+# no row. Several row groups, a partial last stage and (fewer tiles than
+# CUs) tiles split along K.
+@pytest.mark.parametrize("shape", [(500, 64, 900), (700, 256, 1000), (300, 512, 800), (300, 768, 700),
+                                   (300, 1024, 600), (300, 1280, 650), (300, 2560, 500), (700, 4096, 1000),
+                                   (300, 3904, 700), (300, 4160, 600), (257, 16448, 300)])
 def test_grad_bias_inside_grad_weight(cuda, shape):
     n, h, v = shape
     say(f"[gpu] grad_bias inside grad_weight shape={shape}")

@@ -1,6 +1,6 @@
 """GPU parity on a seeded spread of shapes, each compared in full with the
-float64 oracle: hidden sizes on both sides of the 16-tile boundary where
-grad_weight starts to add the grad_bias sums itself, ragged rows and
+float64 oracle: hidden sizes from 1 to 20 tiles of 256 (every count of rows
+per wave that grad_weight's grad_bias sums take), ragged rows and
 vocabulary, bias on and off, none / some / most rows ignored, several row
 groups and chunk sizes, the three reductions (none with per-token upstream
 gradients of 1, which is the sum's gradient), with and without the FP32

@@ -67,10 +67,9 @@ def test_traced_forward_backward_matches_untraced(cuda):
         groups = 3
         # per row group: the forward tiles, their retry (a no-op here), the
         # row scales (and their retry), both row-reference steps and the two
-        # gradient products; at H = 256 (one hidden tile) grad_bias takes its
-        # own column-sum pass
+        # gradient products; grad_weight adds the grad_bias sums itself
         for k, per_group in (("fwd_lse", 1), ("fwd_retry", 1), ("bwd_dlogits", 2), ("row_ref", 2),
-                             ("grad_hidden", 1), ("grad_weight", 1), ("finalize_rows", 1), ("bias_sums", 1)):
+                             ("grad_hidden", 1), ("grad_weight", 1), ("finalize_rows", 1), ("bias_sums", 0)):
             assert names.count(k) == per_group * groups, (k, names)
         assert names.count("label_logit") == 1 and names.count("finalize_loss") == 1
         assert names.count("partition") == 1 and names.count("gather_rows") == 1   # valid rows first
@@ -91,10 +90,14 @@ def test_traced_forward_backward_matches_untraced(cuda):
         ev.close()
 
 
-@pytest.mark.parametrize("h,passes", [(3840, 3), (3904, 0), (4096, 0)])
-def test_grad_bias_inside_grad_weight_trace(cuda, h, passes):
-    """From 16 hidden tiles on (H > 3840) grad_weight's kernel adds the
-    grad_bias column sums itself; below, a column-sum pass per row group
+# one hidden tile (16 rows per wave and stage), 3 tiles (8, some rows past
+# the stage), 4 (4), 10 (2), 15 (2, some rows past) and 16 (1); then
+# grad_bias without grad_weight, which takes the column-sum pass
+@pytest.mark.parametrize("h,want_gw", [(256, True), (768, True), (1024, True), (2560, True), (3840, True),
+                                       (4096, True), (768, False)])
+def test_grad_bias_inside_grad_weight_trace(cuda, h, want_gw):
+    """When grad_weight runs, its kernel adds the grad_bias column sums
+    itself at every hidden size; without it, a column-sum pass per row group
     does. Same results as untraced either way."""
     n, v, g = 600, 700, 256                   # three row groups
     inp = make_case(n, h, v, seed=33, bias_std=0.05, ignore_frac=0.1, weight_std=0.02)
@@ -103,13 +106,18 @@ def test_grad_bias_inside_grad_weight_trace(cuda, h, passes):
     ev = _Events(2 * cap)
     try:
         t, kinds, _ = _trace(ev, cap)
-        say(f"[gpu] traced forward+backward at H={h}, 3 row groups")
-        a = lce.lce_forward_backward(hd, wd, bd, yd, rows_in_flight=g, trace=t)
-        b = lce.lce_forward_backward(hd, wd, bd, yd, rows_in_flight=g)
+        say(f"[gpu] traced forward+backward at H={h}, grad_weight {want_gw}, 3 row groups")
+        a = lce.lce_forward_backward(hd, wd, bd, yd, rows_in_flight=g, trace=t, want_grad_weight=want_gw,
+                                     want_f32=True)
+        b = lce.lce_forward_backward(hd, wd, bd, yd, rows_in_flight=g, want_grad_weight=want_gw, want_f32=True)
         torch.cuda.synchronize()
         names = [_lib.KERNEL_KINDS[kinds[i]] for i in range(t.count)]
-        assert names.count("grad_weight") == 3 and names.count("bias_sums") == passes, names
-        assert torch.equal(a.grad_weight, b.grad_weight) and torch.equal(a.grad_hidden, b.grad_hidden)
+        groups = 3
+        assert names.count("grad_weight") == (groups if want_gw else 0), names
+        assert names.count("bias_sums") == (0 if want_gw else groups), names
+        if want_gw:
+            assert torch.equal(a.grad_weight, b.grad_weight)
+        assert torch.equal(a.grad_hidden, b.grad_hidden)
         # FP32 atomics: equal up to their order
         torch.testing.assert_close(a.grad_bias_f32, b.grad_bias_f32, rtol=1e-5, atol=1e-6)
     finally:
