@@ -142,17 +142,54 @@ __device__ __forceinline__ void tile_coords(int n_m, int n_n, int& tm, int& tn) 
   tile_from_index(t, n_m, n_n, tm, tn);
 }
 // Persistent kernels (grid a multiple of 8, at most one workgroup per CU):
-// XCD x = blockIdx % 8 owns logical tiles [x * per_xcd, (x + 1) * per_xcd),
-// taken in order, so the tiles running at once on one XCD are neighbours, as
-// in tile_coords. Tile k of this workgroup's XCD; false past its range.
-// (The forward walks 8 row tiles at a time, an 8 x 4 window: measured
-// ~1% faster than 4 x 8 there.)
+// tile k of this workgroup's XCD (x = blockIdx % 8), taken in order by the
+// XCD's workgroups; false past the XCD's last tile. The 8 XCDs should walk
+// the column (weight) tiles in step, so that each weight panel comes from
+// HBM once and the other XCDs find it in the MALL. The row tiles go in
+// blocks of 64 and a remainder of r = n_m % 64:
+// * in each block of 64, XCD x owns the 8-row group 8x .. 8x+7 across all
+//   column tiles (tile_from_index<8>: windows of 8 x 4 tiles, measured ~1%
+//   faster than 4 x 8), so the XCDs stay in step on equal work;
+// * a remainder r >= 32: the r x C tiles of each group of C column tiles
+//   (C = 4, or 8 for odd r) are dealt out in row-major order, q = r C / 8 to
+//   each XCD, so every XCD takes the same number of tiles per column group
+//   (a block of r / 8 rows x C columns: at least 4 x 4);
+// * a remainder r < 32: XCD x takes the slice [x, x + 1) / 8 of the
+//   remainder's tiles in row-group order, about n_n / 8 adjacent columns of
+//   all its rows (dealt blocks would be thin slivers with little L2 reuse).
+// Slices of the row-group order over all n_m row tiles put the XCDs on up to
+// 8 unrelated column phases when n_m is not a multiple of 64: the forward
+// tiles ran 3-7% slower per tile there (40-96 row tiles) than at 64; dealt,
+// 40-60 row tiles gained 2-4% per tile.
 __device__ __forceinline__ bool xcd_tile(int n_m, int n_n, int k, int& tm, int& tn) {
-  const int ntiles = n_m * n_n;
+  const int x = (int)(blockIdx.x & 7);
+  const int full = n_m & ~63, r = n_m - full;
+  const int per_block = 8 * n_n;                  // this XCD's tiles in each block of 64 row tiles
+  const int in_blocks = (full >> 6) * per_block;
+  if (k < in_blocks) {
+    const int blk = k / per_block;
+    tile_from_index<8>(k - blk * per_block, 8, n_n, tm, tn);
+    tm += 64 * blk + 8 * x;
+    return true;
+  }
+  k -= in_blocks;
+  if (r >= 32) {
+    const int C = (r & 1) ? 8 : 4, q = r * C / 8;
+    const int cg = k / q;
+    const int cw = min(C, n_n - cg * C);   // columns in this group (the last may be narrower)
+    const int j = x * q + (k - cg * q);    // row-major index in the group
+    if (cw <= 0 || j >= r * cw) return false;
+    const int row = j / cw;
+    tm = full + row;
+    tn = cg * C + (j - row * cw);
+    return true;
+  }
+  const int ntiles = r * n_n;
   const int per_xcd = (ntiles + 7) >> 3;
-  const int t = (int)(blockIdx.x & 7) * per_xcd + k;
+  const int t = x * per_xcd + k;
   if (k >= per_xcd || t >= ntiles) return false;
-  tile_from_index<8>(t, n_m, n_n, tm, tn);
+  tile_from_index<8>(t, r, n_n, tm, tn);
+  tm += full;
   return true;
 }
 
