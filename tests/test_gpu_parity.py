@@ -430,3 +430,25 @@ def test_grad_weight_whole_and_split_tiles(cuda):
     torch.cuda.synchronize()
     check_all(out, oracle_of(inp, "sum"), inp, "sum")
     assert torch.equal(out.grad_weight, again.grad_weight)   # fixed summation order
+
+
+# The forward tiles' order per XCD: blocks of 64 row tiles, then a remainder
+# dealt out per column group (32..63 row tiles) or sliced (below 32). 104
+# row tiles = one block + a dealt 40; 73 (ragged) = one block + a sliced 9;
+# 54 = dealt only. Forward-only over all rows, and forward+backward with the
+# whole input as one row group, compared in full with the oracle.
+@pytest.mark.parametrize("n", [104 * 256, 73 * 256 - 100, 54 * 256 - 7])
+def test_forward_tile_orders(cuda, n):
+    h, v = 64, 1100
+    say(f"[gpu] forward tile orders n={n} ({(n + 255) // 256} row tiles)")
+    inp = make_case(n, h, v, seed=n, bias_std=0.05, ignore_frac=0.1, weight_std=0.05)
+    hd, wd, bd, yd = to_device(inp, cuda)
+    ref = oracle_of(inp, "sum")
+    f = lce.lce_forward(hd, wd, bd, yd, reduction="sum")
+    torch.cuda.synchronize()
+    assert int(f.n_valid.item()) == ref.n_valid
+    assert_loss_close(float(f.loss.item()), ref.loss)
+    assert_rows_close(np32(f.lse), ref.lse, "forward-only lse")
+    out = lce.lce_forward_backward(hd, wd, bd, yd, reduction="sum", rows_in_flight=n)
+    torch.cuda.synchronize()
+    check_all(out, ref, inp, "sum")
