@@ -53,6 +53,7 @@ constexpr int MAINLOOP_LDS = 2 * STAGE;            // 128 KB: double buffered
 constexpr float LOG2E = 1.4426950408889634f;       // log2(e): exp(x) = 2^(x log2 e)
 constexpr float LN2 = 0.6931471805599453f;         // ln(2) = 1 / log2(e)
 constexpr float REF_CAP2 = 60.f * LOG2E;           // largest exponent (base 2) of a stored p~: e^60
+constexpr float REF_SUM_CAP = 1.1420074e26f;       // e^60: largest partial sum against a reference
 // s_waitcnt immediates (gfx9 encoding: vmcnt [3:0]+[15:14], expcnt [6:4],
 // lgkmcnt [11:8]); the other counters are left at their maximum (no wait).
 constexpr int WAIT_LGKM0 = 0xC07F;   // lgkmcnt(0)
@@ -874,6 +875,13 @@ k_fwd_tile(const u16* __restrict__ hidden, int64_t ldh, const u16* __restrict__ 
       hit_lo = __ballot((unsigned)(lp[0] - cw) < 64u);
       hit_hi = __ballot((unsigned)(lp[64] - cw) < 64u);
     }
+    // Whether every one of this wave's 128 rows has a reference (NaN: none),
+    // a wave-uniform choice of the partial sums' shift below.
+    bool all_ref = false;
+    if (use_ref) {
+      const LDS_AS float* wr = (const LDS_AS float*)s_ref + par * TILE + wm * 128;
+      all_ref = __ballot(__builtin_isnan(wr[lane]) || __builtin_isnan(wr[lane + 64])) == 0;
+    }
     // The four rows r of a row block are reduced together so their DPP
     // steps interleave instead of waiting on each other.
 #pragma unroll
@@ -899,53 +907,97 @@ k_fwd_tile(const u16* __restrict__ hidden, int64_t ldh, const u16* __restrict__ 
           }
         }
       }
-      float m[4];                               // row max of z * log2(e)
+      // Stored p~ = exp(z - ref), ref the row's reference (its label logit)
+      // when it has one, else the quarter maximum. When all of the wave's
+      // 128 rows have a reference (all_ref), the partial sums are taken
+      // against it too, (ref, sum 2^(t - ref)): no row maximum, no second
+      // scale, and the stored values are the summed ones. If a sum exceeds
+      // e^60 (some value may, or is infinite), or without all_ref, the
+      // block takes (max, sum 2^(t - max)) and scales each stored value by
+      // fr = exp(max - ref), capped at e^60; a valid row whose maximum lies
+      // more than 60 above its reference raises the overflow flag (the group
+      // is redone against r = lse).
+      const LDS_AS float* refs = (const LDS_AS float*)s_ref + par * TILE + wm * 128 + i * 16 + 4 * (lane >> 4);   // this lane's 4 rows
+      float mo[4], sm[4];                       // the partial: its shift and its sum, base 2
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        m[r] = -INFINITY;
+      for (int r = 0; r < 4; ++r) sm[r] = 0.f;
+      bool ref_sums = all_ref;
+      if (ref_sums) {
+        float rf[4];                            // reference * log2(e)
 #pragma unroll
-        for (int j = 0; j < NBJ; ++j) m[r] = fmaxf(m[r], acc.v[i][j][r]);
-      }
-      max16x4(m);
-      // Stored p~ = exp(z - ref): ref is the row's reference (its label
-      // logit) when it has one, else the quarter maximum. fr = exp(m - ref),
-      // capped at e^60; a valid row whose maximum lies more than 60 above its
-      // reference raises the overflow flag (the group is redone).
-      float ms[4], fr[4], sm[4];
+        for (int r = 0; r < 4; ++r) rf[r] = refs[r] * LOG2E;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        ms[r] = m[r] == -INFINITY ? 0.f : m[r];   // all columns past V: every e = 0
-        fr[r] = 1.f;
-        sm[r] = 0.f;
-      }
-      if (use_ref) {
+        for (int j = 0; j < NBJ; ++j) {
+          float e[4];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float rr = ((const LDS_AS float*)s_ref)[par * TILE + wm * 128 + i * 16 + 4 * (lane >> 4) + r];
-          const float d = ms[r] - rr * LOG2E;      // NaN when the row has no reference
-          overflow |= m[r] != -INFINITY && d > REF_CAP2;
-          fr[r] = __builtin_isnan(rr) ? 1.f : __builtin_amdgcn_exp2f(fminf(d, REF_CAP2));
-        }
-      }
-#pragma unroll
-      for (int j = 0; j < NBJ; ++j) {
-        float e[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          e[r] = __builtin_amdgcn_exp2f(acc.v[i][j][r] - ms[r]);
-          sm[r] += e[r];
-        }
-        if (STORE_P)
-#pragma unroll
-          for (int r = 0; r < 4; r += 2) {
-            const uint32_t pk = f2bf2(e[r] * fr[r], e[r + 1] * fr[r + 1]);
-            pst[(4 * (lane >> 4) + r) * PST_LD + j * 16 + (lane & 15)] = (u16)pk;
-            pst[(4 * (lane >> 4) + r + 1) * PST_LD + j * 16 + (lane & 15)] = (u16)(pk >> 16);
+          for (int r = 0; r < 4; ++r) {
+            e[r] = __builtin_amdgcn_exp2f(acc.v[i][j][r] - rf[r]);
+            sm[r] += e[r];
           }
+          if (STORE_P)
+#pragma unroll
+            for (int r = 0; r < 4; r += 2) {
+              const uint32_t pk = f2bf2(e[r], e[r + 1]);
+              pst[(4 * (lane >> 4) + r) * PST_LD + j * 16 + (lane & 15)] = (u16)pk;
+              pst[(4 * (lane >> 4) + r + 1) * PST_LD + j * 16 + (lane & 15)] = (u16)(pk >> 16);
+            }
+        }
+        sum16x4(sm);
+        bool big = false;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          mo[r] = rf[r];
+          big |= !(sm[r] <= REF_SUM_CAP);
+        }
+        if (__ballot(big) != 0) {   // rare: the block's sums against its maxima instead (which raise the flag)
+          ref_sums = false;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) sm[r] = 0.f;
+        }
       }
-      sum16x4(sm);
+      if (!ref_sums) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          mo[r] = -INFINITY;
+#pragma unroll
+          for (int j = 0; j < NBJ; ++j) mo[r] = fmaxf(mo[r], acc.v[i][j][r]);
+        }
+        max16x4(mo);
+        float ms[4], fr[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          ms[r] = mo[r] == -INFINITY ? 0.f : mo[r];   // all columns past V: every e = 0
+          fr[r] = 1.f;
+        }
+        if (use_ref) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float rr = refs[r];
+            const float d = ms[r] - rr * LOG2E;        // NaN when the row has no reference
+            overflow |= mo[r] != -INFINITY && d > REF_CAP2;
+            fr[r] = __builtin_isnan(rr) ? 1.f : __builtin_amdgcn_exp2f(fminf(d, REF_CAP2));
+          }
+        }
+#pragma unroll
+        for (int j = 0; j < NBJ; ++j) {
+          float e[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            e[r] = __builtin_amdgcn_exp2f(acc.v[i][j][r] - ms[r]);
+            sm[r] += e[r];
+          }
+          if (STORE_P)
+#pragma unroll
+            for (int r = 0; r < 4; r += 2) {
+              const uint32_t pk = f2bf2(e[r] * fr[r], e[r + 1] * fr[r + 1]);
+              pst[(4 * (lane >> 4) + r) * PST_LD + j * 16 + (lane & 15)] = (u16)pk;
+              pst[(4 * (lane >> 4) + r + 1) * PST_LD + j * 16 + (lane & 15)] = (u16)(pk >> 16);
+            }
+        }
+        sum16x4(sm);
+      }
       if ((lane & 15) == 0) {   // rows 4*(lane/16) .. +3 of the block, in base-2 units
-        *(f32x4*)(pm + i * 16) = (f32x4){m[0], m[1], m[2], m[3]};
+        *(f32x4*)(pm + i * 16) = (f32x4){mo[0], mo[1], mo[2], mo[3]};
         *(f32x4*)(ps + i * 16) = (f32x4){sm[0], sm[1], sm[2], sm[3]};
       }
       if (STORE_P) {
@@ -1064,12 +1116,14 @@ __global__ void __launch_bounds__(64 * FIN_WAVES) k_finalize_rows(
     return;
   }
   for (int w = 1; w < FIN_WAVES; ++w) merge_ms(M, S, s_m[w][lane], s_s[w][lane]);
-  // S >= 1: the partial holding the maximum M has its own maximum term
-  // 2^(M - M) = 1, and every other term is >= 0 (the clamp is a guard).
-  const float L = fmaxf(__log2f(S), 0.f);
+  // Against a row maximum M, S >= 1 (the maximum's own term is 2^0 = 1);
+  // against a row reference M = r (its label logit from a separate dot
+  // product), S holds the label's term 2^(t_y - r), ~1. Mathematically
+  // l = lse - z_y >= 0; the clamp only takes off the rounding of r - t_y.
+  const float L = __log2f(S);
   const float lse = LN2 * (M + L);
   const int lab = label32[i];
-  const float l = lab >= 0 ? LN2 * ((M - zy2[i]) + L) : 0.f;   // M >= t_y: never negative
+  const float l = lab >= 0 ? fmaxf(LN2 * ((M - zy2[i]) + L), 0.f) : 0.f;
   lse_ws[i] = lse;
   const int64_t oi = perm != nullptr ? (int64_t)perm[i] : i;   // the caller's row
   if (lse_out) lse_out[oi] = lse;

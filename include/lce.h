@@ -38,9 +38,12 @@
  *    grad_weight (bf16 and FP32) are bit-identical from call to call on the
  *    same device and inputs (fixed summation orders). The SUM / MEAN loss and
  *    the chunk sums add rows with float64 atomics, and grad_bias adds column
- *    sums with FP32 atomics: their last bits may differ between calls.
+ *    sums with FP32 atomics: their last bits may differ between calls. The
+ *    lse of lce_forward_backward can differ from lce_forward's in the last
+ *    bits: the fused call sums a labelled row's exponentials against its
+ *    label logit, the forward alone against the row's maximum.
  *  - The label logit in l_i comes from the same FP32 accumulators as the
- *    row's lse, so l_i >= 0 for every row.
+ *    row's sums, and l_i >= 0 for every row.
  */
 #ifndef LCE_H
 #define LCE_H
