@@ -232,6 +232,33 @@ def test_far_label_logit_retry(cuda, g, reduction):
     check_all(out, ref, inp, reduction)
 
 
+@pytest.mark.parametrize("g", [256, 0])
+def test_reference_sum_fallback(cuda, g):
+    """Rows whose label logit lies 59 below 100 other logits: no value is
+    more than 60 above the reference (no retry), but their sums against it
+    exceed e^60, so those row blocks take their sums against the maximum
+    instead. The results must not notice."""
+    import dataclasses
+    from lce_inputs import bf16_bits
+    inp = make_case(700, 128, 1500, seed=27, bias_std=None, ignore_frac=0.1)
+    h = inp.hidden_f32().copy()
+    w = inp.weight_f32().copy()
+    y = inp.labels.copy()
+    for r in (3, 300, 650):
+        h[r, :] = 1.0
+        y[r] = 9
+    w[100:200, :] = 59.0 / 128.0      # 0.4609375 in bf16: 128 * it = 59
+    w[9, :] = 0.0
+    inp = dataclasses.replace(inp, hidden_bits=bf16_bits(h), weight_bits=bf16_bits(w), labels=y)
+    hd, wd, bd, yd = to_device(inp, cuda)
+    say(f"[gpu] reference-sum fallback, rows_in_flight={g}")
+    out = lce.lce_forward_backward(hd, wd, bd, yd, rows_in_flight=g)
+    torch.cuda.synchronize()
+    ref = oracle_of(inp)
+    assert all(55 < ref.row_loss[r] < 60 + math.log(100) + 1 for r in (3, 300, 650))
+    check_all(out, ref, inp, "sum")
+
+
 def test_strided_hidden_and_weight(cuda):
     inp = make_case(300, 128, 700, seed=13, bias_std=0.05)
     hd, wd, bd, yd = to_device(inp, cuda)
